@@ -1,0 +1,23 @@
+"""Float64 CPU oracle of the FLUX-class VAE decoder (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path never does.
+"""
+from .vae_oracle import (  # noqa: F401
+    EPS,
+    GROUPS,
+    attention,
+    causal_stack,
+    conv2d,
+    conv2d_at,
+    conv3d_causal,
+    conv3d_causal_at,
+    decode,
+    denormalize,
+    group_norm,
+    group_norm_silu,
+    resnet,
+    silu,
+    softmax_rows,
+    upsample_nearest2x,
+)
