@@ -1,0 +1,188 @@
+"""Throughput of the FLUX-class VAE decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode1024|decode256]
+                    [--no-cpu-baseline]
+
+A step is one whole decode (conv_in ... conv_out, every kernel of the chain)
+of a seeded synthetic latent, with seeded synthetic weights already packed on
+the device and the latent already resident in HBM.  Default workload: latent
+[16,128,128] -> RGB [3,1024,1024].  Prints ONE JSON line:
+
+  value        algorithmic TFLOP/s of the decode (direct-conv FLOPs of every
+               conv + attention FLOPs) / wall time per decode
+  ms_per_step  wall time of one decode (HIP-event/host timing around K steps)
+  roofline     the dominant kernel (largest share of device time): its
+               algorithmic FLOPs per launch / its average launch duration
+               measured with HIP events on the decode stream, vs the MI355X
+               FP32 matrix peak
+  cpu_baseline the float64 oracle timed on this host on a bounded sample of
+               the same workload (conv_in + the mid block at latent 128x128)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import vaegen  # noqa: E402
+
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+WORKLOADS = {"decode1024": 128, "decode256": 32}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(seed: int, h: int) -> dict:
+    """The oracle, untuned, on conv_in + mid block (resnet, attention over h*h
+    tokens, resnet) of the benchmarked decode: its FLOP rate on this host."""
+    import ctypes
+
+    try:
+        libc = ctypes.CDLL("libc.so.6")
+        libc.mallopt(-4, 0)
+        libc.mallopt(-1, 1 << 30)
+    except OSError:
+        pass
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        cores = os.cpu_count()
+    p = vaegen.decoder_params(seed)
+    z = vaegen.latent(seed, h, h)
+    c = p["conv_in.weight"].shape[0]
+    n = h * h
+    flops = 2.0 * c * 16 * 9 * n                    # conv_in
+    flops += 2 * 2 * (2.0 * c * c * 9 * n)          # two resnets, two 3x3 convs each
+    flops += 8.0 * n * c * c + 4.0 * n * n * c      # attention
+    t = time.perf_counter()
+    x = oracle.conv2d(oracle.denormalize(z, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR), p["conv_in.weight"],
+                      p["conv_in.bias"])
+    x = oracle.resnet(x, p, "mid_block.resnets.0")
+    x = oracle.attention(x, p, "mid_block.attentions.0")
+    x = oracle.resnet(x, p, "mid_block.resnets.1")
+    dt = time.perf_counter() - t
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"float64 oracle on conv_in + mid block (resnet, attention over {n} tokens, resnet) "
+                      f"of the latent [16,{h},{h}] decode: {flops / 1e9:.1f} GFLOP"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode of one image runs on one MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from diffusion_vae_decoder_amd import api
+
+    h = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    params = vaegen.decoder_params(args.seed)
+    dec = api.Decoder({k: torch.from_numpy(v).cuda() for k, v in params.items()}, vaegen.SCALING_FACTOR,
+                      vaegen.SHIFT_FACTOR)
+    z = torch.from_numpy(vaegen.latent(args.seed, h, h)).cuda()
+    co, ho, wo = dec.output_shape(h, h)
+    rgb = torch.empty((co, ho, wo), dtype=torch.float32, device="cuda")
+
+    for _ in range(args.warmup):
+        dec.decode(z, out=rgb)
+    torch.cuda.synchronize()
+
+    # timed region: K decodes, every launch bracketed by HIP events on the stream
+    dec.set_profiling(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dec.decode(z, out=rgb)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    recs = dec.profile()
+    dec.set_profiling(False)
+    ms_per_step = wall * 1e3 / args.steps
+
+    # second measurement without the per-launch events, for the wall time
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dec.decode(z, out=rgb)
+    torch.cuda.synchronize()
+    ms_plain = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = min(ms_per_step, ms_plain)
+
+    flops_per_step = sum(r["flops"] for r in recs) / args.steps
+    by_kernel = {}
+    for r in recs:
+        k = by_kernel.setdefault(r["kernel"], {"ms": 0.0, "flops": 0.0, "bytes": 0.0, "n": 0})
+        k["ms"] += r["ms"]
+        k["flops"] += r["flops"]
+        k["bytes"] += r["bytes"]
+        k["n"] += 1
+    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
+    conv_recs = [r for r in recs if r["kernel"].startswith("conv3x3_mfma")]
+    conv_ms = sum(r["ms"] for r in conv_recs)
+    conv_fl = sum(r["flops"] for r in conv_recs)
+    if dom["flops"] > 0:
+        achieved = dom["flops"] / (dom["ms"] / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None, "kernel": dom_name,
+                "launches_per_step": dom["n"] // args.steps, "avg_launch_ms": dom["ms"] / dom["n"],
+                "flops_per_launch": dom["flops"] / dom["n"]}
+    else:
+        achieved = dom["bytes"] / (dom["ms"] / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom_name,
+                "launches_per_step": dom["n"] // args.steps, "avg_launch_ms": dom["ms"] / dom["n"],
+                "bytes_per_launch": dom["bytes"] / dom["n"]}
+    breakdown = {k: {"ms_per_step": v["ms"] / args.steps, "launches_per_step": v["n"] // args.steps,
+                     "tflops" if v["flops"] else "gbs":
+                         (v["flops"] / (v["ms"] / 1e3) / 1e12) if v["flops"] else (v["bytes"] / (v["ms"] / 1e3) / 1e9)}
+                 for k, v in sorted(by_kernel.items(), key=lambda kv: -kv[1]["ms"])}
+
+    out = {
+        "metric": "VAE decode ms + conv TFLOP/s f32 (% FP32-MFMA peak) at 256² and 1024²",
+        "value": flops_per_step / (ms_per_step / 1e3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded SplitMix64 latent N(0,1) and weights at the stated init; no trained weights)",
+        "config": {"workload": f"FLUX-class AutoencoderKL decode, latent [16,{h},{h}] -> RGB [3,{ho},{wo}], "
+                               "batch 1, f32 NCHW", "latent": [16, h, h], "rgb": [co, ho, wo],
+                   "flops_per_decode": flops_per_step},
+        "conv3x3": {"ms_per_step": conv_ms / args.steps, "tflops": conv_fl / (conv_ms / 1e3) / 1e12,
+                    "frac_fp32_mfma_peak": conv_fl / (conv_ms / 1e3) / 1e12 / PEAK_FP32_MFMA_TFLOPS},
+        "roofline": roof,
+        "kernels": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.seed, h)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,289 @@
+"""Thin torch-facing binding of libvae.so.
+
+Every function here only marshals arguments: it checks that tensors are
+contiguous float32 tensors on the GPU, allocates outputs and workspaces with
+torch (device memory), passes raw pointers and torch's current stream to the
+C ABI, and turns error codes into :class:`VaeError`.  All computation happens
+in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from ctypes import byref, c_int32, c_size_t, c_void_p
+from typing import Dict, List, Optional
+
+import torch
+
+from . import _lib
+from ._lib import VaeAttn, VaeConv, VaeError, VaeNorm, VaeProfRecord, VaeResnet, VaeUp, VaeWeights, check
+
+__all__ = [
+    "VaeError", "conv2d", "conv_in", "groupnorm_silu", "upsample_nearest2x", "attention",
+    "conv3d_causal", "Decoder",
+]
+
+
+def _lib_():
+    return _lib.load()
+
+
+def _stream() -> c_void_p:
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    return t
+
+
+def _out(out: Optional[torch.Tensor], shape, device) -> torch.Tensor:
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    _dev(out, "out")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    return out
+
+
+def _ws(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _conv(weight: torch.Tensor, bias: torch.Tensor, name: str = "conv") -> VaeConv:
+    _dev(weight, name + ".weight")
+    _dev(bias, name + ".bias")
+    if weight.dim() == 2:
+        k = 1
+    else:
+        k = weight.shape[-1]
+    return VaeConv(weight.data_ptr(), bias.data_ptr(), weight.shape[0], weight.shape[1], k)
+
+
+def _norm(gamma: torch.Tensor, beta: torch.Tensor, name: str = "norm") -> VaeNorm:
+    _dev(gamma, name + ".gamma")
+    _dev(beta, name + ".beta")
+    return VaeNorm(gamma.data_ptr(), beta.data_ptr(), gamma.numel())
+
+
+# ---------------------------------------------------------------------------
+# layers
+# ---------------------------------------------------------------------------
+
+def conv2d(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor, upsample2x: bool = False,
+           residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Conv2d (stride 1, pad k/2) of x [cin, h, w], optionally of its nearest-x2
+    upsample, plus an optional residual; returns [cout, H, W]."""
+    lib = _lib_()
+    _dev(x, "x")
+    cin, h, w = x.shape
+    conv = _conv(weight, bias)
+    H, W = (2 * h, 2 * w) if upsample2x else (h, w)
+    if residual is not None:
+        _dev(residual, "residual")
+    y = _out(out, (weight.shape[0], H, W), x.device)
+    nb = c_size_t()
+    check(lib.vae_conv2d_workspace_bytes(byref(conv), byref(nb)))
+    ws = _ws(nb.value, x.device)
+    check(lib.vae_conv2d(x.data_ptr(), cin, h, w, byref(conv), int(bool(upsample2x)), _ptr(residual),
+                         y.data_ptr(), _ptr(ws), nb.value, _stream()))
+    return y
+
+
+def conv_in(z: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor, scaling_factor: float,
+            shift_factor: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """conv_in applied to z / scaling_factor + shift_factor (padding stays zero)."""
+    lib = _lib_()
+    _dev(z, "z")
+    cin, h, w = z.shape
+    conv = _conv(weight, bias)
+    y = _out(out, (weight.shape[0], h, w), z.device)
+    nb = c_size_t()
+    check(lib.vae_conv2d_workspace_bytes(byref(conv), byref(nb)))
+    ws = _ws(nb.value, z.device)
+    check(lib.vae_conv_in(z.data_ptr(), cin, h, w, byref(conv), float(scaling_factor), float(shift_factor),
+                          y.data_ptr(), _ptr(ws), nb.value, _stream()))
+    return y
+
+
+def groupnorm_silu(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, silu: bool = True,
+                   residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GroupNorm(32, eps 1e-6) over x [c, ...], then SiLU, then + residual.
+    ``out`` may be ``x`` itself (in place)."""
+    lib = _lib_()
+    _dev(x, "x")
+    c = x.shape[0]
+    spatial = x.numel() // c
+    norm = _norm(gamma, beta)
+    if residual is not None:
+        _dev(residual, "residual")
+    y = torch.empty_like(x) if out is None else _dev(out, "out")
+    nb = c_size_t()
+    check(lib.vae_groupnorm_workspace_bytes(c, spatial, byref(nb)))
+    ws = _ws(nb.value, x.device)
+    check(lib.vae_groupnorm_silu(x.data_ptr(), c, spatial, byref(norm), int(bool(silu)), _ptr(residual),
+                                 y.data_ptr(), _ptr(ws), nb.value, _stream()))
+    return y
+
+
+def upsample_nearest2x(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    lib = _lib_()
+    _dev(x, "x")
+    c, h, w = x.shape
+    y = _out(out, (c, 2 * h, 2 * w), x.device)
+    check(lib.vae_upsample_nearest2x(x.data_ptr(), c, h, w, y.data_ptr(), _stream()))
+    return y
+
+
+def attention(x: torch.Tensor, p: Dict[str, torch.Tensor], prefix: str,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Mid-block attention; ``p`` holds diffusers-named tensors under ``prefix``
+    (group_norm, to_q, to_k, to_v, to_out.0)."""
+    lib = _lib_()
+    _dev(x, "x")
+    c, h, w = x.shape
+    a = VaeAttn(_norm(p[prefix + ".group_norm.weight"], p[prefix + ".group_norm.bias"]),
+                _conv(p[prefix + ".to_q.weight"], p[prefix + ".to_q.bias"]),
+                _conv(p[prefix + ".to_k.weight"], p[prefix + ".to_k.bias"]),
+                _conv(p[prefix + ".to_v.weight"], p[prefix + ".to_v.bias"]),
+                _conv(p[prefix + ".to_out.0.weight"], p[prefix + ".to_out.0.bias"]))
+    y = _out(out, (c, h, w), x.device)
+    nb = c_size_t()
+    check(lib.vae_attention_workspace_bytes(c, h, w, byref(nb)))
+    ws = _ws(nb.value, x.device)
+    check(lib.vae_attention(x.data_ptr(), c, h, w, byref(a), y.data_ptr(), _ptr(ws), nb.value, _stream()))
+    return y
+
+
+def conv3d_causal(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal 3x3x3 conv of x [cin, t, h, w] (frame 0 replicated twice in front)."""
+    lib = _lib_()
+    _dev(x, "x")
+    cin, t, h, w = x.shape
+    conv = _conv(weight, bias)
+    y = _out(out, (weight.shape[0], t, h, w), x.device)
+    nb = c_size_t()
+    check(lib.vae_conv3d_causal_workspace_bytes(byref(conv), byref(nb)))
+    ws = _ws(nb.value, x.device)
+    check(lib.vae_conv3d_causal(x.data_ptr(), cin, t, h, w, byref(conv), y.data_ptr(), _ptr(ws), nb.value,
+                                _stream()))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# the decoder
+# ---------------------------------------------------------------------------
+
+class Decoder:
+    """The whole FLUX-class decoder behind ``vae_decode``.
+
+    ``params`` maps diffusers tensor names (conv_in.*, mid_block.*,
+    up_blocks.*, conv_norm_out.*, conv_out.*) to float32 GPU tensors.  The
+    library copies them once into its own packed buffer.
+    """
+
+    def __init__(self, params: Dict[str, torch.Tensor], scaling_factor: float, shift_factor: float):
+        lib = _lib_()
+        self._lib = lib
+        p = params
+        self._keep: List = []
+
+        def conv(prefix):
+            return _conv(p[prefix + ".weight"], p[prefix + ".bias"], prefix)
+
+        def norm(prefix):
+            return _norm(p[prefix + ".weight"], p[prefix + ".bias"], prefix)
+
+        def resnet(prefix):
+            sc = VaeConv(None, None, 0, 0, 0)
+            if prefix + ".conv_shortcut.weight" in p:
+                sc = conv(prefix + ".conv_shortcut")
+            return VaeResnet(norm(prefix + ".norm1"), conv(prefix + ".conv1"), norm(prefix + ".norm2"),
+                             conv(prefix + ".conv2"), sc)
+
+        ups = []
+        i = 0
+        while f"up_blocks.{i}.resnets.0.conv1.weight" in p:
+            j = 0
+            rs = []
+            while f"up_blocks.{i}.resnets.{j}.conv1.weight" in p:
+                rs.append(resnet(f"up_blocks.{i}.resnets.{j}"))
+                j += 1
+            arr = (VaeResnet * len(rs))(*rs)
+            self._keep.append(arr)
+            upc = VaeConv(None, None, 0, 0, 0)
+            if f"up_blocks.{i}.upsamplers.0.conv.weight" in p:
+                upc = conv(f"up_blocks.{i}.upsamplers.0.conv")
+            ups.append(VaeUp(len(rs), arr, upc))
+            i += 1
+        ups_arr = (VaeUp * len(ups))(*ups)
+        self._keep.append(ups_arr)
+        attn = VaeAttn(norm("mid_block.attentions.0.group_norm"), conv("mid_block.attentions.0.to_q"),
+                       conv("mid_block.attentions.0.to_k"), conv("mid_block.attentions.0.to_v"),
+                       conv("mid_block.attentions.0.to_out.0"))
+        w = VaeWeights(conv("conv_in"), resnet("mid_block.resnets.0"), attn, resnet("mid_block.resnets.1"),
+                       len(ups), ups_arr, norm("conv_norm_out"), conv("conv_out"), float(scaling_factor),
+                       float(shift_factor))
+        nb = c_size_t()
+        check(lib.vae_decoder_pack_bytes(byref(w), byref(nb)))
+        device = p["conv_in.weight"].device
+        self.device = device
+        self.pack = torch.empty(nb.value, dtype=torch.uint8, device=device)
+        handle = c_void_p()
+        check(lib.vae_decoder_create(byref(handle), byref(w), self.pack.data_ptr(), nb.value, _stream()))
+        self._h = handle
+        self.latent_channels = p["conv_in.weight"].shape[1]
+        self._ws: Optional[torch.Tensor] = None
+
+    def output_shape(self, h: int, w: int):
+        c, ho, wo = c_int32(), c_int32(), c_int32()
+        check(self._lib.vae_decoder_output_shape(self._h, h, w, byref(c), byref(ho), byref(wo)))
+        return c.value, ho.value, wo.value
+
+    def workspace_bytes(self, h: int, w: int) -> int:
+        nb = c_size_t()
+        check(self._lib.vae_decoder_workspace_bytes(self._h, h, w, byref(nb)))
+        return nb.value
+
+    def decode(self, latent: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        _dev(latent, "latent")
+        c, h, w = latent.shape
+        nb = self.workspace_bytes(h, w)
+        if self._ws is None or self._ws.numel() < nb:
+            self._ws = torch.empty(nb, dtype=torch.uint8, device=latent.device)
+        co, ho, wo = self.output_shape(h, w)
+        rgb = torch.empty((co, ho, wo), dtype=torch.float32, device=latent.device) if out is None else _dev(out, "out")
+        check(self._lib.vae_decode(self._h, latent.data_ptr(), h, w, rgb.data_ptr(), self._ws.data_ptr(),
+                                   self._ws.numel(), _stream()))
+        return rgb
+
+    def set_profiling(self, on: bool) -> None:
+        check(self._lib.vae_decoder_set_profiling(self._h, int(bool(on))))
+
+    def profile(self) -> List[dict]:
+        n = c_int32()
+        check(self._lib.vae_decoder_profile(self._h, None, 0, byref(n)))
+        recs = (VaeProfRecord * max(n.value, 1))()
+        check(self._lib.vae_decoder_profile(self._h, recs, n.value, byref(n)))
+        return [{"kernel": r.kernel.decode(), "layer": r.layer.decode(), "ms": float(r.ms),
+                 "flops": float(r.flops), "bytes": float(r.bytes)} for r in recs[:n.value]]
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.vae_decoder_destroy(self._h)
+            self._h = c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

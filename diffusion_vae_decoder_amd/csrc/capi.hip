@@ -1,0 +1,262 @@
+// C ABI of libvae.so: per-layer entry points and error reporting.  Every
+// entry point validates its arguments completely before enqueuing anything.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "vae_internal.h"
+
+namespace vae {
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+void set_error(const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+}
+
+int32_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return VAE_OK;
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return VAE_ERR_HIP;
+}
+
+int32_t check_launch(const char *what) { return hip_status(hipGetLastError(), what); }
+
+}  // namespace vae
+
+using namespace vae;
+
+namespace {
+
+constexpr long long kMaxElems = 1LL << 34;   // per tensor; offsets inside kernels are 64-bit
+constexpr long long kMaxPlane = 1LL << 30;   // h*w per plane; plane offsets are 32-bit
+
+int32_t bad(const char *fmt, ...) {
+    char buf[400];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    set_error("%s", buf);
+    return VAE_ERR_INVALID_ARG;
+}
+
+int32_t unsupported(const char *fmt, ...) {
+    char buf[400];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    set_error("%s", buf);
+    return VAE_ERR_UNSUPPORTED;
+}
+
+int32_t check_conv(const char *who, const vae_conv *c, int kernel_required /* 0 = 1 or 3 */) {
+    if (!c) return bad("%s: conv is NULL", who);
+    if (!c->weight || !c->bias) return bad("%s: conv weight/bias is NULL", who);
+    if (c->out_channels <= 0 || c->in_channels <= 0)
+        return bad("%s: conv channels must be positive (out %d, in %d)", who, c->out_channels, c->in_channels);
+    if (kernel_required ? c->kernel != kernel_required : (c->kernel != 1 && c->kernel != 3))
+        return unsupported("%s: unsupported kernel size %d", who, c->kernel);
+    return VAE_OK;
+}
+
+int32_t check_plane(const char *who, long long c, long long h, long long w) {
+    if (c <= 0 || h <= 0 || w <= 0) return bad("%s: sizes must be positive (c %lld, h %lld, w %lld)", who, c, h, w);
+    if (h * w > kMaxPlane || c * h * w > kMaxElems)
+        return unsupported("%s: tensor [%lld, %lld, %lld] too large", who, c, h, w);
+    return VAE_OK;
+}
+
+size_t conv_ws(const vae_conv *c, int kt) {
+    if (c->kernel == 1) return 0;
+    return conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *vae_last_error(void) { return g_err; }
+
+int32_t vae_abi_version(void) { return VAE_ABI_VERSION; }
+
+int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, size_t *bytes) {
+    int32_t rc = check_conv("vae_conv2d_workspace_bytes", conv, 0);
+    if (rc) return rc;
+    if (!bytes) return bad("vae_conv2d_workspace_bytes: bytes is NULL");
+    *bytes = conv_ws(conv, 1);
+    return VAE_OK;
+}
+
+int32_t vae_conv2d(const float *x, int32_t cin, int32_t h, int32_t w, const vae_conv *conv,
+                   int32_t upsample2x, const float *residual, float *y, void *ws, size_t ws_bytes,
+                   void *stream) {
+    int32_t rc = check_conv("vae_conv2d", conv, 0);
+    if (rc) return rc;
+    if (!x || !y) return bad("vae_conv2d: x or y is NULL");
+    const int H = upsample2x ? 2 * h : h, W = upsample2x ? 2 * w : w;
+    if ((rc = check_plane("vae_conv2d", cin, h, w))) return rc;
+    if ((rc = check_plane("vae_conv2d", conv->out_channels, H, W))) return rc;
+    if (conv->in_channels != cin)
+        return bad("vae_conv2d: conv expects %d input channels, got %d", conv->in_channels, cin);
+    if (x == y) return bad("vae_conv2d: y may not alias x");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (conv->kernel == 1) {
+        if (upsample2x) return unsupported("vae_conv2d: upsample2x needs a 3x3 conv");
+        GemmLaunch g{};
+        g.A = conv->weight; g.lda = cin; g.a_km = 0;
+        g.B = x; g.ldb = (long long)h * w; g.b_nk = 0;
+        g.bias = conv->bias; g.R = residual; g.ldr = (long long)h * w;
+        g.C = y; g.ldc = (long long)h * w;
+        g.M = conv->out_channels; g.N = h * w; g.K = cin; g.alpha = 1.f;
+        return launch_gemm(g, s);
+    }
+    if (conv->out_channels <= 4 && !upsample2x && !residual)
+        return launch_conv3x3_skinny(x, conv->weight, conv->bias, y, cin, conv->out_channels, h, w, s);
+    const size_t need = conv_ws(conv, 1);
+    if (!ws || ws_bytes < need)
+        return set_error("vae_conv2d: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
+    if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 1, static_cast<float *>(ws), s))) return rc;
+    ConvLaunch a{};
+    a.x = x; a.wpk = static_cast<const float *>(ws); a.bias = conv->bias; a.res = residual; a.y = y;
+    a.cin = cin; a.cout = conv->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
+    a.upsample = upsample2x ? 1 : 0;
+    return launch_conv3x3(a, s);
+}
+
+int32_t vae_conv_in(const float *z, int32_t cin, int32_t h, int32_t w, const vae_conv *conv,
+                    float scaling_factor, float shift_factor, float *y, void *ws, size_t ws_bytes,
+                    void *stream) {
+    int32_t rc = check_conv("vae_conv_in", conv, 3);
+    if (rc) return rc;
+    if (!z || !y) return bad("vae_conv_in: z or y is NULL");
+    if ((rc = check_plane("vae_conv_in", cin, h, w))) return rc;
+    if ((rc = check_plane("vae_conv_in", conv->out_channels, h, w))) return rc;
+    if (conv->in_channels != cin) return bad("vae_conv_in: conv expects %d input channels, got %d", conv->in_channels, cin);
+    if (!(scaling_factor != 0.f)) return bad("vae_conv_in: scaling_factor must be non-zero");
+    if (z == y) return bad("vae_conv_in: y may not alias z");
+    const size_t need = conv_ws(conv, 1);
+    if (!ws || ws_bytes < need)
+        return set_error("vae_conv_in: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 1, static_cast<float *>(ws), s))) return rc;
+    ConvLaunch a{};
+    a.x = z; a.wpk = static_cast<const float *>(ws); a.bias = conv->bias; a.y = y;
+    a.cin = cin; a.cout = conv->out_channels; a.H = h; a.W = w; a.T = 1; a.kt = 1;
+    a.denorm = 1; a.dn_scale = scaling_factor; a.dn_shift = shift_factor;
+    return launch_conv3x3(a, s);
+}
+
+int32_t vae_groupnorm_workspace_bytes(int32_t c, int64_t spatial, size_t *bytes) {
+    if (!bytes) return bad("vae_groupnorm_workspace_bytes: bytes is NULL");
+    if (c <= 0 || spatial <= 0) return bad("vae_groupnorm_workspace_bytes: sizes must be positive");
+    if (c % 32) return unsupported("vae_groupnorm_workspace_bytes: channels %d not divisible by 32", c);
+    *bytes = groupnorm_ws_bytes(c, spatial);
+    return VAE_OK;
+}
+
+int32_t vae_groupnorm_silu(const float *x, int32_t c, int64_t spatial, const vae_norm *norm,
+                           int32_t apply_silu, const float *residual, float *y, void *ws,
+                           size_t ws_bytes, void *stream) {
+    if (!x || !y || !norm || !norm->gamma || !norm->beta) return bad("vae_groupnorm_silu: NULL pointer");
+    if (c <= 0 || spatial <= 0) return bad("vae_groupnorm_silu: sizes must be positive");
+    if (norm->channels != c) return bad("vae_groupnorm_silu: norm has %d channels, tensor %d", norm->channels, c);
+    if (c % 32) return unsupported("vae_groupnorm_silu: channels %d not divisible by 32", c);
+    if ((long long)c * spatial > kMaxElems) return unsupported("vae_groupnorm_silu: tensor too large");
+    const size_t need = groupnorm_ws_bytes(c, spatial);
+    if (!ws || ws_bytes < need)
+        return set_error("vae_groupnorm_silu: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
+    return launch_groupnorm(x, c, spatial, norm->gamma, norm->beta, apply_silu ? 1 : 0, residual, y, ws,
+                            static_cast<hipStream_t>(stream));
+}
+
+int32_t vae_upsample_nearest2x(const float *x, int32_t c, int32_t h, int32_t w, float *y, void *stream) {
+    if (!x || !y) return bad("vae_upsample_nearest2x: NULL pointer");
+    int32_t rc = check_plane("vae_upsample_nearest2x", c, 2LL * h, 2LL * w);
+    if (rc) return rc;
+    if (x == y) return bad("vae_upsample_nearest2x: y may not alias x");
+    return launch_upsample2x(x, c, h, w, y, static_cast<hipStream_t>(stream));
+}
+
+int32_t vae_attention_workspace_bytes(int32_t c, int32_t h, int32_t w, size_t *bytes) {
+    if (!bytes) return bad("vae_attention_workspace_bytes: bytes is NULL");
+    int32_t rc = check_plane("vae_attention_workspace_bytes", c, h, w);
+    if (rc) return rc;
+    if (c % 32) return unsupported("vae_attention_workspace_bytes: channels %d not divisible by 32", c);
+    // plus room for the concatenated q/k/v weights and biases
+    *bytes = attention_ws_bytes(c, (long long)h * w) + (((size_t)3 * c * c + 3 * c) * 4 + 512);
+    return VAE_OK;
+}
+
+int32_t vae_attention(const float *x, int32_t c, int32_t h, int32_t w, const vae_attn *attn, float *y,
+                      void *ws, size_t ws_bytes, void *stream) {
+    if (!x || !y || !attn) return bad("vae_attention: NULL pointer");
+    int32_t rc = check_plane("vae_attention", c, h, w);
+    if (rc) return rc;
+    if ((long long)h * w > (1LL << 31) / 2) return unsupported("vae_attention: too many tokens");
+    if (c % 32) return unsupported("vae_attention: channels %d not divisible by 32", c);
+    if (!attn->norm.gamma || !attn->norm.beta || attn->norm.channels != c)
+        return bad("vae_attention: norm missing or has %d channels (want %d)", attn->norm.channels, c);
+    const vae_conv *lin[4] = {&attn->q, &attn->k, &attn->v, &attn->out};
+    for (int i = 0; i < 4; ++i) {
+        if ((rc = check_conv("vae_attention", lin[i], 1))) return rc;
+        if (lin[i]->in_channels != c || lin[i]->out_channels != c)
+            return bad("vae_attention: projection %d is %dx%d, want %dx%d", i, lin[i]->out_channels,
+                       lin[i]->in_channels, c, c);
+    }
+    if (x == y) return bad("vae_attention: y may not alias x");
+    size_t need = 0;
+    vae_attention_workspace_bytes(c, h, w, &need);
+    if (!ws || ws_bytes < need)
+        return set_error("vae_attention: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t base = attention_ws_bytes(c, (long long)h * w);
+    float *wqkv = reinterpret_cast<float *>(static_cast<char *>(ws) + base);
+    float *bqkv = wqkv + (size_t)3 * c * c;
+    const size_t cc = (size_t)c * c * 4;
+    for (int i = 0; i < 3; ++i) {
+        if ((rc = hip_status(hipMemcpyAsync(wqkv + (size_t)i * c * c, lin[i]->weight, cc, hipMemcpyDeviceToDevice, s), "vae_attention: copy"))) return rc;
+        if ((rc = hip_status(hipMemcpyAsync(bqkv + (size_t)i * c, lin[i]->bias, (size_t)c * 4, hipMemcpyDeviceToDevice, s), "vae_attention: copy"))) return rc;
+    }
+    return launch_attention(x, c, h, w, attn->norm.gamma, attn->norm.beta, wqkv, bqkv, attn->out.weight,
+                            attn->out.bias, y, ws, s);
+}
+
+int32_t vae_conv3d_causal_workspace_bytes(const vae_conv *conv, size_t *bytes) {
+    int32_t rc = check_conv("vae_conv3d_causal_workspace_bytes", conv, 3);
+    if (rc) return rc;
+    if (!bytes) return bad("vae_conv3d_causal_workspace_bytes: bytes is NULL");
+    *bytes = conv_ws(conv, 3);
+    return VAE_OK;
+}
+
+int32_t vae_conv3d_causal(const float *x, int32_t cin, int32_t t, int32_t h, int32_t w,
+                          const vae_conv *conv, float *y, void *ws, size_t ws_bytes, void *stream) {
+    int32_t rc = check_conv("vae_conv3d_causal", conv, 3);
+    if (rc) return rc;
+    if (!x || !y) return bad("vae_conv3d_causal: x or y is NULL");
+    if (t <= 0) return bad("vae_conv3d_causal: t must be positive");
+    if ((rc = check_plane("vae_conv3d_causal", (long long)cin * t, h, w))) return rc;
+    if ((rc = check_plane("vae_conv3d_causal", (long long)conv->out_channels * t, h, w))) return rc;
+    if (t > 65535) return unsupported("vae_conv3d_causal: t %d exceeds the grid limit", t);
+    if (conv->in_channels != cin) return bad("vae_conv3d_causal: conv expects %d input channels, got %d", conv->in_channels, cin);
+    if (x == y) return bad("vae_conv3d_causal: y may not alias x");
+    const size_t need = conv_ws(conv, 3);
+    if (!ws || ws_bytes < need)
+        return set_error("vae_conv3d_causal: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 3, static_cast<float *>(ws), s))) return rc;
+    ConvLaunch a{};
+    a.x = x; a.wpk = static_cast<const float *>(ws); a.bias = conv->bias; a.y = y;
+    a.cin = cin; a.cout = conv->out_channels; a.H = h; a.W = w; a.T = t; a.kt = 3;
+    return launch_conv3x3(a, s);
+}
+
+}  // extern "C"

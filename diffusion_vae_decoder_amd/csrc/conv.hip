@@ -1,0 +1,451 @@
+// Convolutions of the FLUX-class VAE decoder on gfx950.
+//
+// conv3x3_mfma: 3x3 (and causal 3x3x3) stride-1 convolution as an implicit
+// GEMM on FP32 MFMA (v_mfma_f32_32x32x2_f32).  The GEMM is
+//     Y[o, p] = sum_k Wp[o, k] * X[k, p] + bias[o] (+ R[o, p])
+// with o the output channel, p the output pixel and k = (input channel,
+// tap): the "GPU plan" of the VAE decode -> GPU handoff note (im2col then
+// one GEMM per layer), but the im2col matrix is never formed.  Instead each
+// workgroup stages, per chunk of 8 input channels, the input tile plus a
+// one-pixel halo in LDS; one staged pixel then feeds all nine taps.  The
+// nearest-x2 upsample (cortiq-engine 0.7.7 `vae`, VaeUpRef) and the latent
+// de-normalisation (VaeDecoder) are applied while staging, so neither is
+// ever written to memory.  Bias and the resnet skip (VaeResnetRef) are added
+// in the epilogue.
+//
+// Workgroup: 256 threads = 4 waves in a 2 x 2 grid; each wave owns a 64 x 64
+// block of the 128 (channels) x 128 (pixels) tile as 2 x 2 MFMA 32x32 tiles.
+// In every MFMA the two lane halves carry two different K indices; K within
+// a chunk is ordered (channel, tap) and lane half h takes the channels
+// [4h, 4h + 4), so both LDS operand reads are one row of 32 consecutive
+// floats per half-wave, and the strides are padded so the two halves fall in
+// different LDS banks.
+//
+// conv3x3_skinny: the 128 -> 3 conv_out.  With 3 output channels the GEMM is
+// far too thin for MFMA; the layer is bound by reading its input, so a direct
+// FMA kernel over LDS-staged halo tiles is used instead.
+
+#include "vae_internal.h"
+
+namespace vae {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kCK = kConvCC * 9;         // K per chunk (72)
+constexpr int kSteps = kCK / 2;          // MFMA k-steps per chunk (36)
+constexpr int kHalfC = kConvCC / 2;      // channels per lane half
+
+// Smallest stride >= base, a multiple of `align`, with (mult * stride) % 64 == 32:
+// the two lane halves of a wave then read disjoint halves of a 64-bank LDS.
+constexpr int bank_split_stride(int base, int mult, int align) {
+    for (int s = base; s < base + 512; ++s)
+        if (s % align == 0 && (mult * s) % 64 == 32) return s;
+    return -1;
+}
+
+constexpr int kLdaW = bank_split_stride(kConvBM, kHalfC * 9, 4);   // weight row stride (136)
+static_assert(kLdaW > 0, "no bank-split stride for the weight tile");
+
+template <int TC>
+struct Geom {
+    static constexpr int TR = kConvBN / TC;                 // tile rows
+    static constexpr int HWD = TC + 2;                       // halo row width
+    static constexpr int HP = (TR + 2) * HWD;                // halo plane
+    static constexpr int PLANE = bank_split_stride(HP, kHalfC, 1);
+    static constexpr int HALO = kConvCC * HP;                // staged halo floats
+    static constexpr int HALO_PER_T = (HALO + kThreads - 1) / kThreads;
+    static_assert(PLANE > 0, "no bank-split stride for the halo tile");
+};
+
+constexpr int kW4 = kCK * kConvBM / 4;                      // float4s of one weight chunk
+constexpr int kW4_PER_T = (kW4 + kThreads - 1) / kThreads;
+
+struct Params {
+    const float *x, *wpk, *bias, *res;
+    float *y;
+    int cin, cout, H, W, Win, kt, n_cb, tiles_x;
+    long long in_cstride, in_fstride, out_cstride, out_fstride;
+    float dn_scale, dn_shift;
+};
+
+enum { MODE_PLAIN = 0, MODE_UPSAMPLE = 1, MODE_DENORM = 2 };
+
+// Global -> registers: chunk `it` = (time tap dt, channel block cb) of the
+// packed weights and of the input halo.
+template <int TC, int MODE>
+__device__ __attribute__((always_inline)) inline void stage_load(
+    const Params &p, const float *wbase, int it, int frame, const int (&h_sp)[Geom<TC>::HALO_PER_T],
+    const int (&h_c)[Geom<TC>::HALO_PER_T], floatx4 (&wreg)[kW4_PER_T],
+    float (&xreg)[Geom<TC>::HALO_PER_T]) {
+    using G = Geom<TC>;
+    const int tid = threadIdx.x;
+    const int dt = it / p.n_cb;
+    const int cb = it - dt * p.n_cb;
+    const floatx4 *wsrc = reinterpret_cast<const floatx4 *>(wbase + (size_t)it * (kCK * kConvBM));
+#pragma unroll
+    for (int i = 0; i < kW4_PER_T; ++i) {
+        const int idx = tid + i * kThreads;
+        if (kW4 % kThreads == 0 || idx < kW4) wreg[i] = wsrc[idx];
+    }
+    int fr = frame + dt - (p.kt - 1);
+    fr = fr < 0 ? 0 : fr;
+    const float *xs = p.x + (long long)fr * p.in_fstride;
+#pragma unroll
+    for (int i = 0; i < G::HALO_PER_T; ++i) {
+        float v = 0.f;
+        const int c = cb * kConvCC + h_c[i];
+        if (h_sp[i] >= 0 && c < p.cin) {
+            v = xs[(long long)c * p.in_cstride + h_sp[i]];
+            if (MODE == MODE_DENORM) v = v / p.dn_scale + p.dn_shift;
+        }
+        xreg[i] = v;
+    }
+}
+
+// Registers -> LDS buffer.
+template <int TC>
+__device__ __attribute__((always_inline)) inline void stage_store(
+    float *lw, float *lx, const int (&h_lds)[Geom<TC>::HALO_PER_T], const floatx4 (&wreg)[kW4_PER_T],
+    const float (&xreg)[Geom<TC>::HALO_PER_T]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kW4_PER_T; ++i) {
+        const int idx = tid + i * kThreads;
+        if (kW4 % kThreads == 0 || idx < kW4) {
+            const int row = idx >> 5, c4 = idx & 31;
+            *reinterpret_cast<floatx4 *>(&lw[row * kLdaW + c4 * 4]) = wreg[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < Geom<TC>::HALO_PER_T; ++i)
+        if (h_lds[i] >= 0) lx[h_lds[i]] = xreg[i];
+}
+
+template <int TC, int MODE, bool RES>
+__global__ __launch_bounds__(kThreads) void conv3x3_mfma(Params p) {
+    using G = Geom<TC>;
+    __shared__ __attribute__((aligned(16))) float lds_w[2][kCK * kLdaW];
+    __shared__ float lds_x[2][kConvCC * G::PLANE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int half = lane >> 5, l32 = lane & 31;
+
+    const int tile = blockIdx.x;
+    const int ty = tile / p.tiles_x;
+    const int tx = tile - ty * p.tiles_x;
+    const int y0 = ty * G::TR, x0 = tx * TC;
+    const int ob = blockIdx.y;
+    const int frame = blockIdx.z;
+
+    // Per-thread halo elements: their LDS slot, channel within the chunk and
+    // spatial offset in the source plane (-1 = zero padding).  They are the
+    // same for every chunk.
+    int h_lds[G::HALO_PER_T], h_sp[G::HALO_PER_T], h_c[G::HALO_PER_T];
+#pragma unroll
+    for (int i = 0; i < G::HALO_PER_T; ++i) {
+        const int e = tid + i * kThreads;
+        h_lds[i] = -1;
+        h_sp[i] = -1;
+        h_c[i] = 0;
+        if (e < G::HALO) {
+            const int c = e / G::HP;
+            const int rem = e - c * G::HP;
+            const int rr = rem / G::HWD;
+            const int cc = rem - rr * G::HWD;
+            const int yy = y0 - 1 + rr, xx = x0 - 1 + cc;
+            h_lds[i] = c * G::PLANE + rr * G::HWD + cc;
+            h_c[i] = c;
+            if (yy >= 0 && yy < p.H && xx >= 0 && xx < p.W)
+                h_sp[i] = (MODE == MODE_UPSAMPLE) ? (yy >> 1) * p.Win + (xx >> 1) : yy * p.W + xx;
+        }
+    }
+
+    const int n_iter = p.kt * p.n_cb;
+    const float *wbase = p.wpk + (size_t)ob * n_iter * (kCK * kConvBM);
+
+    floatx4 wreg[kW4_PER_T];
+    float xreg[G::HALO_PER_T];
+
+    // Operand addresses of this lane (the per-step parts are immediates).
+    int a_off[2], b_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a_off[i] = half * (kHalfC * 9) * kLdaW + wm * 64 + i * 32 + l32;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int n = wn * 64 + j * 32 + l32;
+        const int r = n / TC, col = n - (n / TC) * TC;
+        b_off[j] = half * kHalfC * G::PLANE + r * G::HWD + col;
+    }
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    stage_load<TC, MODE>(p, wbase, 0, frame, h_sp, h_c, wreg, xreg);
+    stage_store<TC>(lds_w[0], lds_x[0], h_lds, wreg, xreg);
+    __syncthreads();
+
+    for (int it = 0; it < n_iter; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < n_iter) stage_load<TC, MODE>(p, wbase, it + 1, frame, h_sp, h_c, wreg, xreg);
+        const float *A = lds_w[buf];
+        const float *B = lds_x[buf];
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+            const int cl = s / 9, tap = s % 9;
+            const int boff = cl * G::PLANE + (tap / 3) * G::HWD + (tap % 3);
+            const float a0 = A[a_off[0] + s * kLdaW];
+            const float a1 = A[a_off[1] + s * kLdaW];
+            const float b0 = B[b_off[0] + boff];
+            const float b1 = B[b_off[1] + boff];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        }
+        if (it + 1 < n_iter) stage_store<TC>(lds_w[buf ^ 1], lds_x[buf ^ 1], h_lds, wreg, xreg);
+        __syncthreads();
+    }
+
+    // Epilogue: D[i][j] of a 32x32 MFMA tile sits in lane j + 32*((i/4)%2),
+    // register (i%4) + 4*(i/8).
+    const long long fo = (long long)frame * p.out_fstride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = wn * 64 + j * 32 + l32;
+            const int yy = y0 + n / TC, xx = x0 + (n - (n / TC) * TC);
+            if (yy >= p.H || xx >= p.W) continue;
+            const long long sp = fo + (long long)yy * p.W + xx;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const int o = ob * kConvBM + m;
+                if (o < p.cout) {
+                    const long long off = (long long)o * p.out_cstride + sp;
+                    float v = acc[i][j][r] + p.bias[o];
+                    if (RES) v += p.res[off];
+                    p.y[off] = v;
+                }
+            }
+        }
+    }
+}
+
+// Packed layout: [ob][dt][cb][k = c_local * 9 + tap][m], m in [0, 128);
+// zero where the output channel or input channel is out of range.
+__global__ void pack_conv3x3_kernel(const float *__restrict__ w, float *__restrict__ dst, int cout,
+                                    int cin, int kt, int n_cb, long long total) {
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    const int m = (int)(idx % kConvBM);
+    long long rest = idx / kConvBM;
+    const int k = (int)(rest % kCK);
+    rest /= kCK;
+    const int cb = (int)(rest % n_cb);
+    rest /= n_cb;
+    const int dt = (int)(rest % kt);
+    const int ob = (int)(rest / kt);
+    const int o = ob * kConvBM + m;
+    const int c = cb * kConvCC + k / 9;
+    const int tap = k % 9;
+    float v = 0.f;
+    if (o < cout && c < cin) v = w[(((long long)o * cin + c) * kt + dt) * 9 + tap];
+    dst[idx] = v;
+}
+
+template <int TC, int MODE, bool RES>
+void launch_t(const Params &p, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((conv3x3_mfma<TC, MODE, RES>), grid, dim3(kThreads), 0, s, p);
+}
+
+template <int TC>
+void launch_tc(const Params &p, int mode, bool res, dim3 grid, hipStream_t s) {
+    if (mode == MODE_UPSAMPLE) {
+        if (res) launch_t<TC, MODE_UPSAMPLE, true>(p, grid, s);
+        else launch_t<TC, MODE_UPSAMPLE, false>(p, grid, s);
+    } else if (mode == MODE_DENORM) {
+        if (res) launch_t<TC, MODE_DENORM, true>(p, grid, s);
+        else launch_t<TC, MODE_DENORM, false>(p, grid, s);
+    } else {
+        if (res) launch_t<TC, MODE_PLAIN, true>(p, grid, s);
+        else launch_t<TC, MODE_PLAIN, false>(p, grid, s);
+    }
+}
+
+// ---------------------------------------------------------------- conv_out
+constexpr int kSkR = 8;          // tile rows
+constexpr int kSkC = 128;        // tile columns (4 per thread)
+constexpr int kSkCC = 8;         // channels per chunk
+constexpr int kSkHW = kSkC + 2;
+constexpr int kSkHP = (kSkR + 2) * kSkHW;
+
+template <int COUT>
+__global__ __launch_bounds__(kThreads) void conv3x3_skinny(const float *__restrict__ x,
+                                                           const float *__restrict__ w,
+                                                           const float *__restrict__ bias,
+                                                           float *__restrict__ y, int cin, int H,
+                                                           int W, int tiles_x) {
+    __shared__ float halo[kSkCC * kSkHP];
+    __shared__ float wt[COUT * kSkCC * 9];
+    const int tid = threadIdx.x;
+    const int ty = blockIdx.x / tiles_x, tx = blockIdx.x - (blockIdx.x / tiles_x) * tiles_x;
+    const int y0 = ty * kSkR, x0 = tx * kSkC;
+    const int r = tid >> 5, cg = tid & 31;
+    const long long plane = (long long)H * W;
+
+    float acc[COUT][4];
+#pragma unroll
+    for (int o = 0; o < COUT; ++o)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[o][q] = 0.f;
+
+    for (int c0 = 0; c0 < cin; c0 += kSkCC) {
+        for (int e = tid; e < kSkCC * kSkHP; e += kThreads) {
+            const int c = e / kSkHP;
+            const int rem = e - c * kSkHP;
+            const int rr = rem / kSkHW, cc = rem - (rem / kSkHW) * kSkHW;
+            const int yy = y0 - 1 + rr, xx = x0 - 1 + cc;
+            float v = 0.f;
+            if (c0 + c < cin && yy >= 0 && yy < H && xx >= 0 && xx < W)
+                v = x[(long long)(c0 + c) * plane + (long long)yy * W + xx];
+            halo[e] = v;
+        }
+        for (int e = tid; e < COUT * kSkCC * 9; e += kThreads) {
+            const int o = e / (kSkCC * 9);
+            const int rem = e - o * (kSkCC * 9);
+            const int c = rem / 9, tap = rem - (rem / 9) * 9;
+            wt[e] = (c0 + c < cin) ? w[((long long)o * cin + c0 + c) * 9 + tap] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int c = 0; c < kSkCC; ++c) {
+#pragma unroll
+            for (int dy = 0; dy < 3; ++dy) {
+                const float *row = &halo[c * kSkHP + (r + dy) * kSkHW + cg * 4];
+                float v[6];
+#pragma unroll
+                for (int q = 0; q < 6; ++q) v[q] = row[q];
+#pragma unroll
+                for (int dx = 0; dx < 3; ++dx) {
+#pragma unroll
+                    for (int o = 0; o < COUT; ++o) {
+                        const float wv = wt[(o * kSkCC + c) * 9 + dy * 3 + dx];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[o][q] = fmaf(wv, v[q + dx], acc[o][q]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    const int yy = y0 + r;
+    if (yy >= H) return;
+#pragma unroll
+    for (int o = 0; o < COUT; ++o)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int xx = x0 + cg * 4 + q;
+            if (xx < W) y[(long long)o * plane + (long long)yy * W + xx] = acc[o][q] + bias[o];
+        }
+}
+
+}  // namespace
+
+size_t conv3x3_packed_floats(int cout, int cin, int kt) {
+    const size_t n_ob = (size_t)(cout + kConvBM - 1) / kConvBM;
+    const size_t n_cb = (size_t)(cin + kConvCC - 1) / kConvCC;
+    return n_ob * (size_t)kt * n_cb * kCK * kConvBM;
+}
+
+int32_t pack_conv3x3(const float *w, int cout, int cin, int kt, float *dst, hipStream_t s) {
+    const int n_cb = (cin + kConvCC - 1) / kConvCC;
+    const long long total = (long long)conv3x3_packed_floats(cout, cin, kt);
+    const int threads = 256;
+    const long long blocks = (total + threads - 1) / threads;
+    hipLaunchKernelGGL(pack_conv3x3_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, w, dst,
+                       cout, cin, kt, n_cb, total);
+    return check_launch("pack_conv3x3");
+}
+
+namespace {
+int conv_tc(int W) { return W > 16 ? 32 : (W > 8 ? 16 : 8); }
+}  // namespace
+
+const char *conv3x3_kernel_name(const ConvLaunch &a) {
+    static const char *names[3][3][2] = {
+        {{"conv3x3_mfma<32,plain>", "conv3x3_mfma<32,plain,res>"},
+         {"conv3x3_mfma<32,up2x>", "conv3x3_mfma<32,up2x,res>"},
+         {"conv3x3_mfma<32,denorm>", "conv3x3_mfma<32,denorm,res>"}},
+        {{"conv3x3_mfma<16,plain>", "conv3x3_mfma<16,plain,res>"},
+         {"conv3x3_mfma<16,up2x>", "conv3x3_mfma<16,up2x,res>"},
+         {"conv3x3_mfma<16,denorm>", "conv3x3_mfma<16,denorm,res>"}},
+        {{"conv3x3_mfma<8,plain>", "conv3x3_mfma<8,plain,res>"},
+         {"conv3x3_mfma<8,up2x>", "conv3x3_mfma<8,up2x,res>"},
+         {"conv3x3_mfma<8,denorm>", "conv3x3_mfma<8,denorm,res>"}}};
+    const int tc = conv_tc(a.W);
+    const int ti = tc == 32 ? 0 : (tc == 16 ? 1 : 2);
+    const int mi = a.upsample ? 1 : (a.denorm ? 2 : 0);
+    return names[ti][mi][a.res ? 1 : 0];
+}
+
+int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s) {
+    Params p;
+    p.x = a.x;
+    p.wpk = a.wpk;
+    p.bias = a.bias;
+    p.res = a.res;
+    p.y = a.y;
+    p.cin = a.cin;
+    p.cout = a.cout;
+    p.H = a.H;
+    p.W = a.W;
+    p.Win = a.upsample ? a.W / 2 : a.W;
+    const int Hin = a.upsample ? a.H / 2 : a.H;
+    p.kt = a.kt;
+    p.n_cb = (a.cin + kConvCC - 1) / kConvCC;
+    p.in_fstride = (long long)Hin * p.Win;
+    p.in_cstride = p.in_fstride * a.T;
+    p.out_fstride = (long long)a.H * a.W;
+    p.out_cstride = p.out_fstride * a.T;
+    p.dn_scale = a.dn_scale;
+    p.dn_shift = a.dn_shift;
+    const int TC = conv_tc(a.W);
+    const int TR = kConvBN / TC;
+    p.tiles_x = (a.W + TC - 1) / TC;
+    const int tiles_y = (a.H + TR - 1) / TR;
+    const dim3 grid((unsigned)(p.tiles_x * tiles_y), (unsigned)((a.cout + kConvBM - 1) / kConvBM),
+                    (unsigned)a.T);
+    const int mode = a.upsample ? MODE_UPSAMPLE : (a.denorm ? MODE_DENORM : MODE_PLAIN);
+    const bool res = a.res != nullptr;
+    if (TC == 32) launch_tc<32>(p, mode, res, grid, s);
+    else if (TC == 16) launch_tc<16>(p, mode, res, grid, s);
+    else launch_tc<8>(p, mode, res, grid, s);
+    return check_launch("conv3x3_mfma");
+}
+
+int32_t launch_conv3x3_skinny(const float *x, const float *w, const float *bias, float *y, int cin,
+                              int cout, int H, int W, hipStream_t s) {
+    const int tiles_x = (W + kSkC - 1) / kSkC;
+    const int tiles_y = (H + kSkR - 1) / kSkR;
+    const dim3 grid((unsigned)(tiles_x * tiles_y));
+    switch (cout) {
+        case 1: hipLaunchKernelGGL(conv3x3_skinny<1>, grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W, tiles_x); break;
+        case 2: hipLaunchKernelGGL(conv3x3_skinny<2>, grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W, tiles_x); break;
+        case 3: hipLaunchKernelGGL(conv3x3_skinny<3>, grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W, tiles_x); break;
+        case 4: hipLaunchKernelGGL(conv3x3_skinny<4>, grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W, tiles_x); break;
+        default: set_error("conv3x3_skinny: out_channels %d > 4", cout); return VAE_ERR_UNSUPPORTED;
+    }
+    return check_launch("conv3x3_skinny");
+}
+
+}  // namespace vae

@@ -1,0 +1,561 @@
+// The decoder chain (cortiq-engine 0.7.7 `vae`, VaeChainArgs / VaeDecoder):
+// conv_in (with the latent de-normalisation in its gather) -> mid resnet ->
+// mid attention -> mid resnet -> up blocks (resnets, then nearest x2 folded
+// into the upsample conv) -> GroupNorm + SiLU -> conv_out.
+//
+// vae_decoder_create copies every weight once into the caller's `pack`
+// buffer (3x3 weights already in the conv kernel's layout, q/k/v
+// concatenated), so a decode launches kernels only.  All activations live in
+// the caller's workspace, reused across layers:
+//   X (block input) | Y (block output) | T, U (resnet temporaries) | S (1x1 skip)
+// each sized for the largest activation of the chain, plus GroupNorm
+// partials and the attention workspace.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "vae_internal.h"
+
+using namespace vae;
+
+namespace {
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct DConv {
+    const float *w = nullptr;   // packed (3x3) or raw [cout, cin] (1x1)
+    const float *b = nullptr;
+    int cout = 0, cin = 0, k = 0;
+    bool present = false;
+};
+struct DNorm {
+    const float *g = nullptr, *b = nullptr;
+    int c = 0;
+};
+struct DRes {
+    DNorm n1, n2;
+    DConv c1, c2, sc;
+    std::string name;
+};
+struct DAttn {
+    DNorm n;
+    const float *wqkv = nullptr, *bqkv = nullptr, *wo = nullptr, *bo = nullptr;
+    int c = 0;
+};
+struct DUp {
+    std::vector<DRes> res;
+    DConv up;
+};
+
+struct ProfEntry {
+    hipEvent_t start = nullptr, stop = nullptr;
+    std::string kernel, layer;
+    double flops = 0, bytes = 0;
+};
+
+// Walks the weights once to size the pack (dst == nullptr) or to fill it.
+struct Packer {
+    char *dst;
+    size_t off = 0;
+    hipStream_t s;
+    int32_t rc = VAE_OK;
+
+    const float *take(size_t floats) {
+        const size_t at = off;
+        off += align256(floats * 4);
+        return dst ? reinterpret_cast<const float *>(dst + at) : nullptr;
+    }
+    const float *copy(const float *src, size_t floats) {
+        const float *d = take(floats);
+        if (dst && rc == VAE_OK)
+            rc = hip_status(hipMemcpyAsync(const_cast<float *>(d), src, floats * 4, hipMemcpyDeviceToDevice, s),
+                            "vae_decoder_create: copy");
+        return d;
+    }
+    // raw3: keep a 3x3 weight in its own [cout, cin, 3, 3] layout (the
+    // direct conv_out kernel reads that); otherwise 3x3 weights are repacked.
+    DConv conv(const vae_conv &c, bool raw3 = false) {
+        DConv d;
+        d.present = true;
+        d.cout = c.out_channels;
+        d.cin = c.in_channels;
+        d.k = c.kernel;
+        if (c.kernel == 3 && raw3) {
+            d.w = copy(c.weight, (size_t)c.out_channels * c.in_channels * 9);
+        } else if (c.kernel == 3) {
+            const float *p = take(conv3x3_packed_floats(c.out_channels, c.in_channels, 1));
+            if (dst && rc == VAE_OK) rc = pack_conv3x3(c.weight, c.out_channels, c.in_channels, 1, const_cast<float *>(p), s);
+            d.w = p;
+        } else {
+            d.w = copy(c.weight, (size_t)c.out_channels * c.in_channels);
+        }
+        d.b = copy(c.bias, c.out_channels);
+        return d;
+    }
+    DNorm norm(const vae_norm &n) {
+        DNorm d;
+        d.c = n.channels;
+        d.g = copy(n.gamma, n.channels);
+        d.b = copy(n.beta, n.channels);
+        return d;
+    }
+    DRes resnet(const vae_resnet &r, const std::string &name) {
+        DRes d;
+        d.name = name;
+        d.n1 = norm(r.norm1);
+        d.c1 = conv(r.conv1);
+        d.n2 = norm(r.norm2);
+        d.c2 = conv(r.conv2);
+        if (r.shortcut.weight) d.sc = conv(r.shortcut);
+        return d;
+    }
+    DAttn attn(const vae_attn &a) {
+        DAttn d;
+        d.c = a.norm.channels;
+        d.n = norm(a.norm);
+        const size_t cc = (size_t)d.c * d.c;
+        float *wqkv = const_cast<float *>(take(3 * cc));
+        float *bqkv = const_cast<float *>(take(3 * (size_t)d.c));
+        if (dst) {
+            const vae_conv *qkv[3] = {&a.q, &a.k, &a.v};
+            for (int i = 0; i < 3 && rc == VAE_OK; ++i) {
+                rc = hip_status(hipMemcpyAsync(wqkv + i * cc, qkv[i]->weight, cc * 4, hipMemcpyDeviceToDevice, s), "vae_decoder_create: copy");
+                if (rc == VAE_OK)
+                    rc = hip_status(hipMemcpyAsync(bqkv + (size_t)i * d.c, qkv[i]->bias, (size_t)d.c * 4, hipMemcpyDeviceToDevice, s), "vae_decoder_create: copy");
+            }
+        }
+        d.wqkv = wqkv;
+        d.bqkv = bqkv;
+        d.wo = copy(a.out.weight, cc);
+        d.bo = copy(a.out.bias, d.c);
+        return d;
+    }
+};
+
+int32_t fail(int32_t code, const char *fmt, ...) {
+    char buf[400];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    set_error("%s", buf);
+    return code;
+}
+
+int32_t check_conv_shape(const char *what, const vae_conv &c, int k, int cin, int cout) {
+    if (!c.weight || !c.bias) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: %s weight/bias is NULL", what);
+    if (c.kernel != k) return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_create: %s kernel %d, want %d", what, c.kernel, k);
+    if (c.in_channels != cin || (cout > 0 && c.out_channels != cout))
+        return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: %s is %d->%d, want %d->%d", what, c.in_channels,
+                    c.out_channels, cin, cout);
+    if (c.out_channels <= 0) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: %s has no outputs", what);
+    return VAE_OK;
+}
+
+int32_t check_norm(const char *what, const vae_norm &n, int c) {
+    if (!n.gamma || !n.beta) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: %s gamma/beta is NULL", what);
+    if (n.channels != c) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: %s has %d channels, want %d", what, n.channels, c);
+    if (c % 32) return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_create: %s channels %d not divisible by 32", what, c);
+    return VAE_OK;
+}
+
+int32_t check_resnet(const std::string &name, const vae_resnet &r, int cin, int *cout) {
+    int32_t rc;
+    const int co = r.conv1.out_channels;
+    if ((rc = check_norm((name + ".norm1").c_str(), r.norm1, cin))) return rc;
+    if ((rc = check_conv_shape((name + ".conv1").c_str(), r.conv1, 3, cin, -1))) return rc;
+    if ((rc = check_norm((name + ".norm2").c_str(), r.norm2, co))) return rc;
+    if ((rc = check_conv_shape((name + ".conv2").c_str(), r.conv2, 3, co, co))) return rc;
+    if (r.shortcut.weight) {
+        if ((rc = check_conv_shape((name + ".conv_shortcut").c_str(), r.shortcut, 1, cin, co))) return rc;
+    } else if (cin != co) {
+        return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: %s changes channels %d->%d without a shortcut",
+                    name.c_str(), cin, co);
+    }
+    *cout = co;
+    return VAE_OK;
+}
+
+int32_t validate(const vae_weights *w) {
+    if (!w) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: weights is NULL");
+    int32_t rc;
+    const int zc = w->conv_in.in_channels;
+    if (zc <= 0) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: conv_in has no inputs");
+    if ((rc = check_conv_shape("conv_in", w->conv_in, 3, zc, -1))) return rc;
+    if (!(w->scaling_factor != 0.f)) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: scaling_factor is 0");
+    int c = w->conv_in.out_channels;
+    if ((rc = check_resnet("mid_block.resnets.0", w->mid_res0, c, &c))) return rc;
+    if ((rc = check_norm("mid_block.attentions.0.group_norm", w->mid_attn.norm, c))) return rc;
+    const vae_conv *lin[4] = {&w->mid_attn.q, &w->mid_attn.k, &w->mid_attn.v, &w->mid_attn.out};
+    for (int i = 0; i < 4; ++i)
+        if ((rc = check_conv_shape("mid_block.attentions.0 projection", *lin[i], 1, c, c))) return rc;
+    if ((rc = check_resnet("mid_block.resnets.1", w->mid_res1, c, &c))) return rc;
+    if (w->n_up <= 0 || !w->ups) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: no up blocks");
+    for (int i = 0; i < w->n_up; ++i) {
+        const vae_up &u = w->ups[i];
+        if (u.n_resnets <= 0 || !u.resnets) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: up block %d has no resnets", i);
+        for (int j = 0; j < u.n_resnets; ++j) {
+            const std::string name = "up_blocks." + std::to_string(i) + ".resnets." + std::to_string(j);
+            if ((rc = check_resnet(name, u.resnets[j], c, &c))) return rc;
+        }
+        if (u.upsample.weight)
+            if ((rc = check_conv_shape("upsample conv", u.upsample, 3, c, c))) return rc;
+    }
+    if ((rc = check_norm("conv_norm_out", w->norm_out, c))) return rc;
+    if ((rc = check_conv_shape("conv_out", w->conv_out, 3, c, -1))) return rc;
+    return VAE_OK;
+}
+
+}  // namespace
+
+struct vae_decoder {
+    DConv conv_in;
+    DRes mid0, mid1;
+    DAttn attn;
+    std::vector<DUp> ups;
+    DNorm norm_out;
+    DConv conv_out;
+    float scaling = 1.f, shift = 0.f;
+    int latent_c = 0;
+    // profiling
+    bool profiling = false;
+    std::vector<ProfEntry> prof;
+    size_t prof_used = 0;
+};
+
+namespace {
+
+struct Buffers {
+    float *X, *Y, *T, *U, *S;
+    void *gn;
+    void *attn;
+};
+
+// The chain's spatial plan for a latent of (h, w): largest activation (floats),
+// largest GroupNorm workspace, attention workspace.
+struct Plan {
+    size_t act = 0, gn = 0, attn = 0;
+};
+
+Plan plan_for(const vae_decoder *d, int h, int w) {
+    Plan p;
+    auto act = [&](long long c, long long H, long long W) {
+        const size_t n = (size_t)(c * H * W);
+        if (n > p.act) p.act = n;
+    };
+    auto gn = [&](long long c, long long H, long long W) {
+        const size_t b = groupnorm_ws_bytes((int)c, H * W);
+        if (b > p.gn) p.gn = b;
+    };
+    long long H = h, W = w;
+    act(d->latent_c, H, W);
+    act(d->conv_in.cout, H, W);
+    auto res = [&](const DRes &r) {
+        gn(r.c1.cin, H, W);
+        gn(r.c1.cout, H, W);
+        act(r.c1.cin, H, W);
+        act(r.c1.cout, H, W);
+    };
+    res(d->mid0);
+    p.attn = attention_ws_bytes(d->attn.c, H * W);
+    res(d->mid1);
+    for (const DUp &u : d->ups) {
+        for (const DRes &r : u.res) res(r);
+        if (u.up.present) {
+            H *= 2;
+            W *= 2;
+            act(u.up.cout, H, W);
+        }
+    }
+    gn(d->norm_out.c, H, W);
+    return p;
+}
+
+double conv_flops(const DConv &c, long long H, long long W) { return 2.0 * c.cout * c.cin * c.k * c.k * (double)(H * W); }
+
+struct Runner {
+    vae_decoder *d;
+    hipStream_t s;
+    int32_t rc = VAE_OK;
+
+    ProfEntry *begin(const char *kernel, const std::string &layer, double flops, double bytes) {
+        if (!d->profiling || rc != VAE_OK) return nullptr;
+        if (d->prof_used == d->prof.size()) {
+            ProfEntry e;
+            if ((rc = hip_status(hipEventCreate(&e.start), "hipEventCreate")) != VAE_OK) return nullptr;
+            if ((rc = hip_status(hipEventCreate(&e.stop), "hipEventCreate")) != VAE_OK) return nullptr;
+            d->prof.push_back(e);
+        }
+        ProfEntry *e = &d->prof[d->prof_used++];
+        e->kernel = kernel;
+        e->layer = layer;
+        e->flops = flops;
+        e->bytes = bytes;
+        rc = hip_status(hipEventRecord(e->start, s), "hipEventRecord");
+        return e;
+    }
+    void end(ProfEntry *e) {
+        if (e && rc == VAE_OK) rc = hip_status(hipEventRecord(e->stop, s), "hipEventRecord");
+    }
+
+    void conv3(const std::string &layer, const DConv &c, const float *x, int H, int W, bool up,
+               const float *res, float *y, bool denorm = false) {
+        if (rc != VAE_OK) return;
+        ConvLaunch a{};
+        a.x = x;
+        a.wpk = c.w;
+        a.bias = c.b;
+        a.res = res;
+        a.y = y;
+        a.cin = c.cin;
+        a.cout = c.cout;
+        a.H = H;
+        a.W = W;
+        a.T = 1;
+        a.kt = 1;
+        a.upsample = up ? 1 : 0;
+        a.denorm = denorm ? 1 : 0;
+        a.dn_scale = d->scaling;
+        a.dn_shift = d->shift;
+        const double in_elems = (double)c.cin * H * W / (up ? 4.0 : 1.0);
+        const double bytes = 4.0 * (in_elems + (double)c.cout * H * W * (res ? 2.0 : 1.0));
+        ProfEntry *e = begin(conv3x3_kernel_name(a), layer, conv_flops(c, H, W), bytes);
+        if (rc != VAE_OK) return;
+        rc = launch_conv3x3(a, s);
+        end(e);
+    }
+    void conv1(const std::string &layer, const DConv &c, const float *x, int H, int W, float *y) {
+        if (rc != VAE_OK) return;
+        GemmLaunch g{};
+        g.A = c.w;
+        g.lda = c.cin;
+        g.B = x;
+        g.ldb = (long long)H * W;
+        g.bias = c.b;
+        g.C = y;
+        g.ldc = (long long)H * W;
+        g.M = c.cout;
+        g.N = H * W;
+        g.K = c.cin;
+        g.alpha = 1.f;
+        ProfEntry *e = begin("gemm_mfma", layer, conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
+        if (rc != VAE_OK) return;
+        rc = launch_gemm(g, s);
+        end(e);
+    }
+    void gn(const std::string &layer, const DNorm &n, const float *x, long long spatial, float *y, void *ws) {
+        if (rc != VAE_OK) return;
+        ProfEntry *e = begin("groupnorm_silu", layer, 0.0, 8.0 * n.c * (double)spatial);
+        if (rc != VAE_OK) return;
+        rc = launch_groupnorm(x, n.c, spatial, n.g, n.b, 1, nullptr, y, ws, s);
+        end(e);
+    }
+    // X -> Y; uses T, U (and S for a 1x1 skip).
+    void resnet(const DRes &r, Buffers &b, int H, int W) {
+        const long long sp = (long long)H * W;
+        gn(r.name + ".norm1", r.n1, b.X, sp, b.T, b.gn);
+        conv3(r.name + ".conv1", r.c1, b.T, H, W, false, nullptr, b.U);
+        gn(r.name + ".norm2", r.n2, b.U, sp, b.U, b.gn);
+        const float *skip = b.X;
+        if (r.sc.present) {
+            conv1(r.name + ".conv_shortcut", r.sc, b.X, H, W, b.S);
+            skip = b.S;
+        }
+        conv3(r.name + ".conv2", r.c2, b.U, H, W, false, skip, b.Y);
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+int32_t vae_decoder_pack_bytes(const vae_weights *w, size_t *bytes) {
+    int32_t rc = validate(w);
+    if (rc) return rc;
+    if (!bytes) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_pack_bytes: bytes is NULL");
+    Packer p{nullptr, 0, nullptr};
+    p.conv(w->conv_in);
+    p.resnet(w->mid_res0, "");
+    p.attn(w->mid_attn);
+    p.resnet(w->mid_res1, "");
+    for (int i = 0; i < w->n_up; ++i) {
+        for (int j = 0; j < w->ups[i].n_resnets; ++j) p.resnet(w->ups[i].resnets[j], "");
+        if (w->ups[i].upsample.weight) p.conv(w->ups[i].upsample);
+    }
+    p.norm(w->norm_out);
+    p.conv(w->conv_out, w->conv_out.out_channels <= 4);
+    *bytes = p.off;
+    return VAE_OK;
+}
+
+int32_t vae_decoder_create(vae_decoder **out, const vae_weights *w, void *pack, size_t pack_bytes, void *stream) {
+    if (!out) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: out is NULL");
+    *out = nullptr;
+    size_t need = 0;
+    int32_t rc = vae_decoder_pack_bytes(w, &need);
+    if (rc) return rc;
+    if (!pack || pack_bytes < need)
+        return fail(VAE_ERR_WORKSPACE, "vae_decoder_create: pack buffer %zu bytes < %zu", pack_bytes, need);
+    if (reinterpret_cast<uintptr_t>(pack) & 255)
+        return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: pack buffer must be 256-byte aligned");
+    vae_decoder *d = new vae_decoder();
+    Packer p{static_cast<char *>(pack), 0, static_cast<hipStream_t>(stream)};
+    d->conv_in = p.conv(w->conv_in);
+    d->mid0 = p.resnet(w->mid_res0, "mid_block.resnets.0");
+    d->attn = p.attn(w->mid_attn);
+    d->mid1 = p.resnet(w->mid_res1, "mid_block.resnets.1");
+    for (int i = 0; i < w->n_up; ++i) {
+        DUp u;
+        for (int j = 0; j < w->ups[i].n_resnets; ++j)
+            u.res.push_back(p.resnet(w->ups[i].resnets[j], "up_blocks." + std::to_string(i) + ".resnets." + std::to_string(j)));
+        if (w->ups[i].upsample.weight) u.up = p.conv(w->ups[i].upsample);
+        d->ups.push_back(u);
+    }
+    d->norm_out = p.norm(w->norm_out);
+    d->conv_out = p.conv(w->conv_out, w->conv_out.out_channels <= 4);
+    d->scaling = w->scaling_factor;
+    d->shift = w->shift_factor;
+    d->latent_c = w->conv_in.in_channels;
+    if (p.rc != VAE_OK) {
+        delete d;
+        return p.rc;
+    }
+    *out = d;
+    return VAE_OK;
+}
+
+int32_t vae_decoder_output_shape(const vae_decoder *d, int32_t h, int32_t w, int32_t *c, int32_t *ho, int32_t *wo) {
+    if (!d || !c || !ho || !wo) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_output_shape: NULL pointer");
+    long long H = h, W = w;
+    for (const DUp &u : d->ups)
+        if (u.up.present) {
+            H *= 2;
+            W *= 2;
+        }
+    *c = d->conv_out.cout;
+    *ho = (int32_t)H;
+    *wo = (int32_t)W;
+    return VAE_OK;
+}
+
+int32_t vae_decoder_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, size_t *bytes) {
+    if (!d || !bytes) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_workspace_bytes: NULL pointer");
+    if (h <= 0 || w <= 0) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_workspace_bytes: sizes must be positive");
+    int32_t c, ho, wo;
+    vae_decoder_output_shape(d, h, w, &c, &ho, &wo);
+    if ((long long)ho * wo > (1LL << 30) || (long long)h * w > (1LL << 20))
+        return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_workspace_bytes: latent %dx%d too large", h, w);
+    const Plan p = plan_for(d, h, w);
+    *bytes = 5 * align256(p.act * 4) + align256(p.gn) + align256(p.attn);
+    return VAE_OK;
+}
+
+int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, float *rgb, void *ws, size_t ws_bytes,
+                   void *stream) {
+    if (!d || !latent || !rgb) return fail(VAE_ERR_INVALID_ARG, "vae_decode: NULL pointer");
+    size_t need = 0;
+    int32_t rc = vae_decoder_workspace_bytes(d, h, w, &need);
+    if (rc) return rc;
+    if (!ws || ws_bytes < need) return fail(VAE_ERR_WORKSPACE, "vae_decode: workspace %zu bytes < %zu", ws_bytes, need);
+    const Plan pl = plan_for(d, h, w);
+    char *base = static_cast<char *>(ws);
+    const size_t a = align256(pl.act * 4);
+    Buffers b;
+    b.X = reinterpret_cast<float *>(base);
+    b.Y = reinterpret_cast<float *>(base + a);
+    b.T = reinterpret_cast<float *>(base + 2 * a);
+    b.U = reinterpret_cast<float *>(base + 3 * a);
+    b.S = reinterpret_cast<float *>(base + 4 * a);
+    b.gn = base + 5 * a;
+    b.attn = base + 5 * a + align256(pl.gn);
+
+    Runner r{d, static_cast<hipStream_t>(stream)};
+    int H = h, W = w;
+    r.conv3("conv_in", d->conv_in, latent, H, W, false, nullptr, b.X, /*denorm=*/true);
+    r.resnet(d->mid0, b, H, W);
+    std::swap(b.X, b.Y);
+    if (r.rc == VAE_OK) {
+        const double n = (double)H * W, c = d->attn.c;
+        ProfEntry *e = r.begin("attention", "mid_block.attentions.0", 8.0 * n * c * c + 4.0 * n * n * c,
+                               4.0 * (2.0 * c * n + 2.0 * n * n));
+        if (r.rc == VAE_OK) {
+            r.rc = launch_attention(b.X, d->attn.c, H, W, d->attn.n.g, d->attn.n.b, d->attn.wqkv, d->attn.bqkv,
+                                    d->attn.wo, d->attn.bo, b.Y, b.attn, r.s);
+            r.end(e);
+        }
+    }
+    std::swap(b.X, b.Y);
+    r.resnet(d->mid1, b, H, W);
+    std::swap(b.X, b.Y);
+    for (size_t i = 0; i < d->ups.size(); ++i) {
+        const DUp &u = d->ups[i];
+        for (const DRes &res : u.res) {
+            r.resnet(res, b, H, W);
+            std::swap(b.X, b.Y);
+        }
+        if (u.up.present) {
+            H *= 2;
+            W *= 2;
+            r.conv3("up_blocks." + std::to_string(i) + ".upsamplers.0.conv", u.up, b.X, H, W, true, nullptr, b.Y);
+            std::swap(b.X, b.Y);
+        }
+    }
+    r.gn("conv_norm_out", d->norm_out, b.X, (long long)H * W, b.T, b.gn);
+    if (r.rc == VAE_OK) {
+        const DConv &c = d->conv_out;
+        ProfEntry *e = r.begin(c.cout <= 4 ? "conv3x3_skinny" : "conv3x3_mfma", "conv_out", conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
+        if (r.rc == VAE_OK) {
+            if (c.cout <= 4) {
+                r.rc = launch_conv3x3_skinny(b.T, c.w, c.b, rgb, c.cin, c.cout, H, W, r.s);
+            } else {
+                ConvLaunch a{};
+                a.x = b.T; a.wpk = c.w; a.bias = c.b; a.y = rgb; a.cin = c.cin; a.cout = c.cout;
+                a.H = H; a.W = W; a.T = 1; a.kt = 1;
+                r.rc = launch_conv3x3(a, r.s);
+            }
+            r.end(e);
+        }
+    }
+    return r.rc;
+}
+
+void vae_decoder_destroy(vae_decoder *d) {
+    if (!d) return;
+    for (ProfEntry &e : d->prof) {
+        if (e.start) (void)hipEventDestroy(e.start);
+        if (e.stop) (void)hipEventDestroy(e.stop);
+    }
+    delete d;
+}
+
+int32_t vae_decoder_set_profiling(vae_decoder *d, int32_t on) {
+    if (!d) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_set_profiling: NULL decoder");
+    d->profiling = on != 0;
+    d->prof_used = 0;   // records restart; decodes append until the next call
+    return VAE_OK;
+}
+
+int32_t vae_decoder_profile(vae_decoder *d, vae_prof_record *out, int32_t max, int32_t *n) {
+    if (!d || !n || (max > 0 && !out)) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_profile: NULL pointer");
+    *n = (int32_t)d->prof_used;
+    for (size_t i = 0; i < d->prof_used && (int32_t)i < max; ++i) {
+        ProfEntry &e = d->prof[i];
+        int32_t rc = hip_status(hipEventSynchronize(e.stop), "hipEventSynchronize");
+        if (rc) return rc;
+        float ms = 0.f;
+        if ((rc = hip_status(hipEventElapsedTime(&ms, e.start, e.stop), "hipEventElapsedTime"))) return rc;
+        vae_prof_record &o = out[i];
+        memset(&o, 0, sizeof o);
+        snprintf(o.kernel, sizeof o.kernel, "%s", e.kernel.c_str());
+        snprintf(o.layer, sizeof o.layer, "%s", e.layer.c_str());
+        o.ms = ms;
+        o.flops = e.flops;
+        o.bytes = e.bytes;
+    }
+    return VAE_OK;
+}
+
+}  // extern "C"

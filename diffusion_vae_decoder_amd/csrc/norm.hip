@@ -1,0 +1,318 @@
+// GroupNorm(32, eps 1e-6, affine) + SiLU (cortiq-engine 0.7.7 `vae`,
+// GroupNorm / VaeNormRef; cortiq-engine 0.8.78 vae3d.rs GroupNorm::apply for
+// the statistics: group mean and biased variance), nearest x2 upsample
+// (VaeUpRef) and the row softmax of the attention scores (vae3d.rs
+// softmax_inplace: subtract the row max, exponentiate, divide by the sum).
+//
+// GroupNorm runs as two HBM-streaming kernels.  gn_stats: a grid of
+// (parts, 32 groups) workgroups each reduces one contiguous slice of a group
+// to (sum d, sum d^2) with d = x - x_first (the group's first value, a shift
+// that keeps the variance free of cancellation); float32 per float4, float64
+// across float4s and threads.  gn_apply: a grid of (spatial chunks,
+// channels); each workgroup merges its group's partials in a fixed order
+// (deterministic), then streams y = silu((x - mean) * rstd * gamma + beta)
+// [+ residual] with float4 loads and stores.
+
+#include "vae_internal.h"
+
+namespace vae {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kGroups = 32;
+constexpr int kMaxParts = 64;
+constexpr long long kPartElems = 16384;   // group elements per stats workgroup, at least
+constexpr int kApplyElems = 4096;         // elements per apply workgroup (16 per thread)
+
+int parts_for(long long gsize) {
+    long long p = (gsize + kPartElems - 1) / kPartElems;
+    if (p < 1) p = 1;
+    if (p > kMaxParts) p = kMaxParts;
+    return (int)p;
+}
+
+__device__ inline double warp_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_down(v, o, 64);
+    return v;
+}
+
+// Sum over the 256 threads of a workgroup in a fixed order; result valid in thread 0.
+__device__ inline void block_sum2(double &a, double &b, double *scratch) {
+    a = warp_sum(a);
+    b = warp_sum(b);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        scratch[wave] = a;
+        scratch[4 + wave] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a = (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
+        b = (scratch[4] + scratch[5]) + (scratch[6] + scratch[7]);
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void gn_stats(const float *__restrict__ x, long long gsize,
+                                                     int parts, double *__restrict__ part,
+                                                     double *__restrict__ shift_out) {
+    __shared__ double scratch[8];
+    const int g = blockIdx.y, pi = blockIdx.x;
+    const float *base = x + (long long)g * gsize;
+    const float shift = base[0];
+    long long chunk = (gsize + parts - 1) / parts;
+    chunk = (chunk + 3) & ~3LL;
+    const long long lo = (long long)pi * chunk;
+    long long hi = lo + chunk;
+    if (hi > gsize) hi = gsize;
+    double s1 = 0.0, s2 = 0.0;
+    if (VEC) {
+        const floatx4 *b4 = reinterpret_cast<const floatx4 *>(base);
+        for (long long i = lo / 4 + threadIdx.x; i < hi / 4; i += kThreads) {
+            const floatx4 v = b4[i];
+            const float d0 = v[0] - shift, d1 = v[1] - shift, d2 = v[2] - shift, d3 = v[3] - shift;
+            s1 += (double)((d0 + d1) + (d2 + d3));
+            s2 += (double)((d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3));
+        }
+    } else {
+        for (long long i = lo + threadIdx.x; i < hi; i += kThreads) {
+            const float d = base[i] - shift;
+            s1 += (double)d;
+            s2 += (double)d * (double)d;
+        }
+    }
+    block_sum2(s1, s2, scratch);
+    if (threadIdx.x == 0) {
+        part[2 * ((long long)g * parts + pi)] = s1;
+        part[2 * ((long long)g * parts + pi) + 1] = s2;
+        if (pi == 0) shift_out[g] = (double)shift;
+    }
+}
+
+template <bool VEC, bool SILU, bool RES>
+__global__ __launch_bounds__(kThreads) void gn_apply(const float *x, long long spatial, int cpg,
+                                                     int parts, const double *__restrict__ part,
+                                                     const double *__restrict__ shifts,
+                                                     const float *__restrict__ gamma,
+                                                     const float *__restrict__ beta,
+                                                     const float *res, float *y) {
+    __shared__ double scratch[8];
+    __shared__ float stat[2];
+    const int c = blockIdx.y;
+    const int g = c / cpg;
+    double s1 = 0.0, s2 = 0.0;
+    if (threadIdx.x < parts) {
+        s1 = part[2 * ((long long)g * parts + threadIdx.x)];
+        s2 = part[2 * ((long long)g * parts + threadIdx.x) + 1];
+    }
+    block_sum2(s1, s2, scratch);
+    if (threadIdx.x == 0) {
+        const double n = (double)spatial * cpg;
+        const double md = s1 / n;
+        double var = s2 / n - md * md;
+        if (var < 0.0) var = 0.0;
+        const double rstd = 1.0 / sqrt(var + 1e-6);
+        stat[0] = (float)(shifts[g] + md);
+        stat[1] = (float)(rstd * (double)gamma[c]);
+    }
+    __syncthreads();
+    const float mean = stat[0], scale = stat[1], b = beta[c];
+    const long long cbase = (long long)c * spatial;
+    const long long lo = (long long)blockIdx.x * kApplyElems;
+    long long hi = lo + kApplyElems;
+    if (hi > spatial) hi = spatial;
+    auto f = [&](float v) {
+        float t = (v - mean) * scale + b;
+        if (SILU) t = t / (1.0f + __expf(-t));
+        return t;
+    };
+    if (VEC) {
+        const floatx4 *x4 = reinterpret_cast<const floatx4 *>(x + cbase);
+        const floatx4 *r4 = reinterpret_cast<const floatx4 *>(res + cbase);
+        floatx4 *y4 = reinterpret_cast<floatx4 *>(y + cbase);
+        for (long long i = lo / 4 + threadIdx.x; i < hi / 4; i += kThreads) {
+            const floatx4 v = x4[i];
+            floatx4 o;
+            o[0] = f(v[0]);
+            o[1] = f(v[1]);
+            o[2] = f(v[2]);
+            o[3] = f(v[3]);
+            if (RES) {
+                const floatx4 r = r4[i];
+                o[0] += r[0];
+                o[1] += r[1];
+                o[2] += r[2];
+                o[3] += r[3];
+            }
+            y4[i] = o;
+        }
+    } else {
+        for (long long i = lo + threadIdx.x; i < hi; i += kThreads) {
+            float t = f(x[cbase + i]);
+            if (RES) t += res[cbase + i];
+            y[cbase + i] = t;
+        }
+    }
+}
+
+template <bool VEC, bool SILU>
+void apply2(bool res, dim3 grid, hipStream_t s, const float *x, long long spatial, int cpg,
+            int parts, const double *part, const double *shifts, const float *gamma,
+            const float *beta, const float *r, float *y) {
+    if (res)
+        hipLaunchKernelGGL((gn_apply<VEC, SILU, true>), grid, dim3(kThreads), 0, s, x, spatial, cpg,
+                           parts, part, shifts, gamma, beta, r, y);
+    else
+        hipLaunchKernelGGL((gn_apply<VEC, SILU, false>), grid, dim3(kThreads), 0, s, x, spatial, cpg,
+                           parts, part, shifts, gamma, beta, r, y);
+}
+
+// ------------------------------------------------------------- upsample x2
+__global__ void upsample2x_pairs(const float *__restrict__ x, float *__restrict__ y, int h, int w,
+                                 long long total_pairs) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total_pairs) return;
+    const int half_w = w >> 1;
+    const long long row = i / half_w;        // (c, yy) input row
+    const int q = (int)(i - row * half_w);
+    const float a = x[row * w + 2 * q];
+    const float b = x[row * w + 2 * q + 1];
+    const long long c = row / h;
+    const int yy = (int)(row - c * h);
+    const long long obase = (c * 2 * h + 2 * yy) * (long long)(2 * w) + 4 * q;
+    const floatx4 v = {a, a, b, b};
+    *reinterpret_cast<floatx4 *>(y + obase) = v;
+    *reinterpret_cast<floatx4 *>(y + obase + 2 * w) = v;
+}
+
+__global__ void upsample2x_scalar(const float *__restrict__ x, float *__restrict__ y, int h, int w,
+                                  long long total) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int W2 = 2 * w, H2 = 2 * h;
+    const int xx = (int)(i % W2);
+    const long long r = i / W2;
+    const int yy = (int)(r % H2);
+    const long long c = r / H2;
+    y[i] = x[(c * h + (yy >> 1)) * w + (xx >> 1)];
+}
+
+// ------------------------------------------------------------- row softmax
+__device__ inline void merge_ms(float &m, float &s, float m2, float s2) {
+    const float mn = fmaxf(m, m2);
+    const float a = (m == -INFINITY) ? 0.f : s * __expf(m - mn);
+    const float b = (m2 == -INFINITY) ? 0.f : s2 * __expf(m2 - mn);
+    m = mn;
+    s = a + b;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void softmax_rows_kernel(float *S, int cols) {
+    __shared__ float sm[4], ss[4];
+    float *row = S + (long long)blockIdx.x * cols;
+    float m = -INFINITY, s = 0.f;
+    if (VEC) {
+        const floatx4 *r4 = reinterpret_cast<const floatx4 *>(row);
+        for (int i = threadIdx.x; i < cols / 4; i += kThreads) {
+            const floatx4 v = r4[i];
+            const float vm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+            const float vs = __expf(v[0] - vm) + __expf(v[1] - vm) + __expf(v[2] - vm) + __expf(v[3] - vm);
+            merge_ms(m, s, vm, vs);
+        }
+    } else {
+        for (int i = threadIdx.x; i < cols; i += kThreads) merge_ms(m, s, row[i], 1.f);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+        merge_ms(m, s, m2, s2);
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        sm[wave] = m;
+        ss[wave] = s;
+    }
+    __syncthreads();
+    m = sm[0];
+    s = ss[0];
+#pragma unroll
+    for (int wv = 1; wv < 4; ++wv) merge_ms(m, s, sm[wv], ss[wv]);
+    const float inv = 1.0f / s;
+    if (VEC) {
+        floatx4 *r4 = reinterpret_cast<floatx4 *>(row);
+        for (int i = threadIdx.x; i < cols / 4; i += kThreads) {
+            floatx4 v = r4[i];
+            v[0] = __expf(v[0] - m) * inv;
+            v[1] = __expf(v[1] - m) * inv;
+            v[2] = __expf(v[2] - m) * inv;
+            v[3] = __expf(v[3] - m) * inv;
+            r4[i] = v;
+        }
+    } else {
+        for (int i = threadIdx.x; i < cols; i += kThreads) row[i] = __expf(row[i] - m) * inv;
+    }
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+size_t groupnorm_ws_bytes(int c, long long spatial) {
+    const long long gsize = (long long)(c / kGroups) * spatial;
+    return (size_t)kGroups * parts_for(gsize) * 2 * sizeof(double) + kGroups * sizeof(double);
+}
+
+int32_t launch_groupnorm(const float *x, int c, long long spatial, const float *gamma,
+                         const float *beta, int silu, const float *res, float *y, void *ws,
+                         hipStream_t s) {
+    const int cpg = c / kGroups;
+    const long long gsize = (long long)cpg * spatial;
+    const int parts = parts_for(gsize);
+    double *part = reinterpret_cast<double *>(ws);
+    double *shifts = part + 2 * kGroups * parts;
+    const bool vec_stats = gsize % 4 == 0 && aligned16(x);
+    if (vec_stats)
+        hipLaunchKernelGGL(gn_stats<true>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize, parts,
+                           part, shifts);
+    else
+        hipLaunchKernelGGL(gn_stats<false>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize,
+                           parts, part, shifts);
+    int32_t rc = check_launch("gn_stats");
+    if (rc != VAE_OK) return rc;
+    const bool vec = spatial % 4 == 0 && aligned16(x) && aligned16(y) && (!res || aligned16(res));
+    const dim3 grid((unsigned)((spatial + kApplyElems - 1) / kApplyElems), (unsigned)c);
+    if (vec) {
+        if (silu) apply2<true, true>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y);
+        else apply2<true, false>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y);
+    } else {
+        if (silu) apply2<false, true>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y);
+        else apply2<false, false>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y);
+    }
+    return check_launch("gn_apply");
+}
+
+int32_t launch_upsample2x(const float *x, int c, int h, int w, float *y, hipStream_t s) {
+    const int threads = 256;
+    if (w % 2 == 0 && aligned16(y)) {
+        const long long pairs = (long long)c * h * (w / 2);
+        hipLaunchKernelGGL(upsample2x_pairs, dim3((unsigned)((pairs + threads - 1) / threads)),
+                           dim3(threads), 0, s, x, y, h, w, pairs);
+    } else {
+        const long long total = (long long)c * 4 * h * w;
+        hipLaunchKernelGGL(upsample2x_scalar, dim3((unsigned)((total + threads - 1) / threads)),
+                           dim3(threads), 0, s, x, y, h, w, total);
+    }
+    return check_launch("upsample2x");
+}
+
+int32_t launch_softmax_rows(float *S, int rows, int cols, hipStream_t s) {
+    if (cols % 4 == 0 && aligned16(S))
+        hipLaunchKernelGGL(softmax_rows_kernel<true>, dim3(rows), dim3(kThreads), 0, s, S, cols);
+    else
+        hipLaunchKernelGGL(softmax_rows_kernel<false>, dim3(rows), dim3(kThreads), 0, s, S, cols);
+    return check_launch("softmax_rows");
+}
+
+}  // namespace vae

@@ -1,0 +1,90 @@
+// Internal declarations shared by the HIP sources of libvae.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/vae.h"
+
+namespace vae {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ errors
+void set_error(const char *fmt, ...);
+int32_t hip_status(hipError_t e, const char *what);
+int32_t check_launch(const char *what);
+
+// ------------------------------------------------------------------ conv
+// Geometry of the implicit-GEMM 3x3 conv: a workgroup computes 128 output
+// channels x 128 output pixels (TR rows x TC columns of one frame).
+constexpr int kConvBM = 128;
+constexpr int kConvBN = 128;
+constexpr int kConvCC = 8;   // input channels per K chunk (K chunk = 8 x 9 taps)
+
+struct ConvLaunch {
+    const float *x;        // input activations
+    const float *wpk;      // weights repacked by pack_conv3x3
+    const float *bias;     // [cout]
+    const float *res;      // residual [cout, (T,) H, W] or nullptr
+    float *y;              // output  [cout, (T,) H, W]
+    int cin, cout;
+    int H, W;              // output height/width (the conv's own input size after upsampling)
+    int T;                 // frames (1 for 2-D)
+    int kt;                // time taps (1 for 2-D, 3 for causal 3-D)
+    int upsample;          // input is the nearest-x2 upsample of x
+    int denorm;            // input is x / dn_scale + dn_shift (padding stays 0)
+    float dn_scale, dn_shift;
+};
+
+// Bytes of the packed weights for a conv with `cout` x `cin` x (kt x 3 x 3).
+size_t conv3x3_packed_floats(int cout, int cin, int kt);
+// Enqueue the repacking of raw weights [cout, cin, (kt,) 3, 3] into `dst`.
+int32_t pack_conv3x3(const float *w, int cout, int cin, int kt, float *dst, hipStream_t s);
+// Enqueue one implicit-GEMM conv.
+int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s);
+// Name of the kernel instantiation launch_conv3x3 picks for `a`.
+const char *conv3x3_kernel_name(const ConvLaunch &a);
+
+// Direct conv for out_channels <= 4 (conv_out).
+int32_t launch_conv3x3_skinny(const float *x, const float *w, const float *bias, float *y,
+                              int cin, int cout, int H, int W, hipStream_t s);
+
+// ------------------------------------------------------------------ GEMM
+// C[m, n] = alpha * sum_k A(m, k) B(k, n) + bias[m] (+ R[m, n]).
+// A(m, k) = a_km ? A[k * lda + m] : A[m * lda + k]
+// B(k, n) = b_nk ? B[n * ldb + k] : B[k * ldb + n]
+struct GemmLaunch {
+    const float *A;
+    const float *B;
+    const float *bias;   // [M] or nullptr
+    const float *R;      // [M, N] with ldr, or nullptr
+    float *C;
+    int M, N, K;
+    long long lda, ldb, ldc, ldr;
+    int a_km, b_nk;
+    float alpha;
+};
+int32_t launch_gemm(const GemmLaunch &g, hipStream_t s);
+
+// ------------------------------------------------------------------ norm
+size_t groupnorm_ws_bytes(int c, long long spatial);
+int32_t launch_groupnorm(const float *x, int c, long long spatial, const float *gamma,
+                         const float *beta, int silu, const float *res, float *y, void *ws,
+                         hipStream_t s);
+
+// ------------------------------------------------------------------ misc
+int32_t launch_upsample2x(const float *x, int c, int h, int w, float *y, hipStream_t s);
+int32_t launch_softmax_rows(float *S, int rows, int cols, hipStream_t s);
+
+// Attention on x [c, n] with packed qkv weights [3c, c] and bias [3c].
+size_t attention_ws_bytes(int c, long long n);
+int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_gamma,
+                         const float *gn_beta, const float *wqkv, const float *bqkv,
+                         const float *wo, const float *bo, float *y, void *ws, hipStream_t s);
+
+}  // namespace vae

@@ -1,0 +1,238 @@
+/*
+ * vae.h -- C ABI of libvae.so, an MI355X (gfx950) FLUX-class VAE decoder.
+ *
+ * The library decodes a FLUX-class AutoencoderKL latent [16, h, w] into RGB
+ * [3, 8h, 8w] (docs.rs, cortiq-engine 0.7.7, module `vae`: module doc and
+ * struct VaeDecoder) and exports the decoder's layers one by one.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are float32, batch 1, channel-major (NCHW without the N, or
+ *    C,T,H,W for the 3-D conv), densely packed, in DEVICE memory of the
+ *    current HIP device.  Pointers are borrowed: the caller owns and frees
+ *    every buffer, including workspaces.  The library allocates nothing.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns; nothing is synchronised.  Inputs must
+ *    stay alive and unmodified until that work has run.
+ *  - Outputs must not overlap inputs unless a function says otherwise.
+ *  - Return value: VAE_OK (0) or a negative VAE_ERR_* code.  On error nothing
+ *    has been enqueued, except for VAE_ERR_HIP, which reports a failed
+ *    launch.  vae_last_error() then returns a message (per calling thread).
+ *  - Every size is validated before any launch: non-positive sizes, NULL
+ *    required pointers, a workspace that is too small, and shapes the
+ *    kernels do not support are reported, never run.
+ */
+#ifndef VAE_H_
+#define VAE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VAE_ABI_VERSION 1
+
+#define VAE_OK 0
+#define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
+#define VAE_ERR_UNSUPPORTED (-2) /* a shape the kernels do not handle (e.g. C % 32 != 0) */
+#define VAE_ERR_WORKSPACE (-3)   /* workspace smaller than the matching *_workspace_bytes */
+#define VAE_ERR_HIP (-4)         /* a HIP launch or runtime call failed */
+
+/* One convolution: weight [out_channels, in_channels, k, k] row-major
+ * (k x k x k for the 3-D conv), bias [out_channels]; stride 1, zero padding
+ * k/2 (cortiq-engine 0.7.7 `vae`, structs Conv2d and VaeConvRef).  A conv
+ * with weight == NULL is "absent" where the struct is optional. */
+typedef struct vae_conv {
+    const float *weight;
+    const float *bias;
+    int32_t out_channels;
+    int32_t in_channels;
+    int32_t kernel; /* 1 or 3 */
+} vae_conv;
+
+/* GroupNorm(32 groups, eps 1e-6) affine parameters gamma[c], beta[c]
+ * (cortiq-engine 0.7.7 `vae`, structs GroupNorm and VaeNormRef). */
+typedef struct vae_norm {
+    const float *gamma;
+    const float *beta;
+    int32_t channels;
+} vae_norm;
+
+/* x + conv2(silu(norm2(conv1(silu(norm1(x)))))), the skip going through the
+ * 1x1 `shortcut` when the block changes the channel count (VaeResnetRef).
+ * shortcut.weight == NULL means the identity skip. */
+typedef struct vae_resnet {
+    vae_norm norm1;
+    vae_conv conv1;
+    vae_norm norm2;
+    vae_conv conv2;
+    vae_conv shortcut;
+} vae_resnet;
+
+/* Mid-block single-head spatial attention (VaeAttnRef): GroupNorm, then
+ * token-major Linear q, k, v ([c, c] row-major out x in, + bias, given as
+ * kernel-1 convs), softmax(q k^T / sqrt(c)) v, Linear `out` + bias, residual
+ * add onto the block input. */
+typedef struct vae_attn {
+    vae_norm norm;
+    vae_conv q, k, v, out;
+} vae_attn;
+
+/* One up block (VaeUpRef): its resnets in order, then, if upsample.weight is
+ * not NULL, nearest x2 upsampling followed by the 3x3 `upsample` conv. */
+typedef struct vae_up {
+    int32_t n_resnets;
+    const vae_resnet *resnets;
+    vae_conv upsample;
+} vae_up;
+
+/* The whole decoder in execution order (VaeChainArgs): conv_in -> mid_res0 ->
+ * mid_attn -> mid_res1 -> ups[0..n_up) -> norm_out + SiLU -> conv_out, with
+ * the latent de-normalised first as z / scaling_factor + shift_factor
+ * (VaeDecoder). */
+typedef struct vae_weights {
+    vae_conv conv_in;
+    vae_resnet mid_res0;
+    vae_attn mid_attn;
+    vae_resnet mid_res1;
+    int32_t n_up;
+    const vae_up *ups;
+    vae_norm norm_out;
+    vae_conv conv_out;
+    float scaling_factor;
+    float shift_factor;
+} vae_weights;
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *vae_last_error(void);
+int32_t vae_abi_version(void);
+
+/* ---------------------------------------------------------------- layers */
+
+/* Workspace (device bytes) needed by vae_conv2d / vae_conv_in for `conv`:
+ * the weights repacked for the kernel.  0 for kernel-1 convs. */
+int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, size_t *bytes);
+
+/* 2-D convolution (Conv2d / VaeConvRef): y = conv(u) + bias [+ residual].
+ *   x        [cin, h, w]
+ *   u        = x, or its nearest-x2 upsample [cin, 2h, 2w] when upsample2x
+ *              (VaeUpRef; the upsampled tensor is never formed in memory)
+ *   y        [cout, H, W] with (H, W) = (h, w), or (2h, 2w) when upsample2x
+ *   residual NULL or [cout, H, W], added after the bias (the resnet skip)
+ *   conv     kernel 1 or 3; conv->in_channels must equal cin
+ *   ws       >= vae_conv2d_workspace_bytes(conv) device bytes (may be NULL if 0)
+ * A convolution with out_channels <= 4 (the decoder's conv_out) runs on a
+ * direct kernel; other 3x3 convolutions run as implicit GEMM on FP32 MFMA.
+ * upsample2x requires kernel 3.  y may not alias x; it may alias residual. */
+int32_t vae_conv2d(const float *x, int32_t cin, int32_t h, int32_t w, const vae_conv *conv,
+                   int32_t upsample2x, const float *residual, float *y,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* conv_in with the latent de-normalisation folded into its input gather
+ * (VaeDecoder): y = conv(z / scaling_factor + shift_factor) + bias, where
+ * the zero padding stays zero.  z [cin, h, w], y [cout, h, w], kernel 3. */
+int32_t vae_conv_in(const float *z, int32_t cin, int32_t h, int32_t w, const vae_conv *conv,
+                    float scaling_factor, float shift_factor, float *y,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace for vae_groupnorm_silu on x [c, spatial]: per-group partial sums. */
+int32_t vae_groupnorm_workspace_bytes(int32_t c, int64_t spatial, size_t *bytes);
+
+/* GroupNorm(32, eps 1e-6, affine) (GroupNorm / VaeNormRef) over x [c, spatial]
+ * (spatial = h*w, or t*h*w for the 3-D stack), then SiLU v/(1+exp(-v)) if
+ * apply_silu, then + residual [c, spatial] if residual != NULL.
+ * Statistics: the group mean and biased variance, accumulated in float64.
+ * c % 32 == 0.  y may alias x (in place) and/or residual. */
+int32_t vae_groupnorm_silu(const float *x, int32_t c, int64_t spatial, const vae_norm *norm,
+                           int32_t apply_silu, const float *residual, float *y,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Nearest x2 upsample (VaeUpRef): y[c, Y, X] = x[c, Y/2, X/2];
+ * x [c, h, w] -> y [c, 2h, 2w].  Exact copy. */
+int32_t vae_upsample_nearest2x(const float *x, int32_t c, int32_t h, int32_t w, float *y,
+                               void *stream);
+
+/* Workspace for vae_attention on x [c, h, w]: the normalised input, q/k/v,
+ * the [h*w, h*w] score matrix and the attention output. */
+int32_t vae_attention_workspace_bytes(int32_t c, int32_t h, int32_t w, size_t *bytes);
+
+/* Mid-block attention (VaeAttnRef) on x [c, h, w] -> y [c, h, w]; tokens are
+ * the h*w positions in row-major order.  c % 32 == 0; q, k, v, out are
+ * kernel-1 convs with c in and c out channels.  y may not alias x. */
+int32_t vae_attention(const float *x, int32_t c, int32_t h, int32_t w, const vae_attn *attn,
+                      float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace for vae_conv3d_causal: the repacked 3x3x3 weights. */
+int32_t vae_conv3d_causal_workspace_bytes(const vae_conv *conv, size_t *bytes);
+
+/* Causal 3-D convolution (VAE decode -> GPU handoff, "The CPU VAE code" and
+ * "GPU plan": LTX's 3-D causal conv with causal padding on time):
+ * x [cin, t, h, w] -> y [cout, t, h, w]; weight [cout, cin, 3, 3, 3];
+ * time padded at the front with two copies of frame 0, h and w zero-padded
+ * by 1; stride 1.  y may not alias x. */
+int32_t vae_conv3d_causal(const float *x, int32_t cin, int32_t t, int32_t h, int32_t w,
+                          const vae_conv *conv, float *y, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* --------------------------------------------------------------- decoder */
+
+typedef struct vae_decoder vae_decoder; /* opaque; created and freed by the library */
+
+/* Device bytes of the decoder's own weight copy ("pack") for `w`. */
+int32_t vae_decoder_pack_bytes(const vae_weights *w, size_t *bytes);
+
+/* Validates the chain, then copies and repacks every weight of `w` into the
+ * caller's device buffer `pack` (>= vae_decoder_pack_bytes) on `stream`.
+ * The decoder keeps using `pack` (which the caller must keep alive until
+ * vae_decoder_destroy); the arrays `w` points to may be freed once the
+ * enqueued copies have run.  This is the weight cache keyed by the decoder
+ * handle (VaeChainArgs: a key stable for the life of the decoder). */
+int32_t vae_decoder_create(vae_decoder **out, const vae_weights *w, void *pack, size_t pack_bytes,
+                           void *stream);
+
+/* Workspace for one vae_decode of a [latent_channels, h, w] latent. */
+int32_t vae_decoder_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, size_t *bytes);
+
+/* latent [latent_channels, h, w] -> rgb [out_channels, 8h, 8w] (for four up
+ * blocks), raw conv_out values.  Every activation stays in `ws`; only the
+ * caller's rgb buffer is written.  Calls on one decoder must not overlap in
+ * time on different streams (they share the handle's profiling state). */
+int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, float *rgb,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Output spatial scale of the chain (8 for four up blocks) and its channels. */
+int32_t vae_decoder_output_shape(const vae_decoder *d, int32_t h, int32_t w, int32_t *c,
+                                 int32_t *ho, int32_t *wo);
+
+void vae_decoder_destroy(vae_decoder *d);
+
+/* ------------------------------------------------------------- profiling */
+
+/* One kernel launch (or one composite layer: GroupNorm = stats + apply,
+ * attention = its GEMMs and softmax) of a profiled vae_decode. */
+typedef struct vae_prof_record {
+    char kernel[40];   /* kernel class, e.g. "conv3x3_mfma" */
+    char layer[72];    /* decoder layer, e.g. "up_blocks.3.resnets.1.conv2" */
+    float ms;          /* launch duration from HIP events on the decode stream */
+    double flops;      /* algorithmic FLOPs of the launch (direct-conv count) */
+    double bytes;      /* algorithmic HBM bytes of the launch (one read of each input, one write) */
+} vae_prof_record;
+
+/* Clears the recorded launches.  on != 0: the following vae_decode calls
+ * bracket every launch with HIP events on their stream and append one
+ * record per launch (events are created on first use; a failure to create
+ * one is reported as VAE_ERR_HIP by vae_decode). */
+int32_t vae_decoder_set_profiling(vae_decoder *d, int32_t on);
+
+/* Synchronises on the recorded events and copies up to `max` records
+ * (oldest first) into `out`; *n receives the number recorded since the last
+ * vae_decoder_set_profiling call. */
+int32_t vae_decoder_profile(vae_decoder *d, vae_prof_record *out, int32_t max, int32_t *n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VAE_H_ */

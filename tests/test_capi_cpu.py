@@ -1,0 +1,170 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/vae.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+from ctypes import byref, c_int32, c_size_t, c_void_p
+
+import pytest
+
+from diffusion_vae_decoder_amd import _lib
+from diffusion_vae_decoder_amd._lib import (VAE_ERR_INVALID_ARG, VAE_ERR_UNSUPPORTED, VAE_ERR_WORKSPACE, VAE_OK,
+                                            VaeAttn, VaeConv, VaeNorm, VaeResnet, VaeUp, VaeWeights)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vae.h")
+FAKE = 0x7F0000000000          # a non-NULL "device" pointer; never dereferenced on these paths
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vae_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+
+
+def test_abi_version(lib):
+    assert lib.vae_abi_version() == _lib.ABI_VERSION
+
+
+def conv(cout, cin, k, w=FAKE, b=FAKE):
+    return VaeConv(w, b, cout, cin, k)
+
+
+def err(lib):
+    return lib.vae_last_error().decode()
+
+
+def test_conv2d_validation(lib):
+    c = conv(64, 32, 3)
+    ws = c_size_t()
+    assert lib.vae_conv2d_workspace_bytes(byref(c), byref(ws)) == VAE_OK
+    assert ws.value == 1 * 4 * 9 * 8 * 128 * 4        # 1 output block x 4 channel chunks x 72 x 128 floats
+    args = lambda **k: dict(dict(x=FAKE, cin=32, h=8, w=8, conv=byref(c), up=0, res=NULL, y=FAKE + 4096,
+                                 ws=FAKE + 8192, nb=ws.value, s=NULL), **k)
+
+    def call(a):
+        return lib.vae_conv2d(a["x"], a["cin"], a["h"], a["w"], a["conv"], a["up"], a["res"], a["y"], a["ws"],
+                              a["nb"], a["s"])
+    assert call(args(x=NULL)) == VAE_ERR_INVALID_ARG
+    assert call(args(cin=31)) == VAE_ERR_INVALID_ARG and "input channels" in err(lib)
+    assert call(args(h=0)) == VAE_ERR_INVALID_ARG
+    assert call(args(w=-3)) == VAE_ERR_INVALID_ARG
+    assert call(args(nb=ws.value - 1)) == VAE_ERR_WORKSPACE
+    assert call(args(ws=NULL)) == VAE_ERR_WORKSPACE
+    assert call(args(y=FAKE)) == VAE_ERR_INVALID_ARG and "alias" in err(lib)
+    bad = conv(64, 32, 5)
+    assert call(args(conv=byref(bad))) == VAE_ERR_UNSUPPORTED
+    nob = conv(64, 32, 3, b=NULL)
+    assert call(args(conv=byref(nob))) == VAE_ERR_INVALID_ARG
+    one = conv(64, 32, 1)
+    assert call(args(conv=byref(one), up=1)) == VAE_ERR_UNSUPPORTED
+    assert call(args(h=1 << 16, w=1 << 16)) == VAE_ERR_UNSUPPORTED
+
+
+def test_conv_in_and_3d_validation(lib):
+    c = conv(512, 16, 3)
+    nb = c_size_t()
+    assert lib.vae_conv2d_workspace_bytes(byref(c), byref(nb)) == VAE_OK
+    assert lib.vae_conv_in(FAKE, 16, 8, 8, byref(c), 0.0, 0.1, FAKE + 64, FAKE + 128, nb.value, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_conv_in(FAKE, 16, 8, 8, byref(conv(512, 16, 1)), 0.36, 0.1, FAKE + 64, FAKE, 0, NULL) == VAE_ERR_UNSUPPORTED
+    c3 = conv(128, 128, 3)
+    assert lib.vae_conv3d_causal_workspace_bytes(byref(c3), byref(nb)) == VAE_OK
+    assert nb.value == 3 * 16 * 72 * 128 * 4
+    assert lib.vae_conv3d_causal(FAKE, 128, 0, 8, 8, byref(c3), FAKE + 64, FAKE, nb.value, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_conv3d_causal(FAKE, 128, 3, 8, 8, byref(c3), FAKE + 64, FAKE, nb.value - 4, NULL) == VAE_ERR_WORKSPACE
+    assert lib.vae_conv3d_causal(FAKE, 64, 3, 8, 8, byref(c3), FAKE + 64, FAKE, nb.value, NULL) == VAE_ERR_INVALID_ARG
+
+
+def test_groupnorm_validation(lib):
+    nb = c_size_t()
+    assert lib.vae_groupnorm_workspace_bytes(128, 512 * 512, byref(nb)) == VAE_OK
+    assert nb.value > 0
+    assert lib.vae_groupnorm_workspace_bytes(100, 64, byref(nb)) == VAE_ERR_UNSUPPORTED
+    n = VaeNorm(FAKE, FAKE, 64)
+    assert lib.vae_groupnorm_silu(FAKE, 64, 16, byref(n), 1, NULL, FAKE, FAKE, 0, NULL) == VAE_ERR_WORKSPACE
+    assert lib.vae_groupnorm_silu(FAKE, 96, 16, byref(n), 1, NULL, FAKE, FAKE, 1 << 20, NULL) == VAE_ERR_INVALID_ARG
+    n40 = VaeNorm(FAKE, FAKE, 40)
+    assert lib.vae_groupnorm_silu(FAKE, 40, 16, byref(n40), 1, NULL, FAKE, FAKE, 1 << 20, NULL) == VAE_ERR_UNSUPPORTED
+    nn = VaeNorm(NULL, FAKE, 64)
+    assert lib.vae_groupnorm_silu(FAKE, 64, 16, byref(nn), 1, NULL, FAKE, FAKE, 1 << 20, NULL) == VAE_ERR_INVALID_ARG
+
+
+def test_attention_and_upsample_validation(lib):
+    nb = c_size_t()
+    assert lib.vae_attention_workspace_bytes(512, 128, 128, byref(nb)) == VAE_OK
+    n = 128 * 128
+    assert nb.value >= 4 * (n * n + 5 * 512 * n)
+    a = VaeAttn(VaeNorm(FAKE, FAKE, 64), conv(64, 64, 1), conv(64, 64, 1), conv(64, 64, 1), conv(64, 64, 1))
+    assert lib.vae_attention(FAKE, 64, 4, 4, byref(a), FAKE + 64, FAKE, 16, NULL) == VAE_ERR_WORKSPACE
+    a.k = conv(64, 32, 1)
+    assert lib.vae_attention(FAKE, 64, 4, 4, byref(a), FAKE + 64, FAKE, 1 << 30, NULL) == VAE_ERR_INVALID_ARG
+    a.k = conv(64, 64, 3)
+    assert lib.vae_attention(FAKE, 64, 4, 4, byref(a), FAKE + 64, FAKE, 1 << 30, NULL) == VAE_ERR_UNSUPPORTED
+    assert lib.vae_upsample_nearest2x(FAKE, 4, 3, 3, FAKE, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_upsample_nearest2x(FAKE, 0, 3, 3, FAKE + 64, NULL) == VAE_ERR_INVALID_ARG
+
+
+def fake_weights(widths=(512, 512, 256, 128), zc=16, oc=3):
+    keep = []
+
+    def resnet(cin, cout):
+        sc = conv(cout, cin, 1) if cin != cout else VaeConv(None, None, 0, 0, 0)
+        return VaeResnet(VaeNorm(FAKE, FAKE, cin), conv(cout, cin, 3), VaeNorm(FAKE, FAKE, cout),
+                         conv(cout, cout, 3), sc)
+    c0 = widths[0]
+    ups = []
+    prev = c0
+    for i, c in enumerate(widths):
+        rs = (VaeResnet * 3)(*[resnet(prev if j == 0 else c, c) for j in range(3)])
+        keep.append(rs)
+        prev = c
+        up = conv(c, c, 3) if i + 1 < len(widths) else VaeConv(None, None, 0, 0, 0)
+        ups.append(VaeUp(3, rs, up))
+    ua = (VaeUp * len(ups))(*ups)
+    keep.append(ua)
+    attn = VaeAttn(VaeNorm(FAKE, FAKE, c0), *[conv(c0, c0, 1) for _ in range(4)])
+    w = VaeWeights(conv(c0, zc, 3), resnet(c0, c0), attn, resnet(c0, c0), len(ups), ua,
+                   VaeNorm(FAKE, FAKE, prev), conv(oc, prev, 3), 0.3611, 0.1159)
+    return w, keep
+
+
+def test_decoder_pack_and_validation(lib):
+    w, keep = fake_weights()
+    nb = c_size_t()
+    assert lib.vae_decoder_pack_bytes(byref(w), byref(nb)) == VAE_OK, err(lib)
+    # about 50M parameters, 3x3 weights padded to 8-channel chunks
+    assert 49_000_000 * 4 < nb.value < 52_000_000 * 4
+    h = c_void_p()
+    assert lib.vae_decoder_create(byref(h), byref(w), FAKE, nb.value - 1, NULL) == VAE_ERR_WORKSPACE
+    assert lib.vae_decoder_create(byref(h), byref(w), FAKE + 4, nb.value, NULL) == VAE_ERR_INVALID_ARG
+    # broken chains
+    w2, k2 = fake_weights()
+    w2.mid_res1.conv1 = conv(512, 256, 3)
+    assert lib.vae_decoder_pack_bytes(byref(w2), byref(nb)) == VAE_ERR_INVALID_ARG
+    w3, k3 = fake_weights()
+    w3.ups[2].resnets[0].shortcut = VaeConv(None, None, 0, 0, 0)
+    assert lib.vae_decoder_pack_bytes(byref(w3), byref(nb)) == VAE_ERR_INVALID_ARG
+    assert "shortcut" in err(lib)
+    w4, k4 = fake_weights(widths=(512, 512, 256, 100))
+    assert lib.vae_decoder_pack_bytes(byref(w4), byref(nb)) == VAE_ERR_UNSUPPORTED
+    w5, k5 = fake_weights()
+    w5.scaling_factor = 0.0
+    assert lib.vae_decoder_pack_bytes(byref(w5), byref(nb)) == VAE_ERR_INVALID_ARG
+    w6, k6 = fake_weights()
+    w6.n_up = 0
+    assert lib.vae_decoder_pack_bytes(byref(w6), byref(nb)) == VAE_ERR_INVALID_ARG
+    assert lib.vae_decode(NULL, FAKE, 8, 8, FAKE, FAKE, 1, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_decoder_set_profiling(NULL, 1) == VAE_ERR_INVALID_ARG

@@ -1,0 +1,279 @@
+"""GPU parity: every entry point of libvae.so against the float64 oracle.
+
+Inputs come from the seeded generator and are rounded to float32 once; both
+sides see the same float32 values.  Outputs are pre-filled with NaN so that
+an element the kernel never writes fails the comparison.
+
+Bars (per layer): max|gpu - ref| / max|ref| <= 1e-4 over the layer output.
+End to end (RGB): cosine >= 0.99999 and max|gpu - ref| <= 1e-3 * max|ref|.
+Exact copies (upsample) must be bit-identical.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import vaegen
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LAYER_TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from diffusion_vae_decoder_amd import api as a
+    a._lib_()           # raises if libvae.so is missing: no fallback
+    return a
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def nan_like(shape):
+    return torch.full(tuple(shape), float("nan"), dtype=torch.float32, device="cuda")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy().astype(np.float64)
+
+
+def rel_err(g, r):
+    assert not np.isnan(g).any(), "output has unwritten (NaN) elements"
+    return float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-30))
+
+
+def conv_params(seed, name, cin, cout, k, dims=2):
+    p = vaegen.conv_params(seed, name, cin, cout, k, dims)
+    return p[name + ".weight"], p[name + ".bias"]
+
+
+# ---------------------------------------------------------------------------
+# 3x3 convolution (implicit GEMM on MFMA)
+# ---------------------------------------------------------------------------
+
+CONV_CASES = [
+    # cin, cout, h, w
+    (16, 128, 8, 8),        # conv_in width: TC=8 tiles
+    (32, 64, 19, 37),       # ragged rows/cols, partial output block
+    (24, 200, 13, 70),      # cin not a multiple of 8, cout not a multiple of 128
+    (64, 64, 5, 5),         # image smaller than one tile
+    (8, 128, 16, 16),       # TC=16 tiles
+    (512, 512, 8, 8),       # long K (64 chunks)
+    (128, 128, 64, 64),     # several full tiles
+    (256, 128, 40, 33),     # the 256->128 shape, ragged
+]
+
+
+@pytest.mark.parametrize("cin,cout,h,w", CONV_CASES)
+def test_conv3x3(api, cin, cout, h, w):
+    x = vaegen.activation(1, f"x{cin}_{h}_{w}", (cin, h, w))
+    wt, b = conv_params(1, f"c{cin}_{cout}", cin, cout, 3)
+    y = api.conv2d(dev(x), dev(wt), dev(b), out=nan_like((cout, h, w)))
+    assert rel_err(host(y), oracle.conv2d(x, wt, b)) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("cin,cout,h,w", [(32, 64, 9, 13), (64, 128, 16, 16), (16, 32, 4, 4), (128, 128, 32, 32)])
+def test_conv3x3_upsample_folded(api, cin, cout, h, w):
+    x = vaegen.activation(2, "xu", (cin, h, w))
+    wt, b = conv_params(2, "cu", cin, cout, 3)
+    y = api.conv2d(dev(x), dev(wt), dev(b), upsample2x=True, out=nan_like((cout, 2 * h, 2 * w)))
+    ref = oracle.conv2d(oracle.upsample_nearest2x(x), wt, b)
+    assert rel_err(host(y), ref) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("cin,cout,h,w", [(64, 64, 23, 17), (128, 128, 32, 32)])
+def test_conv3x3_residual_epilogue(api, cin, cout, h, w):
+    x = vaegen.activation(3, "xr", (cin, h, w))
+    r = vaegen.activation(3, "rr", (cout, h, w))
+    wt, b = conv_params(3, "cr", cin, cout, 3)
+    y = api.conv2d(dev(x), dev(wt), dev(b), residual=dev(r), out=nan_like((cout, h, w)))
+    assert rel_err(host(y), oracle.conv2d(x, wt, b) + r) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("h,w", [(8, 8), (32, 32), (11, 7)])
+def test_conv_in_with_denormalisation(api, h, w):
+    z = vaegen.latent(4, h, w)
+    wt, b = conv_params(4, "conv_in", 16, 512, 3)
+    s, t = vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR
+    y = api.conv_in(dev(z), dev(wt), dev(b), s, t, out=nan_like((512, h, w)))
+    ref = oracle.conv2d(oracle.denormalize(z, s, t), wt, b)
+    assert rel_err(host(y), ref) <= LAYER_TOL
+
+
+# ---------------------------------------------------------------------------
+# 1x1 conv (GEMM) and conv_out (direct)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cin,cout,h,w,res", [(256, 128, 32, 32, False), (512, 256, 16, 16, True),
+                                               (37, 50, 11, 13, False), (64, 130, 9, 9, True)])
+def test_conv1x1(api, cin, cout, h, w, res):
+    x = vaegen.activation(5, "x1", (cin, h, w))
+    wt, b = conv_params(5, "c1", cin, cout, 1)
+    r = vaegen.activation(5, "r1", (cout, h, w)) if res else None
+    y = api.conv2d(dev(x), dev(wt), dev(b), residual=dev(r) if res else None, out=nan_like((cout, h, w)))
+    ref = oracle.conv2d(x, wt, b) + (r if res else 0.0)
+    assert rel_err(host(y), ref) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("cin,cout,h,w", [(128, 3, 64, 64), (128, 3, 37, 45), (64, 1, 10, 130), (32, 4, 9, 9),
+                                          (24, 2, 16, 16)])
+def test_conv_out_skinny(api, cin, cout, h, w):
+    x = vaegen.activation(6, "xo", (cin, h, w))
+    wt, b = conv_params(6, "co", cin, cout, 3)
+    y = api.conv2d(dev(x), dev(wt), dev(b), out=nan_like((cout, h, w)))
+    assert rel_err(host(y), oracle.conv2d(x, wt, b)) <= LAYER_TOL
+
+
+# ---------------------------------------------------------------------------
+# GroupNorm + SiLU, upsample
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,silu,res", [((128, 32, 32), True, False), ((512, 16, 16), True, False),
+                                            ((64, 7, 5), True, False), ((256, 9, 31), False, False),
+                                            ((128, 3, 8, 8), True, True), ((32, 1, 1), True, False)])
+def test_groupnorm_silu(api, shape, silu, res):
+    x = vaegen.activation(7, "xg", shape) * 2.0 + 0.5
+    n = vaegen.norm_params(7, "gn", shape[0])
+    g, bt = n["gn.weight"], n["gn.bias"]
+    r = vaegen.activation(7, "rg", shape) if res else None
+    y = api.groupnorm_silu(dev(x), dev(g), dev(bt), silu=silu, residual=dev(r) if res else None,
+                           out=nan_like(shape))
+    ref = oracle.group_norm(x, g, bt)
+    if silu:
+        ref = oracle.silu(ref)
+    if res:
+        ref = ref + r
+    assert rel_err(host(y), ref) <= LAYER_TOL
+
+
+def test_groupnorm_in_place_and_large_mean(api):
+    # a large common offset: the statistics must not cancel
+    shape = (64, 40, 40)
+    x = (vaegen.activation(8, "xm", shape) + 100.0).astype(np.float32)
+    n = vaegen.norm_params(8, "gm", 64)
+    t = dev(x)
+    api.groupnorm_silu(t, dev(n["gm.weight"]), dev(n["gm.bias"]), out=t)
+    ref = oracle.silu(oracle.group_norm(x, n["gm.weight"], n["gm.bias"]))
+    assert rel_err(host(t), ref) <= LAYER_TOL
+
+
+@pytest.mark.parametrize("c,h,w", [(128, 64, 64), (3, 5, 7), (16, 1, 1)])
+def test_upsample_exact(api, c, h, w):
+    x = vaegen.activation(9, "xu2", (c, h, w))
+    y = api.upsample_nearest2x(dev(x), out=nan_like((c, 2 * h, 2 * w)))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), oracle.upsample_nearest2x(x).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("c,h,w", [(512, 8, 8), (64, 7, 9), (512, 32, 32), (128, 1, 1)])
+def test_attention(api, c, h, w):
+    p = vaegen.attention_params(10, "a", c)
+    x = vaegen.activation(10, "xa", (c, h, w))
+    y = api.attention(dev(x), {k: dev(v) for k, v in p.items()}, "a", out=nan_like((c, h, w)))
+    assert rel_err(host(y), oracle.attention(x, p, "a")) <= LAYER_TOL
+
+
+# ---------------------------------------------------------------------------
+# causal 3-D conv
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cin,cout,t,h,w", [(16, 32, 5, 6, 10), (128, 128, 4, 16, 16), (24, 130, 3, 9, 35)])
+def test_conv3d_causal(api, cin, cout, t, h, w):
+    x = vaegen.activation(11, "x3", (cin, t, h, w))
+    wt, b = conv_params(11, "c3", cin, cout, 3, dims=3)
+    y = api.conv3d_causal(dev(x), dev(wt), dev(b), out=nan_like((cout, t, h, w)))
+    assert rel_err(host(y), oracle.conv3d_causal(x, wt, b)) <= LAYER_TOL
+
+
+def test_causal_stack_small(api):
+    c = 64
+    p = vaegen.causal_stack_params(12, c=c)
+    x = vaegen.activation(12, "xs", (c, 5, 12, 12))
+    P = {k: dev(v) for k, v in p.items()}
+    h = dev(x)
+    for i in (0, 2):
+        cur = h
+        for j in (i, i + 1):
+            cur = api.conv3d_causal(cur, P[f"stack.{j}.conv.weight"], P[f"stack.{j}.conv.bias"])
+            cur = api.groupnorm_silu(cur, P[f"stack.{j}.norm.weight"], P[f"stack.{j}.norm.bias"],
+                                     residual=h if j == i + 1 else None, out=cur)
+        h = cur
+    ref = oracle.causal_stack(x, p)
+    assert rel_err(host(h), ref) <= LAYER_TOL
+
+
+# ---------------------------------------------------------------------------
+# whole decoder
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def params():
+    return vaegen.decoder_params(0)
+
+
+@pytest.fixture(scope="module")
+def decoder(api, params):
+    d = api.Decoder({k: dev(v) for k, v in params.items()}, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    yield d
+    d.close()
+
+
+def rgb_metrics(g, r):
+    assert not np.isnan(g).any()
+    cos = float((g * r).sum() / math.sqrt((g * g).sum() * (r * r).sum()))
+    return cos, float(np.abs(g - r).max())
+
+
+def test_decode_64(decoder, params):
+    z = vaegen.latent(0, 8, 8)
+    rgb = decoder.decode(dev(z), out=nan_like((3, 64, 64)))
+    ref = oracle.decode(z, params, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    cos, mx = rgb_metrics(host(rgb), ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
+def test_decode_ragged_latent(decoder, params):
+    z = vaegen.latent(5, 5, 3)
+    rgb = decoder.decode(dev(z), out=nan_like((3, 40, 24)))
+    ref = oracle.decode(z, params, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    cos, mx = rgb_metrics(host(rgb), ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
+@pytest.mark.parametrize("name,h", [("decode_256", 32), ("decode_1024", 128)])
+def test_decode_full_size_against_stored_oracle(decoder, name, h):
+    path = os.path.join(GOLDEN, name + ".npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    g = np.load(path)
+    assert int(g["seed"]) == 0
+    z = vaegen.latent(0, h, h)
+    rgb = host(decoder.decode(dev(z), out=nan_like(tuple(g["shape"]))))
+    s = int(g["stride"])
+    sample = rgb[:, ::s, ::s]
+    ref = g["sample"]
+    cos, mx = rgb_metrics(sample, ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * float(g["max_abs"]), (cos, mx)
+    # the whole image: finite, and its norm matches the oracle's
+    assert np.isfinite(rgb).all()
+    assert abs(math.sqrt((rgb * rgb).sum()) / float(g["l2"]) - 1.0) < 1e-4
+
+
+def test_decode_is_deterministic(decoder):
+    z = dev(vaegen.latent(1, 16, 16))
+    a = decoder.decode(z).cpu()
+    b = decoder.decode(z).cpu()
+    assert torch.equal(a, b)
