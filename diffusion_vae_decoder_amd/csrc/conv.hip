@@ -71,34 +71,46 @@ struct Params {
 
 enum { MODE_PLAIN = 0, MODE_UPSAMPLE = 1, MODE_DENORM = 2 };
 
+// Offset that lies outside every buffer range below: a buffer load from it
+// returns 0 without touching memory (the zero padding of the halo).
+constexpr int kOOB = 0x7FFFFFF0;
+
+__device__ __attribute__((always_inline)) inline __amdgpu_buffer_rsrc_t make_rsrc(const float *base,
+                                                                                 unsigned bytes) {
+    // raw buffer (stride 0), range `bytes`, gfx9 resource word 3
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Global -> registers: chunk `it` = (time tap dt, channel block cb) of the
-// packed weights and of the input halo.
+// packed weights and of the input halo.  The halo buffer range covers only the
+// chunk's valid channels, so channels past cin and padding positions (offset
+// kOOB) both read as 0 with no branch.
 template <int TC, int MODE>
 __device__ __attribute__((always_inline)) inline void stage_load(
-    const Params &p, const float *wbase, int it, int frame, const int (&h_sp)[Geom<TC>::HALO_PER_T],
+    const Params &p, const float *wbase, int it, int frame, const int (&h_boff)[Geom<TC>::HALO_PER_T],
     const int (&h_c)[Geom<TC>::HALO_PER_T], floatx4 (&wreg)[kW4_PER_T],
     float (&xreg)[Geom<TC>::HALO_PER_T]) {
     using G = Geom<TC>;
     const int tid = threadIdx.x;
     const int dt = it / p.n_cb;
     const int cb = it - dt * p.n_cb;
-    const floatx4 *wsrc = reinterpret_cast<const floatx4 *>(wbase + (size_t)it * (kCK * kConvBM));
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase + (size_t)it * (kCK * kConvBM), kCK * kConvBM * 4);
 #pragma unroll
     for (int i = 0; i < kW4_PER_T; ++i) {
         const int idx = tid + i * kThreads;
-        if (kW4 % kThreads == 0 || idx < kW4) wreg[i] = wsrc[idx];
+        if (kW4 % kThreads == 0 || (i + 1) * kThreads <= kW4 || idx < kW4)
+            wreg[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(wr, idx * 16, 0, 0));
     }
     int fr = frame + dt - (p.kt - 1);
     fr = fr < 0 ? 0 : fr;
-    const float *xs = p.x + (long long)fr * p.in_fstride;
+    const int c0 = cb * kConvCC;
+    const int nc = p.cin - c0 < kConvCC ? p.cin - c0 : kConvCC;
+    const float *xs = p.x + (long long)fr * p.in_fstride + (long long)c0 * p.in_cstride;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(xs, (unsigned)(nc * p.in_cstride * 4));
 #pragma unroll
     for (int i = 0; i < G::HALO_PER_T; ++i) {
-        float v = 0.f;
-        const int c = cb * kConvCC + h_c[i];
-        if (h_sp[i] >= 0 && c < p.cin) {
-            v = xs[(long long)c * p.in_cstride + h_sp[i]];
-            if (MODE == MODE_DENORM) v = v / p.dn_scale + p.dn_shift;
-        }
+        float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xr, h_boff[i], 0, 0));
+        if (MODE == MODE_DENORM) v = (h_boff[i] != kOOB && h_c[i] < nc) ? v / p.dn_scale + p.dn_shift : 0.f;
         xreg[i] = v;
     }
 }
@@ -112,18 +124,18 @@ __device__ __attribute__((always_inline)) inline void stage_store(
 #pragma unroll
     for (int i = 0; i < kW4_PER_T; ++i) {
         const int idx = tid + i * kThreads;
-        if (kW4 % kThreads == 0 || idx < kW4) {
+        if (kW4 % kThreads == 0 || (i + 1) * kThreads <= kW4 || idx < kW4) {
             const int row = idx >> 5, c4 = idx & 31;
             *reinterpret_cast<floatx4 *>(&lw[row * kLdaW + c4 * 4]) = wreg[i];
         }
     }
 #pragma unroll
     for (int i = 0; i < Geom<TC>::HALO_PER_T; ++i)
-        if (h_lds[i] >= 0) lx[h_lds[i]] = xreg[i];
+        if ((i + 1) * kThreads <= Geom<TC>::HALO || h_lds[i] >= 0) lx[h_lds[i]] = xreg[i];
 }
 
 template <int TC, int MODE, bool RES>
-__global__ __launch_bounds__(kThreads) void conv3x3_mfma(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void conv3x3_mfma(Params p) {
     using G = Geom<TC>;
     __shared__ __attribute__((aligned(16))) float lds_w[2][kCK * kLdaW];
     __shared__ float lds_x[2][kConvCC * G::PLANE];
@@ -134,7 +146,12 @@ __global__ __launch_bounds__(kThreads) void conv3x3_mfma(Params p) {
     const int wm = wave >> 1, wn = wave & 1;
     const int half = lane >> 5, l32 = lane & 31;
 
-    const int tile = blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round-robin by linear id.  When the
+    // tile count is a multiple of 8 (then the linear id and blockIdx.x agree
+    // mod 8), renumber so each XCD walks one contiguous band of tiles: tiles
+    // that share halo rows and columns then share one L2.
+    int tile = blockIdx.x;
+    if ((gridDim.x & 7) == 0) tile = (tile & 7) * (gridDim.x >> 3) + (tile >> 3);
     const int ty = tile / p.tiles_x;
     const int tx = tile - ty * p.tiles_x;
     const int y0 = ty * G::TR, x0 = tx * TC;
@@ -142,14 +159,14 @@ __global__ __launch_bounds__(kThreads) void conv3x3_mfma(Params p) {
     const int frame = blockIdx.z;
 
     // Per-thread halo elements: their LDS slot, channel within the chunk and
-    // spatial offset in the source plane (-1 = zero padding).  They are the
-    // same for every chunk.
-    int h_lds[G::HALO_PER_T], h_sp[G::HALO_PER_T], h_c[G::HALO_PER_T];
+    // byte offset from the chunk's first channel (kOOB = zero padding).  They
+    // are the same for every chunk.
+    int h_lds[G::HALO_PER_T], h_boff[G::HALO_PER_T], h_c[G::HALO_PER_T];
 #pragma unroll
     for (int i = 0; i < G::HALO_PER_T; ++i) {
         const int e = tid + i * kThreads;
         h_lds[i] = -1;
-        h_sp[i] = -1;
+        h_boff[i] = kOOB;
         h_c[i] = 0;
         if (e < G::HALO) {
             const int c = e / G::HP;
@@ -159,8 +176,10 @@ __global__ __launch_bounds__(kThreads) void conv3x3_mfma(Params p) {
             const int yy = y0 - 1 + rr, xx = x0 - 1 + cc;
             h_lds[i] = c * G::PLANE + rr * G::HWD + cc;
             h_c[i] = c;
-            if (yy >= 0 && yy < p.H && xx >= 0 && xx < p.W)
-                h_sp[i] = (MODE == MODE_UPSAMPLE) ? (yy >> 1) * p.Win + (xx >> 1) : yy * p.W + xx;
+            if (yy >= 0 && yy < p.H && xx >= 0 && xx < p.W) {
+                const int sp = (MODE == MODE_UPSAMPLE) ? (yy >> 1) * p.Win + (xx >> 1) : yy * p.W + xx;
+                h_boff[i] = (c * (int)p.in_cstride + sp) * 4;
+            }
         }
     }
 
@@ -189,13 +208,13 @@ __global__ __launch_bounds__(kThreads) void conv3x3_mfma(Params p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    stage_load<TC, MODE>(p, wbase, 0, frame, h_sp, h_c, wreg, xreg);
+    stage_load<TC, MODE>(p, wbase, 0, frame, h_boff, h_c, wreg, xreg);
     stage_store<TC>(lds_w[0], lds_x[0], h_lds, wreg, xreg);
     __syncthreads();
 
     for (int it = 0; it < n_iter; ++it) {
         const int buf = it & 1;
-        if (it + 1 < n_iter) stage_load<TC, MODE>(p, wbase, it + 1, frame, h_sp, h_c, wreg, xreg);
+        if (it + 1 < n_iter) stage_load<TC, MODE>(p, wbase, it + 1, frame, h_boff, h_c, wreg, xreg);
         const float *A = lds_w[buf];
         const float *B = lds_x[buf];
 #pragma unroll
@@ -425,6 +444,11 @@ int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s) {
     const int tiles_y = (a.H + TR - 1) / TR;
     const dim3 grid((unsigned)(p.tiles_x * tiles_y), (unsigned)((a.cout + kConvBM - 1) / kConvBM),
                     (unsigned)a.T);
+    // byte offsets inside one channel chunk are 32-bit
+    if (p.in_cstride * kConvCC * 4 >= (1LL << 31)) {
+        set_error("conv3x3: input plane of %lld elements is too large", p.in_cstride);
+        return VAE_ERR_UNSUPPORTED;
+    }
     const int mode = a.upsample ? MODE_UPSAMPLE : (a.denorm ? MODE_DENORM : MODE_PLAIN);
     const bool res = a.res != nullptr;
     if (TC == 32) launch_tc<32>(p, mode, res, grid, s);

@@ -24,7 +24,7 @@ int32_t check_launch(const char *what);
 // channels x 128 output pixels (TR rows x TC columns of one frame).
 constexpr int kConvBM = 128;
 constexpr int kConvBN = 128;
-constexpr int kConvCC = 8;   // input channels per K chunk (K chunk = 8 x 9 taps)
+constexpr int kConvCC = 4;   // input channels per K chunk (K chunk = 4 x 9 taps)
 
 struct ConvLaunch {
     const float *x;        // input activations
