@@ -21,6 +21,7 @@ the device and the latent already resident in HBM.  Default workload: latent
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -52,6 +53,31 @@ def parse():
                     help="after the decodes, run one plain device copy of this many MiB "
                          "(reference dispatch for calibrating HBM byte counters)")
     return ap.parse_args()
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "conv3x3_mfma_decode1024_hbm_counters.md")
+CONV_SRC = os.path.join(ROOT, "diffusion_vae_decoder_amd", "csrc", "conv.hip")
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when that summary was taken on another kernel,
+    another workload, or a conv source that has changed since."""
+    if workload != "decode1024":
+        return None
+    try:
+        text = open(COUNTERS).read()
+        src = open(CONV_SRC, "rb").read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        key, _, val = line.partition(": ")
+        if key in ("traffic_bytes_per_launch", "kernel", "kernel_source_sha256"):
+            vals[key] = val.strip()
+    if vals.get("kernel") != kernel or vals.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return float(vals["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(seed: int, h: int) -> dict:
@@ -163,9 +189,10 @@ def main():
     if dom["flops"] > 0:
         achieved = dom["flops"] / (dom["ms"] / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": None, "kernel": dom_name,
-                "launches_per_step": dom["n"] // args.steps, "avg_launch_ms": dom["ms"] / dom["n"],
-                "flops_per_launch": dom["flops"] / dom["n"]}
+                "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "traffic": counter_traffic(dom_name, args.workload),
+                "kernel": dom_name, "launches_per_step": dom["n"] // args.steps,
+                "avg_launch_ms": dom["ms"] / dom["n"], "flops_per_launch": dom["flops"] / dom["n"],
+                "algorithmic_bytes_per_launch": dom["bytes"] / dom["n"]}
     else:
         achieved = dom["bytes"] / (dom["ms"] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
