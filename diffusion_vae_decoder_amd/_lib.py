@@ -16,7 +16,7 @@ VAE_ERR_INVALID_ARG = -1
 VAE_ERR_UNSUPPORTED = -2
 VAE_ERR_WORKSPACE = -3
 VAE_ERR_HIP = -4
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class VaeConv(ctypes.Structure):
@@ -57,7 +57,7 @@ class VaeProfRecord(ctypes.Structure):
 SIGNATURES = {
     "vae_last_error": (c_char_p, []),
     "vae_abi_version": (c_int32, []),
-    "vae_conv2d_workspace_bytes": (c_int32, [POINTER(VaeConv), POINTER(c_size_t)]),
+    "vae_conv2d_workspace_bytes": (c_int32, [POINTER(VaeConv), c_int32, c_int32, c_int32, POINTER(c_size_t)]),
     "vae_conv2d": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(VaeConv), c_int32, c_void_p,
                              c_void_p, c_void_p, c_size_t, c_void_p]),
     "vae_conv_in": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(VaeConv), c_float, c_float,
@@ -69,7 +69,8 @@ SIGNATURES = {
     "vae_attention_workspace_bytes": (c_int32, [c_int32, c_int32, c_int32, POINTER(c_size_t)]),
     "vae_attention": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(VaeAttn), c_void_p,
                                 c_void_p, c_size_t, c_void_p]),
-    "vae_conv3d_causal_workspace_bytes": (c_int32, [POINTER(VaeConv), POINTER(c_size_t)]),
+    "vae_conv3d_causal_workspace_bytes": (c_int32, [POINTER(VaeConv), c_int32, c_int32, c_int32,
+                                                    POINTER(c_size_t)]),
     "vae_conv3d_causal": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(VaeConv),
                                     c_void_p, c_void_p, c_size_t, c_void_p]),
     "vae_decoder_pack_bytes": (c_int32, [POINTER(VaeWeights), POINTER(c_size_t)]),

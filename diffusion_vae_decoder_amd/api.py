@@ -91,7 +91,7 @@ def conv2d(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor, upsample2x
         _dev(residual, "residual")
     y = _out(out, (weight.shape[0], H, W), x.device)
     nb = c_size_t()
-    check(lib.vae_conv2d_workspace_bytes(byref(conv), byref(nb)))
+    check(lib.vae_conv2d_workspace_bytes(byref(conv), h, w, int(bool(upsample2x)), byref(nb)))
     ws = _ws(nb.value, x.device)
     check(lib.vae_conv2d(x.data_ptr(), cin, h, w, byref(conv), int(bool(upsample2x)), _ptr(residual),
                          y.data_ptr(), _ptr(ws), nb.value, _stream()))
@@ -107,7 +107,7 @@ def conv_in(z: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor, scaling_f
     conv = _conv(weight, bias)
     y = _out(out, (weight.shape[0], h, w), z.device)
     nb = c_size_t()
-    check(lib.vae_conv2d_workspace_bytes(byref(conv), byref(nb)))
+    check(lib.vae_conv2d_workspace_bytes(byref(conv), h, w, 0, byref(nb)))
     ws = _ws(nb.value, z.device)
     check(lib.vae_conv_in(z.data_ptr(), cin, h, w, byref(conv), float(scaling_factor), float(shift_factor),
                           y.data_ptr(), _ptr(ws), nb.value, _stream()))
@@ -172,7 +172,7 @@ def conv3d_causal(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor,
     conv = _conv(weight, bias)
     y = _out(out, (weight.shape[0], t, h, w), x.device)
     nb = c_size_t()
-    check(lib.vae_conv3d_causal_workspace_bytes(byref(conv), byref(nb)))
+    check(lib.vae_conv3d_causal_workspace_bytes(byref(conv), t, h, w, byref(nb)))
     ws = _ws(nb.value, x.device)
     check(lib.vae_conv3d_causal(x.data_ptr(), cin, t, h, w, byref(conv), y.data_ptr(), _ptr(ws), nb.value,
                                 _stream()))

@@ -74,9 +74,19 @@ int32_t check_plane(const char *who, long long c, long long h, long long w) {
     return VAE_OK;
 }
 
-size_t conv_ws(const vae_conv *c, int kt) {
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace of a 3x3 conv producing [cout, T, H, W]: the repacked weights, then
+// the split-K partial sums (if the shape is split).
+size_t conv_ws(const vae_conv *c, int kt, int T, int H, int W) {
     if (c->kernel == 1) return 0;
-    return conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float);
+    return align256(conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float)) +
+           conv3x3_partial_floats(c->out_channels, c->in_channels, kt, H, W, T) * sizeof(float);
+}
+
+float *conv_ws_part(const vae_conv *c, int kt, void *ws) {
+    return reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                     align256(conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float)));
 }
 
 }  // namespace
@@ -87,11 +97,14 @@ const char *vae_last_error(void) { return g_err; }
 
 int32_t vae_abi_version(void) { return VAE_ABI_VERSION; }
 
-int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, size_t *bytes) {
+int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, int32_t h, int32_t w, int32_t upsample2x,
+                                   size_t *bytes) {
     int32_t rc = check_conv("vae_conv2d_workspace_bytes", conv, 0);
     if (rc) return rc;
     if (!bytes) return bad("vae_conv2d_workspace_bytes: bytes is NULL");
-    *bytes = conv_ws(conv, 1);
+    if ((rc = check_plane("vae_conv2d_workspace_bytes", conv->out_channels, upsample2x ? 2LL * h : h,
+                          upsample2x ? 2LL * w : w))) return rc;
+    *bytes = conv_ws(conv, 1, 1, upsample2x ? 2 * h : h, upsample2x ? 2 * w : w);
     return VAE_OK;
 }
 
@@ -120,12 +133,13 @@ int32_t vae_conv2d(const float *x, int32_t cin, int32_t h, int32_t w, const vae_
     }
     if (conv->out_channels <= 4 && !upsample2x && !residual)
         return launch_conv3x3_skinny(x, conv->weight, conv->bias, y, cin, conv->out_channels, h, w, s);
-    const size_t need = conv_ws(conv, 1);
+    const size_t need = conv_ws(conv, 1, 1, H, W);
     if (!ws || ws_bytes < need)
         return set_error("vae_conv2d: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
     if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 1, static_cast<float *>(ws), s))) return rc;
     ConvLaunch a{};
     a.x = x; a.wpk = static_cast<const float *>(ws); a.bias = conv->bias; a.res = residual; a.y = y;
+    a.part = conv_ws_part(conv, 1, ws);
     a.cin = cin; a.cout = conv->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
     a.upsample = upsample2x ? 1 : 0;
     return launch_conv3x3(a, s);
@@ -142,13 +156,14 @@ int32_t vae_conv_in(const float *z, int32_t cin, int32_t h, int32_t w, const vae
     if (conv->in_channels != cin) return bad("vae_conv_in: conv expects %d input channels, got %d", conv->in_channels, cin);
     if (!(scaling_factor != 0.f)) return bad("vae_conv_in: scaling_factor must be non-zero");
     if (z == y) return bad("vae_conv_in: y may not alias z");
-    const size_t need = conv_ws(conv, 1);
+    const size_t need = conv_ws(conv, 1, 1, h, w);
     if (!ws || ws_bytes < need)
         return set_error("vae_conv_in: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 1, static_cast<float *>(ws), s))) return rc;
     ConvLaunch a{};
     a.x = z; a.wpk = static_cast<const float *>(ws); a.bias = conv->bias; a.y = y;
+    a.part = conv_ws_part(conv, 1, ws);
     a.cin = cin; a.cout = conv->out_channels; a.H = h; a.W = w; a.T = 1; a.kt = 1;
     a.denorm = 1; a.dn_scale = scaling_factor; a.dn_shift = shift_factor;
     return launch_conv3x3(a, s);
@@ -229,11 +244,15 @@ int32_t vae_attention(const float *x, int32_t c, int32_t h, int32_t w, const vae
                             attn->out.bias, y, ws, s);
 }
 
-int32_t vae_conv3d_causal_workspace_bytes(const vae_conv *conv, size_t *bytes) {
+int32_t vae_conv3d_causal_workspace_bytes(const vae_conv *conv, int32_t t, int32_t h, int32_t w,
+                                          size_t *bytes) {
     int32_t rc = check_conv("vae_conv3d_causal_workspace_bytes", conv, 3);
     if (rc) return rc;
     if (!bytes) return bad("vae_conv3d_causal_workspace_bytes: bytes is NULL");
-    *bytes = conv_ws(conv, 3);
+    if (t <= 0) return bad("vae_conv3d_causal_workspace_bytes: t must be positive");
+    if (t > 65535) return unsupported("vae_conv3d_causal_workspace_bytes: t %d exceeds the grid limit", t);
+    if ((rc = check_plane("vae_conv3d_causal_workspace_bytes", (long long)conv->out_channels * t, h, w))) return rc;
+    *bytes = conv_ws(conv, 3, t, h, w);
     return VAE_OK;
 }
 
@@ -248,13 +267,14 @@ int32_t vae_conv3d_causal(const float *x, int32_t cin, int32_t t, int32_t h, int
     if (t > 65535) return unsupported("vae_conv3d_causal: t %d exceeds the grid limit", t);
     if (conv->in_channels != cin) return bad("vae_conv3d_causal: conv expects %d input channels, got %d", conv->in_channels, cin);
     if (x == y) return bad("vae_conv3d_causal: y may not alias x");
-    const size_t need = conv_ws(conv, 3);
+    const size_t need = conv_ws(conv, 3, t, h, w);
     if (!ws || ws_bytes < need)
         return set_error("vae_conv3d_causal: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 3, static_cast<float *>(ws), s))) return rc;
     ConvLaunch a{};
     a.x = x; a.wpk = static_cast<const float *>(ws); a.bias = conv->bias; a.y = y;
+    a.part = conv_ws_part(conv, 3, ws);
     a.cin = cin; a.cout = conv->out_channels; a.H = h; a.W = w; a.T = t; a.kt = 3;
     return launch_conv3x3(a, s);
 }

@@ -64,8 +64,9 @@ constexpr int kW4_PER_T = (kW4 + kThreads - 1) / kThreads;
 struct Params {
     const float *x, *wpk, *bias, *res;
     float *y;
-    int cin, cout, H, W, Win, kt, n_cb, tiles_x;
-    long long in_cstride, in_fstride, out_cstride, out_fstride;
+    float *part;            // split-K partial sums [ksplit][cout][T][H][W] (ksplit > 1)
+    int cin, cout, H, W, Win, kt, n_cb, tiles_x, ksplit;
+    long long in_cstride, in_fstride, out_cstride, out_fstride, part_stride;
     float dn_scale, dn_shift;
 };
 
@@ -134,7 +135,7 @@ __device__ __attribute__((always_inline)) inline void stage_store(
         if ((i + 1) * kThreads <= Geom<TC>::HALO || h_lds[i] >= 0) lx[h_lds[i]] = xreg[i];
 }
 
-template <int TC, int MODE, bool RES>
+template <int TC, int MODE, bool RES, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void conv3x3_mfma(Params p) {
     using G = Geom<TC>;
     __shared__ __attribute__((aligned(16))) float lds_w[2][kCK * kLdaW];
@@ -156,7 +157,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int tx = tile - ty * p.tiles_x;
     const int y0 = ty * G::TR, x0 = tx * TC;
     const int ob = blockIdx.y;
-    const int frame = blockIdx.z;
+    // blockIdx.z = frame * ksplit + split: split s accumulates the K chunks
+    // [s * n / ksplit, (s + 1) * n / ksplit) of the n = kt * n_cb chunks.
+    const int frame = SPLIT ? blockIdx.z / p.ksplit : blockIdx.z;
+    const int split = SPLIT ? blockIdx.z - frame * p.ksplit : 0;
 
     // Per-thread halo elements: their LDS slot, channel within the chunk and
     // byte offset from the chunk's first channel (kOOB = zero padding).  They
@@ -184,6 +188,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 
     const int n_iter = p.kt * p.n_cb;
+    const int it0 = SPLIT ? (int)((long long)split * n_iter / p.ksplit) : 0;
+    const int it1 = SPLIT ? (int)((long long)(split + 1) * n_iter / p.ksplit) : n_iter;
     const float *wbase = p.wpk + (size_t)ob * n_iter * (kCK * kConvBM);
 
     floatx4 wreg[kW4_PER_T];
@@ -208,13 +214,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    stage_load<TC, MODE>(p, wbase, 0, frame, h_boff, h_c, wreg, xreg);
+    stage_load<TC, MODE>(p, wbase, it0, frame, h_boff, h_c, wreg, xreg);
     stage_store<TC>(lds_w[0], lds_x[0], h_lds, wreg, xreg);
     __syncthreads();
 
-    for (int it = 0; it < n_iter; ++it) {
-        const int buf = it & 1;
-        if (it + 1 < n_iter) stage_load<TC, MODE>(p, wbase, it + 1, frame, h_boff, h_c, wreg, xreg);
+    for (int it = it0; it < it1; ++it) {
+        const int buf = (it - it0) & 1;
+        if (it + 1 < it1) stage_load<TC, MODE>(p, wbase, it + 1, frame, h_boff, h_c, wreg, xreg);
         const float *A = lds_w[buf];
         const float *B = lds_x[buf];
 #pragma unroll
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
             acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
         }
-        if (it + 1 < n_iter) stage_store<TC>(lds_w[buf ^ 1], lds_x[buf ^ 1], h_lds, wreg, xreg);
+        if (it + 1 < it1) stage_store<TC>(lds_w[buf ^ 1], lds_x[buf ^ 1], h_lds, wreg, xreg);
         __syncthreads();
     }
 
@@ -251,9 +257,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 const int o = ob * kConvBM + m;
                 if (o < p.cout) {
                     const long long off = (long long)o * p.out_cstride + sp;
-                    float v = acc[i][j][r] + p.bias[o];
-                    if (RES) v += p.res[off];
-                    p.y[off] = v;
+                    if (SPLIT) {
+                        p.part[split * p.part_stride + off] = acc[i][j][r];
+                    } else {
+                        float v = acc[i][j][r] + p.bias[o];
+                        if (RES) v += p.res[off];
+                        p.y[off] = v;
+                    }
                 }
             }
         }
@@ -282,22 +292,54 @@ __global__ void pack_conv3x3_kernel(const float *__restrict__ w, float *__restri
     dst[idx] = v;
 }
 
+// y[o, :] = bias[o] + sum_s part[s, o, :] (+ res[o, :]), summed in split order.
+constexpr int kRedElems = 4096;   // elements per workgroup
+
+template <bool VEC, bool RES>
+__global__ __launch_bounds__(kThreads) void splitk_reduce(const float *__restrict__ part, long long part_stride,
+                                                          int ksplit, const float *__restrict__ bias,
+                                                          const float *res, float *y, long long plane) {
+    const int o = blockIdx.y;
+    const long long base = (long long)o * plane;
+    const long long lo = (long long)blockIdx.x * kRedElems;
+    long long hi = lo + kRedElems;
+    if (hi > plane) hi = plane;
+    const float b = bias[o];
+    if (VEC) {
+        for (long long i = lo / 4 + threadIdx.x; i < hi / 4; i += kThreads) {
+            floatx4 v = {b, b, b, b};
+            for (int sp = 0; sp < ksplit; ++sp)
+                v += reinterpret_cast<const floatx4 *>(part + sp * part_stride + base)[i];
+            if (RES) v += reinterpret_cast<const floatx4 *>(res + base)[i];
+            reinterpret_cast<floatx4 *>(y + base)[i] = v;
+        }
+    } else {
+        for (long long i = lo + threadIdx.x; i < hi; i += kThreads) {
+            float v = b;
+            for (int sp = 0; sp < ksplit; ++sp) v += part[sp * part_stride + base + i];
+            if (RES) v += res[base + i];
+            y[base + i] = v;
+        }
+    }
+}
+
 template <int TC, int MODE, bool RES>
-void launch_t(const Params &p, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((conv3x3_mfma<TC, MODE, RES>), grid, dim3(kThreads), 0, s, p);
+void launch_t(const Params &p, bool split, dim3 grid, hipStream_t s) {
+    if (split) hipLaunchKernelGGL((conv3x3_mfma<TC, MODE, false, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((conv3x3_mfma<TC, MODE, RES, false>), grid, dim3(kThreads), 0, s, p);
 }
 
 template <int TC>
-void launch_tc(const Params &p, int mode, bool res, dim3 grid, hipStream_t s) {
+void launch_tc(const Params &p, int mode, bool res, bool split, dim3 grid, hipStream_t s) {
     if (mode == MODE_UPSAMPLE) {
-        if (res) launch_t<TC, MODE_UPSAMPLE, true>(p, grid, s);
-        else launch_t<TC, MODE_UPSAMPLE, false>(p, grid, s);
+        if (res) launch_t<TC, MODE_UPSAMPLE, true>(p, split, grid, s);
+        else launch_t<TC, MODE_UPSAMPLE, false>(p, split, grid, s);
     } else if (mode == MODE_DENORM) {
-        if (res) launch_t<TC, MODE_DENORM, true>(p, grid, s);
-        else launch_t<TC, MODE_DENORM, false>(p, grid, s);
+        if (res) launch_t<TC, MODE_DENORM, true>(p, split, grid, s);
+        else launch_t<TC, MODE_DENORM, false>(p, split, grid, s);
     } else {
-        if (res) launch_t<TC, MODE_PLAIN, true>(p, grid, s);
-        else launch_t<TC, MODE_PLAIN, false>(p, grid, s);
+        if (res) launch_t<TC, MODE_PLAIN, true>(p, split, grid, s);
+        else launch_t<TC, MODE_PLAIN, false>(p, split, grid, s);
     }
 }
 
@@ -398,26 +440,46 @@ int32_t pack_conv3x3(const float *w, int cout, int cin, int kt, float *dst, hipS
 
 namespace {
 int conv_tc(int W) { return W > 16 ? 32 : (W > 8 ? 16 : 8); }
+constexpr int kSlots = 256 * 3;   // CUs x resident conv workgroups per CU
 }  // namespace
 
+int conv3x3_ksplit(int cout, int cin, int kt, int H, int W, int T) {
+    const int TC = conv_tc(W), TR = kConvBN / TC;
+    const long long base = (long long)((W + TC - 1) / TC) * ((H + TR - 1) / TR) *
+                           ((cout + kConvBM - 1) / kConvBM) * T;
+    if (base >= kSlots) return 1;
+    const int n_iter = kt * ((cin + kConvCC - 1) / kConvCC);
+    long long s = (2 * kSlots + base - 1) / base;   // about two rounds of workgroups
+    if (s > n_iter / 8) s = n_iter / 8;              // each split keeps >= 8 K chunks
+    if (s > 16) s = 16;
+    if (s * T > 65535) s = 65535 / T;
+    return s < 1 ? 1 : (int)s;
+}
+
+size_t conv3x3_partial_floats(int cout, int cin, int kt, int H, int W, int T) {
+    const int ks = conv3x3_ksplit(cout, cin, kt, H, W, T);
+    return ks > 1 ? (size_t)ks * cout * T * (size_t)H * W : 0;
+}
+
 const char *conv3x3_kernel_name(const ConvLaunch &a) {
-    static const char *names[3][3][2] = {
-        {{"conv3x3_mfma<32,plain>", "conv3x3_mfma<32,plain,res>"},
-         {"conv3x3_mfma<32,up2x>", "conv3x3_mfma<32,up2x,res>"},
-         {"conv3x3_mfma<32,denorm>", "conv3x3_mfma<32,denorm,res>"}},
-        {{"conv3x3_mfma<16,plain>", "conv3x3_mfma<16,plain,res>"},
-         {"conv3x3_mfma<16,up2x>", "conv3x3_mfma<16,up2x,res>"},
-         {"conv3x3_mfma<16,denorm>", "conv3x3_mfma<16,denorm,res>"}},
-        {{"conv3x3_mfma<8,plain>", "conv3x3_mfma<8,plain,res>"},
-         {"conv3x3_mfma<8,up2x>", "conv3x3_mfma<8,up2x,res>"},
-         {"conv3x3_mfma<8,denorm>", "conv3x3_mfma<8,denorm,res>"}}};
+    static const char *names[3][3][3] = {
+        {{"conv3x3_mfma<32,plain>", "conv3x3_mfma<32,plain,res>", "conv3x3_mfma<32,plain,splitk>"},
+         {"conv3x3_mfma<32,up2x>", "conv3x3_mfma<32,up2x,res>", "conv3x3_mfma<32,up2x,splitk>"},
+         {"conv3x3_mfma<32,denorm>", "conv3x3_mfma<32,denorm,res>", "conv3x3_mfma<32,denorm,splitk>"}},
+        {{"conv3x3_mfma<16,plain>", "conv3x3_mfma<16,plain,res>", "conv3x3_mfma<16,plain,splitk>"},
+         {"conv3x3_mfma<16,up2x>", "conv3x3_mfma<16,up2x,res>", "conv3x3_mfma<16,up2x,splitk>"},
+         {"conv3x3_mfma<16,denorm>", "conv3x3_mfma<16,denorm,res>", "conv3x3_mfma<16,denorm,splitk>"}},
+        {{"conv3x3_mfma<8,plain>", "conv3x3_mfma<8,plain,res>", "conv3x3_mfma<8,plain,splitk>"},
+         {"conv3x3_mfma<8,up2x>", "conv3x3_mfma<8,up2x,res>", "conv3x3_mfma<8,up2x,splitk>"},
+         {"conv3x3_mfma<8,denorm>", "conv3x3_mfma<8,denorm,res>", "conv3x3_mfma<8,denorm,splitk>"}}};
     const int tc = conv_tc(a.W);
     const int ti = tc == 32 ? 0 : (tc == 16 ? 1 : 2);
     const int mi = a.upsample ? 1 : (a.denorm ? 2 : 0);
-    return names[ti][mi][a.res ? 1 : 0];
+    const int si = conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T) > 1 ? 2 : (a.res ? 1 : 0);
+    return names[ti][mi][si];
 }
 
-int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s) {
+int32_t launch_conv3x3_main(const ConvLaunch &a, hipStream_t s) {
     Params p;
     p.x = a.x;
     p.wpk = a.wpk;
@@ -442,19 +504,53 @@ int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s) {
     const int TR = kConvBN / TC;
     p.tiles_x = (a.W + TC - 1) / TC;
     const int tiles_y = (a.H + TR - 1) / TR;
-    const dim3 grid((unsigned)(p.tiles_x * tiles_y), (unsigned)((a.cout + kConvBM - 1) / kConvBM),
-                    (unsigned)a.T);
+    p.ksplit = conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T);
+    p.part = a.part;
+    p.part_stride = p.out_cstride * a.cout;
+    if (p.ksplit > 1 && !a.part) {
+        set_error("conv3x3: split-K needs a partial-sum workspace");
+        return VAE_ERR_WORKSPACE;
+    }
     // byte offsets inside one channel chunk are 32-bit
     if (p.in_cstride * kConvCC * 4 >= (1LL << 31)) {
         set_error("conv3x3: input plane of %lld elements is too large", p.in_cstride);
         return VAE_ERR_UNSUPPORTED;
     }
+    const dim3 grid((unsigned)(p.tiles_x * tiles_y), (unsigned)((a.cout + kConvBM - 1) / kConvBM),
+                    (unsigned)(a.T * p.ksplit));
     const int mode = a.upsample ? MODE_UPSAMPLE : (a.denorm ? MODE_DENORM : MODE_PLAIN);
     const bool res = a.res != nullptr;
-    if (TC == 32) launch_tc<32>(p, mode, res, grid, s);
-    else if (TC == 16) launch_tc<16>(p, mode, res, grid, s);
-    else launch_tc<8>(p, mode, res, grid, s);
+    const bool split = p.ksplit > 1;
+    if (TC == 32) launch_tc<32>(p, mode, res, split, grid, s);
+    else if (TC == 16) launch_tc<16>(p, mode, res, split, grid, s);
+    else launch_tc<8>(p, mode, res, split, grid, s);
     return check_launch("conv3x3_mfma");
+}
+
+int32_t launch_conv3x3_reduce(const ConvLaunch &a, hipStream_t s) {
+    const int ksplit = conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T);
+    if (ksplit == 1) return VAE_OK;
+    const long long plane = (long long)a.T * a.H * a.W;
+    const long long part_stride = plane * a.cout;
+    const bool res = a.res != nullptr;
+    const dim3 rgrid((unsigned)((plane + kRedElems - 1) / kRedElems), (unsigned)a.cout);
+    const bool vec = plane % 4 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.part) & 15) == 0 &&
+                     (!res || (reinterpret_cast<uintptr_t>(a.res) & 15) == 0);
+    if (vec) {
+        if (res) hipLaunchKernelGGL((splitk_reduce<true, true>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane);
+        else hipLaunchKernelGGL((splitk_reduce<true, false>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane);
+    } else {
+        if (res) hipLaunchKernelGGL((splitk_reduce<false, true>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane);
+        else hipLaunchKernelGGL((splitk_reduce<false, false>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane);
+    }
+    return check_launch("splitk_reduce");
+}
+
+int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s) {
+    int32_t rc = launch_conv3x3_main(a, s);
+    if (rc != VAE_OK) return rc;
+    return launch_conv3x3_reduce(a, s);
 }
 
 int32_t launch_conv3x3_skinny(const float *x, const float *w, const float *bias, float *y, int cin,

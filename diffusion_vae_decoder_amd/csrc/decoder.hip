@@ -230,6 +230,7 @@ namespace {
 
 struct Buffers {
     float *X, *Y, *T, *U, *S;
+    float *part;   // split-K partial sums of the small convs
     void *gn;
     void *attn;
 };
@@ -237,7 +238,7 @@ struct Buffers {
 // The chain's spatial plan for a latent of (h, w): largest activation (floats),
 // largest GroupNorm workspace, attention workspace.
 struct Plan {
-    size_t act = 0, gn = 0, attn = 0;
+    size_t act = 0, gn = 0, attn = 0, part = 0;
 };
 
 Plan plan_for(const vae_decoder *d, int h, int w) {
@@ -250,14 +251,21 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
         const size_t b = groupnorm_ws_bytes((int)c, H * W);
         if (b > p.gn) p.gn = b;
     };
+    auto part = [&](const DConv &c, long long H, long long W) {
+        const size_t n = conv3x3_partial_floats(c.cout, c.cin, 1, (int)H, (int)W, 1);
+        if (n > p.part) p.part = n;
+    };
     long long H = h, W = w;
     act(d->latent_c, H, W);
     act(d->conv_in.cout, H, W);
+    part(d->conv_in, H, W);
     auto res = [&](const DRes &r) {
         gn(r.c1.cin, H, W);
         gn(r.c1.cout, H, W);
         act(r.c1.cin, H, W);
         act(r.c1.cout, H, W);
+        part(r.c1, H, W);
+        part(r.c2, H, W);
     };
     res(d->mid0);
     p.attn = attention_ws_bytes(d->attn.c, H * W);
@@ -268,6 +276,7 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
             H *= 2;
             W *= 2;
             act(u.up.cout, H, W);
+            part(u.up, H, W);
         }
     }
     gn(d->norm_out.c, H, W);
@@ -279,6 +288,7 @@ double conv_flops(const DConv &c, long long H, long long W) { return 2.0 * c.cou
 struct Runner {
     vae_decoder *d;
     hipStream_t s;
+    float *part = nullptr;
     int32_t rc = VAE_OK;
 
     ProfEntry *begin(const char *kernel, const std::string &layer, double flops, double bytes) {
@@ -320,11 +330,19 @@ struct Runner {
         a.denorm = denorm ? 1 : 0;
         a.dn_scale = d->scaling;
         a.dn_shift = d->shift;
+        a.part = part;
         const double in_elems = (double)c.cin * H * W / (up ? 4.0 : 1.0);
         const double bytes = 4.0 * (in_elems + (double)c.cout * H * W * (res ? 2.0 : 1.0));
-        ProfEntry *e = begin(conv3x3_kernel_name(a), layer, conv_flops(c, H, W), bytes);
+        const int ks = conv3x3_ksplit(c.cout, c.cin, 1, H, W, 1);
+        ProfEntry *e = begin(conv3x3_kernel_name(a), layer, conv_flops(c, H, W),
+                             ks > 1 ? 4.0 * (in_elems + (double)c.cout * H * W * ks) : bytes);
         if (rc != VAE_OK) return;
-        rc = launch_conv3x3(a, s);
+        rc = launch_conv3x3_main(a, s);
+        end(e);
+        if (rc != VAE_OK || ks == 1) return;
+        e = begin("splitk_reduce", layer, 0.0, 4.0 * (double)c.cout * H * W * (ks + 1 + (res ? 1 : 0)));
+        if (rc != VAE_OK) return;
+        rc = launch_conv3x3_reduce(a, s);
         end(e);
     }
     void conv1(const std::string &layer, const DConv &c, const float *x, int H, int W, float *y) {
@@ -449,7 +467,7 @@ int32_t vae_decoder_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, 
     if ((long long)ho * wo > (1LL << 30) || (long long)h * w > (1LL << 20))
         return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_workspace_bytes: latent %dx%d too large", h, w);
     const Plan p = plan_for(d, h, w);
-    *bytes = 5 * align256(p.act * 4) + align256(p.gn) + align256(p.attn);
+    *bytes = 5 * align256(p.act * 4) + align256(p.gn) + align256(p.attn) + align256(p.part * 4);
     return VAE_OK;
 }
 
@@ -471,8 +489,9 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
     b.S = reinterpret_cast<float *>(base + 4 * a);
     b.gn = base + 5 * a;
     b.attn = base + 5 * a + align256(pl.gn);
+    b.part = reinterpret_cast<float *>(base + 5 * a + align256(pl.gn) + align256(pl.attn));
 
-    Runner r{d, static_cast<hipStream_t>(stream)};
+    Runner r{d, static_cast<hipStream_t>(stream), b.part};
     int H = h, W = w;
     r.conv3("conv_in", d->conv_in, latent, H, W, false, nullptr, b.X, /*denorm=*/true);
     r.resnet(d->mid0, b, H, W);

@@ -39,14 +39,22 @@ struct ConvLaunch {
     int upsample;          // input is the nearest-x2 upsample of x
     int denorm;            // input is x / dn_scale + dn_shift (padding stays 0)
     float dn_scale, dn_shift;
+    float *part;           // split-K partial sums, conv3x3_partial_floats() floats (or nullptr if 0)
 };
 
 // Bytes of the packed weights for a conv with `cout` x `cin` x (kt x 3 x 3).
 size_t conv3x3_packed_floats(int cout, int cin, int kt);
 // Enqueue the repacking of raw weights [cout, cin, (kt,) 3, 3] into `dst`.
 int32_t pack_conv3x3(const float *w, int cout, int cin, int kt, float *dst, hipStream_t s);
-// Enqueue one implicit-GEMM conv.
+// Enqueue one implicit-GEMM conv: the conv kernel, then (for a K-split
+// shape) the reduction of its partial sums with bias and residual.
 int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s);
+int32_t launch_conv3x3_main(const ConvLaunch &a, hipStream_t s);
+int32_t launch_conv3x3_reduce(const ConvLaunch &a, hipStream_t s);
+// K-split factor launch_conv3x3 uses for a conv of this shape (1 = none), and
+// the partial-sum workspace it then needs (floats, 0 when not split).
+int conv3x3_ksplit(int cout, int cin, int kt, int H, int W, int T);
+size_t conv3x3_partial_floats(int cout, int cin, int kt, int H, int W, int T);
 // Name of the kernel instantiation launch_conv3x3 picks for `a`.
 const char *conv3x3_kernel_name(const ConvLaunch &a);
 

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 1
+#define VAE_ABI_VERSION 2
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -111,9 +111,12 @@ int32_t vae_abi_version(void);
 
 /* ---------------------------------------------------------------- layers */
 
-/* Workspace (device bytes) needed by vae_conv2d / vae_conv_in for `conv`:
- * the weights repacked for the kernel.  0 for kernel-1 convs. */
-int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, size_t *bytes);
+/* Workspace (device bytes) needed by vae_conv2d / vae_conv_in for `conv` on an
+ * input of h x w (upsampled to 2h x 2w when upsample2x): the weights repacked
+ * for the kernel and, for shapes too small to fill the GPU, the partial sums
+ * of a K-split.  0 for kernel-1 convs. */
+int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, int32_t h, int32_t w, int32_t upsample2x,
+                                   size_t *bytes);
 
 /* 2-D convolution (Conv2d / VaeConvRef): y = conv(u) + bias [+ residual].
  *   x        [cin, h, w]
@@ -122,7 +125,7 @@ int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, size_t *bytes);
  *   y        [cout, H, W] with (H, W) = (h, w), or (2h, 2w) when upsample2x
  *   residual NULL or [cout, H, W], added after the bias (the resnet skip)
  *   conv     kernel 1 or 3; conv->in_channels must equal cin
- *   ws       >= vae_conv2d_workspace_bytes(conv) device bytes (may be NULL if 0)
+ *   ws       >= vae_conv2d_workspace_bytes(conv, h, w, upsample2x) device bytes (may be NULL if 0)
  * A convolution with out_channels <= 4 (the decoder's conv_out) runs on a
  * direct kernel; other 3x3 convolutions run as implicit GEMM on FP32 MFMA.
  * upsample2x requires kernel 3.  y may not alias x; it may alias residual. */
@@ -164,8 +167,10 @@ int32_t vae_attention_workspace_bytes(int32_t c, int32_t h, int32_t w, size_t *b
 int32_t vae_attention(const float *x, int32_t c, int32_t h, int32_t w, const vae_attn *attn,
                       float *y, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace for vae_conv3d_causal: the repacked 3x3x3 weights. */
-int32_t vae_conv3d_causal_workspace_bytes(const vae_conv *conv, size_t *bytes);
+/* Workspace for vae_conv3d_causal on [cin, t, h, w]: the repacked 3x3x3
+ * weights (and split-K partial sums for small shapes). */
+int32_t vae_conv3d_causal_workspace_bytes(const vae_conv *conv, int32_t t, int32_t h, int32_t w,
+                                          size_t *bytes);
 
 /* Causal 3-D convolution (VAE decode -> GPU handoff, "The CPU VAE code" and
  * "GPU plan": LTX's 3-D causal conv with causal padding on time):

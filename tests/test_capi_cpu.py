@@ -50,8 +50,16 @@ def err(lib):
 def test_conv2d_validation(lib):
     c = conv(64, 32, 3)
     ws = c_size_t()
-    assert lib.vae_conv2d_workspace_bytes(byref(c), byref(ws)) == VAE_OK
-    assert ws.value == 1 * 4 * 9 * 8 * 128 * 4        # 1 output block x 4 channel chunks x 72 x 128 floats
+    assert lib.vae_conv2d_workspace_bytes(byref(c), 8, 8, 0, byref(ws)) == VAE_OK
+    assert ws.value == 1 * 8 * 36 * 128 * 4           # 1 output block x 8 chunks of 4 channels x 36 x 128 floats
+    # a small shape: the 32x32 conv with 512 channels is K-split, so partial sums are added
+    big = conv(512, 512, 3)
+    w1, w2 = c_size_t(), c_size_t()
+    assert lib.vae_conv2d_workspace_bytes(byref(big), 32, 32, 0, byref(w1)) == VAE_OK
+    assert lib.vae_conv2d_workspace_bytes(byref(big), 256, 256, 0, byref(w2)) == VAE_OK
+    packed = 4 * 128 * 36 * 128 * 4
+    assert w2.value == packed and w1.value == packed + 16 * 512 * 32 * 32 * 4
+    assert lib.vae_conv2d_workspace_bytes(byref(big), 0, 32, 0, byref(w1)) == VAE_ERR_INVALID_ARG
     args = lambda **k: dict(dict(x=FAKE, cin=32, h=8, w=8, conv=byref(c), up=0, res=NULL, y=FAKE + 4096,
                                  ws=FAKE + 8192, nb=ws.value, s=NULL), **k)
 
@@ -77,12 +85,16 @@ def test_conv2d_validation(lib):
 def test_conv_in_and_3d_validation(lib):
     c = conv(512, 16, 3)
     nb = c_size_t()
-    assert lib.vae_conv2d_workspace_bytes(byref(c), byref(nb)) == VAE_OK
+    assert lib.vae_conv2d_workspace_bytes(byref(c), 8, 8, 0, byref(nb)) == VAE_OK
     assert lib.vae_conv_in(FAKE, 16, 8, 8, byref(c), 0.0, 0.1, FAKE + 64, FAKE + 128, nb.value, NULL) == VAE_ERR_INVALID_ARG
     assert lib.vae_conv_in(FAKE, 16, 8, 8, byref(conv(512, 16, 1)), 0.36, 0.1, FAKE + 64, FAKE, 0, NULL) == VAE_ERR_UNSUPPORTED
     c3 = conv(128, 128, 3)
-    assert lib.vae_conv3d_causal_workspace_bytes(byref(c3), byref(nb)) == VAE_OK
-    assert nb.value == 3 * 16 * 72 * 128 * 4
+    assert lib.vae_conv3d_causal_workspace_bytes(byref(c3), 3, 8, 8, byref(nb)) == VAE_OK
+    packed = 3 * 32 * 36 * 128 * 4
+    assert nb.value >= packed and (nb.value - packed) % (128 * 3 * 64 * 4) == 0
+    full = c_size_t()
+    assert lib.vae_conv3d_causal_workspace_bytes(byref(c3), 17, 256, 256, byref(full)) == VAE_OK
+    assert full.value == packed                          # big enough to fill the GPU: no split
     assert lib.vae_conv3d_causal(FAKE, 128, 0, 8, 8, byref(c3), FAKE + 64, FAKE, nb.value, NULL) == VAE_ERR_INVALID_ARG
     assert lib.vae_conv3d_causal(FAKE, 128, 3, 8, 8, byref(c3), FAKE + 64, FAKE, nb.value - 4, NULL) == VAE_ERR_WORKSPACE
     assert lib.vae_conv3d_causal(FAKE, 64, 3, 8, 8, byref(c3), FAKE + 64, FAKE, nb.value, NULL) == VAE_ERR_INVALID_ARG

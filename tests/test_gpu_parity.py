@@ -70,6 +70,7 @@ CONV_CASES = [
     (512, 512, 8, 8),       # long K (64 chunks)
     (128, 128, 64, 64),     # several full tiles
     (256, 128, 40, 33),     # the 256->128 shape, ragged
+    (99, 96, 9, 11),        # K-split into 8/8/9 chunks, last channel chunk partial
 ]
 
 
@@ -90,7 +91,7 @@ def test_conv3x3_upsample_folded(api, cin, cout, h, w):
     assert rel_err(host(y), ref) <= LAYER_TOL
 
 
-@pytest.mark.parametrize("cin,cout,h,w", [(64, 64, 23, 17), (128, 128, 32, 32)])
+@pytest.mark.parametrize("cin,cout,h,w", [(64, 64, 23, 17), (128, 128, 32, 32), (99, 96, 9, 11)])
 def test_conv3x3_residual_epilogue(api, cin, cout, h, w):
     x = vaegen.activation(3, "xr", (cin, h, w))
     r = vaegen.activation(3, "rr", (cout, h, w))
