@@ -80,6 +80,7 @@ SIGNATURES = {
     "vae_decoder_output_shape": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32),
                                            POINTER(c_int32)]),
     "vae_decoder_destroy": (None, [c_void_p]),
+    "vae_decoder_set_groupnorm_fusion": (c_int32, [c_void_p, c_int32]),
     "vae_decoder_set_profiling": (c_int32, [c_void_p, c_int32]),
     "vae_decoder_profile": (c_int32, [c_void_p, POINTER(VaeProfRecord), c_int32, POINTER(c_int32)]),
 }

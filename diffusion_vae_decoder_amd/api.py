@@ -266,6 +266,10 @@ class Decoder:
                                    self._ws.numel(), _stream()))
         return rgb
 
+    def set_groupnorm_fusion(self, on: bool) -> None:
+        """Apply GroupNorm + SiLU while each conv loads its input (off by default)."""
+        check(self._lib.vae_decoder_set_groupnorm_fusion(self._h, int(bool(on))))
+
     def set_profiling(self, on: bool) -> None:
         check(self._lib.vae_decoder_set_profiling(self._h, int(bool(on))))
 

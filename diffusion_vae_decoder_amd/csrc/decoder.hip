@@ -220,6 +220,7 @@ struct vae_decoder {
     DConv conv_out;
     float scaling = 1.f, shift = 0.f;
     int latent_c = 0;
+    bool gn_fused = false;   // GroupNorm + SiLU applied while the consuming conv loads its input
     // profiling
     bool profiling = false;
     std::vector<ProfEntry> prof;
@@ -231,6 +232,7 @@ namespace {
 struct Buffers {
     float *X, *Y, *T, *U, *S;
     float *part;   // split-K partial sums of the small convs
+    float *coef;   // GroupNorm coefficients (mean, rstd*gamma, beta, -) per channel, for the next conv
     void *gn;
     void *attn;
 };
@@ -238,7 +240,7 @@ struct Buffers {
 // The chain's spatial plan for a latent of (h, w): largest activation (floats),
 // largest GroupNorm workspace, attention workspace.
 struct Plan {
-    size_t act = 0, gn = 0, attn = 0, part = 0;
+    size_t act = 0, gn = 0, attn = 0, part = 0, coef = 0;
 };
 
 Plan plan_for(const vae_decoder *d, int h, int w) {
@@ -250,6 +252,7 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
     auto gn = [&](long long c, long long H, long long W) {
         const size_t b = groupnorm_ws_bytes((int)c, H * W);
         if (b > p.gn) p.gn = b;
+        if ((size_t)c * 16 > p.coef) p.coef = (size_t)c * 16;
     };
     auto part = [&](const DConv &c, long long H, long long W) {
         const size_t n = conv3x3_partial_floats(c.cout, c.cin, 1, (int)H, (int)W, 1);
@@ -311,8 +314,10 @@ struct Runner {
         if (e && rc == VAE_OK) rc = hip_status(hipEventRecord(e->stop, s), "hipEventRecord");
     }
 
+    float *coef = nullptr;
+
     void conv3(const std::string &layer, const DConv &c, const float *x, int H, int W, bool up,
-               const float *res, float *y, bool denorm = false) {
+               const float *res, float *y, bool denorm = false, bool gn = false) {
         if (rc != VAE_OK) return;
         ConvLaunch a{};
         a.x = x;
@@ -331,6 +336,7 @@ struct Runner {
         a.dn_scale = d->scaling;
         a.dn_shift = d->shift;
         a.part = part;
+        a.gn_coef = gn ? coef : nullptr;
         const double in_elems = (double)c.cin * H * W / (up ? 4.0 : 1.0);
         const double bytes = 4.0 * (in_elems + (double)c.cout * H * W * (res ? 2.0 : 1.0));
         const int ks = conv3x3_ksplit(c.cout, c.cin, 1, H, W, 1);
@@ -364,6 +370,15 @@ struct Runner {
         rc = launch_gemm(g, s);
         end(e);
     }
+    // GroupNorm statistics of x -> per-channel coefficients in `coef`; the
+    // next conv applies the normalisation and SiLU while loading x.
+    void gnc(const std::string &layer, const DNorm &n, const float *x, long long spatial, void *ws) {
+        if (rc != VAE_OK) return;
+        ProfEntry *e = begin("groupnorm_stats", layer, 0.0, 4.0 * n.c * (double)spatial);
+        if (rc != VAE_OK) return;
+        rc = launch_groupnorm_coef(x, n.c, spatial, n.g, n.b, ws, coef, s);
+        end(e);
+    }
     void gn(const std::string &layer, const DNorm &n, const float *x, long long spatial, float *y, void *ws) {
         if (rc != VAE_OK) return;
         ProfEntry *e = begin("groupnorm_silu", layer, 0.0, 8.0 * n.c * (double)spatial);
@@ -374,15 +389,27 @@ struct Runner {
     // X -> Y; uses T, U (and S for a 1x1 skip).
     void resnet(const DRes &r, Buffers &b, int H, int W) {
         const long long sp = (long long)H * W;
-        gn(r.name + ".norm1", r.n1, b.X, sp, b.T, b.gn);
-        conv3(r.name + ".conv1", r.c1, b.T, H, W, false, nullptr, b.U);
-        gn(r.name + ".norm2", r.n2, b.U, sp, b.U, b.gn);
+        if (!d->gn_fused) {
+            gn(r.name + ".norm1", r.n1, b.X, sp, b.T, b.gn);
+            conv3(r.name + ".conv1", r.c1, b.T, H, W, false, nullptr, b.U);
+            gn(r.name + ".norm2", r.n2, b.U, sp, b.U, b.gn);
+            const float *skip = b.X;
+            if (r.sc.present) {
+                conv1(r.name + ".conv_shortcut", r.sc, b.X, H, W, b.S);
+                skip = b.S;
+            }
+            conv3(r.name + ".conv2", r.c2, b.U, H, W, false, skip, b.Y);
+            return;
+        }
+        gnc(r.name + ".norm1", r.n1, b.X, sp, b.gn);
+        conv3(r.name + ".conv1", r.c1, b.X, H, W, false, nullptr, b.U, false, true);
+        gnc(r.name + ".norm2", r.n2, b.U, sp, b.gn);
         const float *skip = b.X;
         if (r.sc.present) {
             conv1(r.name + ".conv_shortcut", r.sc, b.X, H, W, b.S);
             skip = b.S;
         }
-        conv3(r.name + ".conv2", r.c2, b.U, H, W, false, skip, b.Y);
+        conv3(r.name + ".conv2", r.c2, b.U, H, W, false, skip, b.Y, false, true);
     }
 };
 
@@ -467,7 +494,8 @@ int32_t vae_decoder_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, 
     if ((long long)ho * wo > (1LL << 30) || (long long)h * w > (1LL << 20))
         return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_workspace_bytes: latent %dx%d too large", h, w);
     const Plan p = plan_for(d, h, w);
-    *bytes = 5 * align256(p.act * 4) + align256(p.gn) + align256(p.attn) + align256(p.part * 4);
+    *bytes = 5 * align256(p.act * 4) + align256(p.gn) + align256(p.attn) + align256(p.part * 4) +
+             align256(p.coef);
     return VAE_OK;
 }
 
@@ -487,11 +515,17 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
     b.T = reinterpret_cast<float *>(base + 2 * a);
     b.U = reinterpret_cast<float *>(base + 3 * a);
     b.S = reinterpret_cast<float *>(base + 4 * a);
-    b.gn = base + 5 * a;
-    b.attn = base + 5 * a + align256(pl.gn);
-    b.part = reinterpret_cast<float *>(base + 5 * a + align256(pl.gn) + align256(pl.attn));
+    char *q = base + 5 * a;
+    b.gn = q;
+    q += align256(pl.gn);
+    b.attn = q;
+    q += align256(pl.attn);
+    b.part = reinterpret_cast<float *>(q);
+    q += align256(pl.part * 4);
+    b.coef = reinterpret_cast<float *>(q);
 
     Runner r{d, static_cast<hipStream_t>(stream), b.part};
+    r.coef = b.coef;
     int H = h, W = w;
     r.conv3("conv_in", d->conv_in, latent, H, W, false, nullptr, b.X, /*denorm=*/true);
     r.resnet(d->mid0, b, H, W);
@@ -522,20 +556,22 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
             std::swap(b.X, b.Y);
         }
     }
-    r.gn("conv_norm_out", d->norm_out, b.X, (long long)H * W, b.T, b.gn);
+    // norm_out + SiLU, conv_out: the normalised input is either materialised
+    // in T or applied while conv_out loads X
+    const bool fused = d->gn_fused;
+    const float *cin_x = fused ? b.X : b.T;
+    if (fused) r.gnc("conv_norm_out", d->norm_out, b.X, (long long)H * W, b.gn);
+    else r.gn("conv_norm_out", d->norm_out, b.X, (long long)H * W, b.T, b.gn);
     if (r.rc == VAE_OK) {
         const DConv &c = d->conv_out;
-        ProfEntry *e = r.begin(c.cout <= 4 ? "conv3x3_skinny" : "conv3x3_mfma", "conv_out", conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
-        if (r.rc == VAE_OK) {
-            if (c.cout <= 4) {
-                r.rc = launch_conv3x3_skinny(b.T, c.w, c.b, rgb, c.cin, c.cout, H, W, r.s);
-            } else {
-                ConvLaunch a{};
-                a.x = b.T; a.wpk = c.w; a.bias = c.b; a.y = rgb; a.cin = c.cin; a.cout = c.cout;
-                a.H = H; a.W = W; a.T = 1; a.kt = 1;
-                r.rc = launch_conv3x3(a, r.s);
+        if (c.cout <= 4) {
+            ProfEntry *e = r.begin("conv3x3_skinny", "conv_out", conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
+            if (r.rc == VAE_OK) {
+                r.rc = launch_conv3x3_skinny(cin_x, c.w, c.b, rgb, c.cin, c.cout, H, W, r.s, fused ? b.coef : nullptr);
+                r.end(e);
             }
-            r.end(e);
+        } else {
+            r.conv3("conv_out", c, cin_x, H, W, false, nullptr, rgb, false, fused);
         }
     }
     return r.rc;
@@ -548,6 +584,22 @@ void vae_decoder_destroy(vae_decoder *d) {
         if (e.stop) (void)hipEventDestroy(e.stop);
     }
     delete d;
+}
+
+int32_t vae_decoder_set_groupnorm_fusion(vae_decoder *d, int32_t on) {
+    if (!d) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_set_groupnorm_fusion: NULL decoder");
+    if (on) {
+        // the conv's coefficient table holds 512 input channels
+        auto ok = [](const DConv &c) { return c.cin <= 512; };
+        bool all = ok(d->conv_out);
+        for (const DRes *r : {&d->mid0, &d->mid1}) all = all && ok(r->c1) && ok(r->c2);
+        for (const DUp &u : d->ups)
+            for (const DRes &r : u.res) all = all && ok(r.c1) && ok(r.c2);
+        if (!all)
+            return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_set_groupnorm_fusion: a conv has more than 512 inputs");
+    }
+    d->gn_fused = on != 0;
+    return VAE_OK;
 }
 
 int32_t vae_decoder_set_profiling(vae_decoder *d, int32_t on) {

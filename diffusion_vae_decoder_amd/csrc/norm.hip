@@ -157,6 +157,39 @@ __global__ __launch_bounds__(kThreads) void gn_apply(const float *x, long long s
     }
 }
 
+// Per-channel coefficients of GroupNorm for a consumer that normalises on
+// load: coef[c] = (mean_g, rstd_g * gamma[c], beta[c], 0).  One workgroup per
+// group merges the group's partials in the same fixed order as gn_apply.
+__global__ __launch_bounds__(kThreads) void gn_coef(long long gsize, int cpg, int parts,
+                                                    const double *__restrict__ part,
+                                                    const double *__restrict__ shifts,
+                                                    const float *__restrict__ gamma,
+                                                    const float *__restrict__ beta, float *__restrict__ coef) {
+    __shared__ double scratch[8];
+    __shared__ double stat[2];
+    const int g = blockIdx.x;
+    double s1 = 0.0, s2 = 0.0;
+    if (threadIdx.x < parts) {
+        s1 = part[2 * ((long long)g * parts + threadIdx.x)];
+        s2 = part[2 * ((long long)g * parts + threadIdx.x) + 1];
+    }
+    block_sum2(s1, s2, scratch);
+    if (threadIdx.x == 0) {
+        const double n = (double)gsize;
+        const double md = s1 / n;
+        double var = s2 / n - md * md;
+        if (var < 0.0) var = 0.0;
+        stat[0] = shifts[g] + md;
+        stat[1] = 1.0 / sqrt(var + 1e-6);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < cpg; j += kThreads) {
+        const int c = g * cpg + j;
+        floatx4 v = {(float)stat[0], (float)(stat[1] * (double)gamma[c]), beta[c], 0.f};
+        reinterpret_cast<floatx4 *>(coef)[c] = v;
+    }
+}
+
 template <bool VEC, bool SILU>
 void apply2(bool res, dim3 grid, hipStream_t s, const float *x, long long spatial, int cpg,
             int parts, const double *part, const double *shifts, const float *gamma,
@@ -291,6 +324,23 @@ int32_t launch_groupnorm(const float *x, int c, long long spatial, const float *
         else apply2<false, false>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y);
     }
     return check_launch("gn_apply");
+}
+
+int32_t launch_groupnorm_coef(const float *x, int c, long long spatial, const float *gamma, const float *beta,
+                              void *ws, float *coef, hipStream_t s) {
+    const int cpg = c / kGroups;
+    const long long gsize = (long long)cpg * spatial;
+    const int parts = parts_for(gsize);
+    double *part = reinterpret_cast<double *>(ws);
+    double *shifts = part + 2 * kGroups * parts;
+    if (gsize % 4 == 0 && aligned16(x))
+        hipLaunchKernelGGL(gn_stats<true>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize, parts, part, shifts);
+    else
+        hipLaunchKernelGGL(gn_stats<false>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize, parts, part, shifts);
+    int32_t rc = check_launch("gn_stats");
+    if (rc != VAE_OK) return rc;
+    hipLaunchKernelGGL(gn_coef, dim3(kGroups), dim3(kThreads), 0, s, gsize, cpg, parts, part, shifts, gamma, beta, coef);
+    return check_launch("gn_coef");
 }
 
 int32_t launch_upsample2x(const float *x, int c, int h, int w, float *y, hipStream_t s) {

@@ -40,6 +40,8 @@ struct ConvLaunch {
     int denorm;            // input is x / dn_scale + dn_shift (padding stays 0)
     float dn_scale, dn_shift;
     float *part;           // split-K partial sums, conv3x3_partial_floats() floats (or nullptr if 0)
+    const float *gn_coef;  // if set: the input is silu((x - c[0]) * c[1] + c[2]) with c = gn_coef[4*channel..]
+                           // (GroupNorm + SiLU applied on load; padding stays 0)
 };
 
 // Bytes of the packed weights for a conv with `cout` x `cin` x (kt x 3 x 3).
@@ -58,9 +60,10 @@ size_t conv3x3_partial_floats(int cout, int cin, int kt, int H, int W, int T);
 // Name of the kernel instantiation launch_conv3x3 picks for `a`.
 const char *conv3x3_kernel_name(const ConvLaunch &a);
 
-// Direct conv for out_channels <= 4 (conv_out).
+// Direct conv for out_channels <= 4 (conv_out); gn_coef as in ConvLaunch (may be nullptr).
 int32_t launch_conv3x3_skinny(const float *x, const float *w, const float *bias, float *y,
-                              int cin, int cout, int H, int W, hipStream_t s);
+                              int cin, int cout, int H, int W, hipStream_t s,
+                              const float *gn_coef = nullptr);
 
 // ------------------------------------------------------------------ GEMM
 // C[m, n] = alpha * sum_k A(m, k) B(k, n) + bias[m] (+ R[m, n]).
@@ -84,6 +87,10 @@ size_t groupnorm_ws_bytes(int c, long long spatial);
 int32_t launch_groupnorm(const float *x, int c, long long spatial, const float *gamma,
                          const float *beta, int silu, const float *res, float *y, void *ws,
                          hipStream_t s);
+// Statistics only: writes coef[4*c + {0,1,2}] = (mean of c's group, rstd * gamma[c], beta[c])
+// for a consumer that normalises while loading.  ws as for launch_groupnorm.
+int32_t launch_groupnorm_coef(const float *x, int c, long long spatial, const float *gamma, const float *beta,
+                              void *ws, float *coef, hipStream_t s);
 
 // ------------------------------------------------------------------ misc
 int32_t launch_upsample2x(const float *x, int c, int h, int w, float *y, hipStream_t s);

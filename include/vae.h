@@ -213,6 +213,14 @@ int32_t vae_decoder_output_shape(const vae_decoder *d, int32_t h, int32_t w, int
 
 void vae_decoder_destroy(vae_decoder *d);
 
+/* on != 0: apply each conv input's GroupNorm + SiLU while the conv loads it,
+ * from per-channel coefficients computed by a statistics-only pass, instead
+ * of a separate normalisation pass that writes the normalised tensor (the
+ * default).  Same results up to rounding.  On MI355X the separate pass is
+ * faster, so the default is off.  VAE_ERR_UNSUPPORTED if a normalised conv
+ * has more than 512 input channels. */
+int32_t vae_decoder_set_groupnorm_fusion(vae_decoder *d, int32_t on);
+
 /* ------------------------------------------------------------- profiling */
 
 /* One kernel launch (or one composite layer: GroupNorm = stats + apply,

@@ -273,6 +273,21 @@ def test_decode_full_size_against_stored_oracle(decoder, name, h):
     assert abs(math.sqrt((rgb * rgb).sum()) / float(g["l2"]) - 1.0) < 1e-4
 
 
+@pytest.mark.parametrize("h,w", [(8, 8), (5, 3), (32, 32)])
+def test_decode_with_groupnorm_on_load(decoder, params, h, w):
+    # the optional fused path: GroupNorm + SiLU applied while each conv loads
+    z = vaegen.latent(6, h, w)
+    decoder.set_groupnorm_fusion(True)
+    try:
+        rgb = decoder.decode(dev(z), out=nan_like((3, 8 * h, 8 * w)))
+        got = host(rgb)
+    finally:
+        decoder.set_groupnorm_fusion(False)
+    ref = oracle.decode(z, params, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    cos, mx = rgb_metrics(got, ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
 def test_decode_is_deterministic(decoder):
     z = dev(vaegen.latent(1, 16, 16))
     a = decoder.decode(z).cpu()
