@@ -16,7 +16,7 @@ VAE_ERR_INVALID_ARG = -1
 VAE_ERR_UNSUPPORTED = -2
 VAE_ERR_WORKSPACE = -3
 VAE_ERR_HIP = -4
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class VaeConv(ctypes.Structure):
@@ -65,6 +65,11 @@ SIGNATURES = {
     "vae_groupnorm_workspace_bytes": (c_int32, [c_int32, c_int64, POINTER(c_size_t)]),
     "vae_groupnorm_silu": (c_int32, [c_void_p, c_int32, c_int64, POINTER(VaeNorm), c_int32, c_void_p,
                                      c_void_p, c_void_p, c_size_t, c_void_p]),
+    "vae_conv2d_groupnorm_workspace_bytes": (c_int32, [POINTER(VaeConv), c_int32, c_int32, c_int32,
+                                                       POINTER(c_size_t)]),
+    "vae_conv2d_groupnorm_silu": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(VaeConv), c_int32,
+                                            c_void_p, POINTER(VaeNorm), c_int32, c_void_p, c_void_p, c_void_p,
+                                            c_size_t, c_void_p]),
     "vae_upsample_nearest2x": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "vae_attention_workspace_bytes": (c_int32, [c_int32, c_int32, c_int32, POINTER(c_size_t)]),
     "vae_attention": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(VaeAttn), c_void_p,

@@ -134,6 +134,32 @@ def groupnorm_silu(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, sil
     return y
 
 
+def conv2d_groupnorm_silu(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor, gamma: torch.Tensor,
+                          beta: torch.Tensor, silu: bool = True, upsample2x: bool = False,
+                          residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                          out_norm: Optional[torch.Tensor] = None):
+    """y = conv2d(x) (+ residual) as :func:`conv2d` (3x3), then
+    z = SiLU(GroupNorm(y)) with the group statistics taken in the conv's
+    epilogue.  Returns (y, z); ``out_norm`` may be ``out`` (z overwrites y)."""
+    lib = _lib_()
+    _dev(x, "x")
+    cin, h, w = x.shape
+    conv = _conv(weight, bias)
+    norm = _norm(gamma, beta)
+    H, W = (2 * h, 2 * w) if upsample2x else (h, w)
+    if residual is not None:
+        _dev(residual, "residual")
+    y = _out(out, (weight.shape[0], H, W), x.device)
+    z = _out(out_norm, (weight.shape[0], H, W), x.device)
+    nb = c_size_t()
+    check(lib.vae_conv2d_groupnorm_workspace_bytes(byref(conv), h, w, int(bool(upsample2x)), byref(nb)))
+    ws = _ws(nb.value, x.device)
+    check(lib.vae_conv2d_groupnorm_silu(x.data_ptr(), cin, h, w, byref(conv), int(bool(upsample2x)),
+                                        _ptr(residual), byref(norm), int(bool(silu)), y.data_ptr(),
+                                        z.data_ptr(), _ptr(ws), nb.value, _stream()))
+    return y, z
+
+
 def upsample_nearest2x(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     lib = _lib_()
     _dev(x, "x")

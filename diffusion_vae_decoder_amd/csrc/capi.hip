@@ -192,6 +192,73 @@ int32_t vae_groupnorm_silu(const float *x, int32_t c, int64_t spatial, const vae
                             static_cast<hipStream_t>(stream));
 }
 
+namespace {
+// Workspace of vae_conv2d_groupnorm_silu: the conv's workspace, then the
+// GroupNorm records of its output, then the GroupNorm partial sums.
+size_t conv_gn_records_bytes(const vae_conv *c, int cin, int H, int W) {
+    ConvLaunch a{};
+    a.cin = cin; a.cout = c->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
+    return (size_t)32 * conv3x3_gn_records(a) * sizeof(floatx4);
+}
+size_t conv_gn_ws(const vae_conv *c, int H, int W) {
+    return align256(conv_ws(c, 1, 1, H, W)) + align256(conv_gn_records_bytes(c, c->in_channels, H, W)) +
+           groupnorm_ws_bytes(c->out_channels, (long long)H * W);
+}
+}  // namespace
+
+int32_t vae_conv2d_groupnorm_workspace_bytes(const vae_conv *conv, int32_t h, int32_t w, int32_t upsample2x,
+                                             size_t *bytes) {
+    int32_t rc = check_conv("vae_conv2d_groupnorm_workspace_bytes", conv, 3);
+    if (rc) return rc;
+    if (!bytes) return bad("vae_conv2d_groupnorm_workspace_bytes: bytes is NULL");
+    const long long H = upsample2x ? 2LL * h : h, W = upsample2x ? 2LL * w : w;
+    if ((rc = check_plane("vae_conv2d_groupnorm_workspace_bytes", conv->out_channels, H, W))) return rc;
+    if (conv->out_channels % 32)
+        return unsupported("vae_conv2d_groupnorm_workspace_bytes: out_channels %d not divisible by 32",
+                           conv->out_channels);
+    *bytes = conv_gn_ws(conv, (int)H, (int)W);
+    return VAE_OK;
+}
+
+int32_t vae_conv2d_groupnorm_silu(const float *x, int32_t cin, int32_t h, int32_t w, const vae_conv *conv,
+                                  int32_t upsample2x, const float *residual, const vae_norm *norm,
+                                  int32_t apply_silu, float *y, float *z, void *ws, size_t ws_bytes,
+                                  void *stream) {
+    int32_t rc = check_conv("vae_conv2d_groupnorm_silu", conv, 3);
+    if (rc) return rc;
+    if (!x || !y || !z) return bad("vae_conv2d_groupnorm_silu: x, y or z is NULL");
+    if (!norm || !norm->gamma || !norm->beta) return bad("vae_conv2d_groupnorm_silu: norm missing");
+    const int H = upsample2x ? 2 * h : h, W = upsample2x ? 2 * w : w;
+    if ((rc = check_plane("vae_conv2d_groupnorm_silu", cin, h, w))) return rc;
+    if ((rc = check_plane("vae_conv2d_groupnorm_silu", conv->out_channels, H, W))) return rc;
+    if (conv->in_channels != cin)
+        return bad("vae_conv2d_groupnorm_silu: conv expects %d input channels, got %d", conv->in_channels, cin);
+    if (norm->channels != conv->out_channels)
+        return bad("vae_conv2d_groupnorm_silu: norm has %d channels, conv output %d", norm->channels,
+                   conv->out_channels);
+    if (conv->out_channels % 32)
+        return unsupported("vae_conv2d_groupnorm_silu: out_channels %d not divisible by 32", conv->out_channels);
+    if (x == y) return bad("vae_conv2d_groupnorm_silu: y may not alias x");
+    const size_t need = conv_gn_ws(conv, H, W);
+    if (!ws || ws_bytes < need)
+        return set_error("vae_conv2d_groupnorm_silu: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(ws);
+    if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 1, reinterpret_cast<float *>(base), s))) return rc;
+    ConvLaunch a{};
+    a.x = x; a.wpk = reinterpret_cast<const float *>(base); a.bias = conv->bias; a.res = residual; a.y = y;
+    a.part = conv_ws_part(conv, 1, ws);
+    a.cin = cin; a.cout = conv->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
+    a.upsample = upsample2x ? 1 : 0;
+    char *recs = base + align256(conv_ws(conv, 1, 1, H, W));
+    void *gws = recs + align256(conv_gn_records_bytes(conv, cin, H, W));
+    const int nrec = conv3x3_gn_records(a);
+    a.gn_rec = nrec > 0 ? reinterpret_cast<floatx4 *>(recs) : nullptr;
+    if ((rc = launch_conv3x3(a, s))) return rc;
+    return launch_groupnorm(y, conv->out_channels, (long long)H * W, norm->gamma, norm->beta, apply_silu ? 1 : 0,
+                            nullptr, z, gws, s, a.gn_rec, nrec);
+}
+
 int32_t vae_upsample_nearest2x(const float *x, int32_t c, int32_t h, int32_t w, float *y, void *stream) {
     if (!x || !y) return bad("vae_upsample_nearest2x: NULL pointer");
     int32_t rc = check_plane("vae_upsample_nearest2x", c, 2LL * h, 2LL * w);

@@ -80,7 +80,8 @@ struct Params {
     const float *gn_coef;   // MODE_GNSILU: (mean, scale, beta, -) per input channel
     float *y;
     float *part;            // split-K partial sums [ksplit][cout][T][H][W] (ksplit > 1)
-    int cin, cout, H, W, Win, kt, n_cb, tiles_x, ksplit;
+    floatx4 *gn_rec;        // if set: GroupNorm records of y, [32 groups][gn_nrec] (count, mean, M2, 0)
+    int cin, cout, H, W, Win, kt, n_cb, tiles_x, ksplit, gn_cpg, gn_nrec;
     long long in_cstride, in_fstride, out_cstride, out_fstride, part_stride;
     float dn_scale, dn_shift;
 };
@@ -161,6 +162,16 @@ __device__ __attribute__((always_inline)) inline void stage_store(
 #pragma unroll
     for (int i = 0; i < Geom<TC>::HALO_PER_T; ++i)
         if ((i + 1) * kThreads <= Geom<TC>::HALO || h_lds[i] >= 0) lx[h_lds[i]] = xreg[i];
+}
+
+// Sum each value over the 32 lanes of its lane half (butterfly within 32).
+__device__ __attribute__((always_inline)) inline void half_wave_sum(float (&q)[2][4]) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) q[i][rq] += __shfl_xor(q[i][rq], o, 64);
 }
 
 template <int TC, int MODE, bool RES, bool SPLIT>
@@ -282,14 +293,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // Epilogue: D[i][j] of a 32x32 MFMA tile sits in lane j + 32*((i/4)%2),
     // register (i%4) + 4*(i/8).
     const long long fo = (long long)frame * p.out_fstride;
+    bool pv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int n = wn * 64 + j * 32 + l32;
+        pv[j] = y0 + n / TC < p.H && x0 + (n - (n / TC) * TC) < p.W;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+            if (!pv[j]) continue;
             const int n = wn * 64 + j * 32 + l32;
-            const int yy = y0 + n / TC, xx = x0 + (n - (n / TC) * TC);
-            if (yy >= p.H || xx >= p.W) continue;
-            const long long sp = fo + (long long)yy * p.W + xx;
+            const long long sp = fo + (long long)(y0 + n / TC) * p.W + x0 + (n - (n / TC) * TC);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -302,9 +318,80 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                         float v = acc[i][j][r] + p.bias[o];
                         if (RES) v += p.res[off];
                         p.y[off] = v;
+                        acc[i][j][r] = v;
                     }
                 }
             }
+        }
+    }
+    if (!SPLIT && p.gn_rec) {
+        // GroupNorm statistics of this tile's outputs for the layer that
+        // normalises them next: per group (count, mean, sum of squared
+        // deviations from that mean), two passes over the registers.  The
+        // host enables this only for cout % 128 == 0 and channels per group a
+        // multiple of 4, so a group is a whole number of the 4-channel row
+        // quads the MFMA layout gives each lane half.  The staging buffers
+        // are free after the main loop's last barrier.
+        float *red = lds_x[0];          // [2 column waves][32 quads]
+        float *gmean = lds_x[0] + 64;   // [32 quads]: mean of the quad's group
+        const int qpg = p.gn_cpg >> 2;
+        const int npx = (p.H - y0 < G::TR ? p.H - y0 : G::TR) * (p.W - x0 < TC ? p.W - x0 : TC);
+        const float cnt = (float)(npx * p.gn_cpg);
+        float q[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                float t = 0.f;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    if (pv[j])
+                        t += (acc[i][j][4 * rq] + acc[i][j][4 * rq + 1]) + (acc[i][j][4 * rq + 2] + acc[i][j][4 * rq + 3]);
+                q[i][rq] = t;
+            }
+        half_wave_sum(q);
+        if (l32 == 0)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) red[wn * 32 + wm * 16 + i * 8 + 2 * rq + half] = q[i][rq];
+        __syncthreads();
+        if (tid < 32) {
+            const int g0 = (tid / qpg) * qpg;
+            float t = 0.f;
+            for (int k = 0; k < qpg; ++k) t += red[g0 + k] + red[32 + g0 + k];
+            gmean[tid] = t / cnt;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const float mu = gmean[wm * 16 + i * 8 + 2 * rq + half];
+                float t = 0.f;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    if (pv[j])
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float d = acc[i][j][4 * rq + e] - mu;
+                            t += d * d;
+                        }
+                q[i][rq] = t;
+            }
+        half_wave_sum(q);
+        if (l32 == 0)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) red[wn * 32 + wm * 16 + i * 8 + 2 * rq + half] = q[i][rq];
+        __syncthreads();
+        const int gpb = kConvBM / p.gn_cpg;   // groups in this output-channel block
+        if (tid < gpb) {
+            float m2 = 0.f;
+            for (int k = 0; k < qpg; ++k) m2 += red[tid * qpg + k] + red[32 + tid * qpg + k];
+            const long long rec = (long long)(ob * gpb + tid) * p.gn_nrec + (long long)frame * gridDim.x + tile;
+            p.gn_rec[rec] = floatx4{cnt, gmean[tid * qpg], m2, 0.f};
         }
     }
 }
@@ -334,16 +421,32 @@ __global__ void pack_conv3x3_kernel(const float *__restrict__ w, float *__restri
 // y[o, :] = bias[o] + sum_s part[s, o, :] (+ res[o, :]), summed in split order.
 constexpr int kRedElems = 4096;   // elements per workgroup
 
+// Sum over the 256 threads of a workgroup; every thread gets the result.
+__device__ inline float block_sum(float v, float *scratch) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    __syncthreads();   // scratch may still be read from a previous call
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
+}
+
+// With gn_rec set, each workgroup also writes the GroupNorm record (count,
+// mean, sum of squared deviations) of the elements it produced: record
+// (o % cpg) * gridDim.x + blockIdx.x of group o / cpg.
 template <bool VEC, bool RES>
 __global__ __launch_bounds__(kThreads) void splitk_reduce(const float *__restrict__ part, long long part_stride,
                                                           int ksplit, const float *__restrict__ bias,
-                                                          const float *res, float *y, long long plane) {
+                                                          const float *res, float *y, long long plane,
+                                                          floatx4 *__restrict__ gn_rec, int gn_cpg) {
+    __shared__ float scratch[4];
     const int o = blockIdx.y;
     const long long base = (long long)o * plane;
     const long long lo = (long long)blockIdx.x * kRedElems;
     long long hi = lo + kRedElems;
     if (hi > plane) hi = plane;
     const float b = bias[o];
+    float sum = 0.f;
     if (VEC) {
         for (long long i = lo / 4 + threadIdx.x; i < hi / 4; i += kThreads) {
             floatx4 v = {b, b, b, b};
@@ -351,6 +454,7 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce(const float *__restric
                 v += reinterpret_cast<const floatx4 *>(part + sp * part_stride + base)[i];
             if (RES) v += reinterpret_cast<const floatx4 *>(res + base)[i];
             reinterpret_cast<floatx4 *>(y + base)[i] = v;
+            sum += (v[0] + v[1]) + (v[2] + v[3]);
         }
     } else {
         for (long long i = lo + threadIdx.x; i < hi; i += kThreads) {
@@ -358,7 +462,30 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce(const float *__restric
             for (int sp = 0; sp < ksplit; ++sp) v += part[sp * part_stride + base + i];
             if (RES) v += res[base + i];
             y[base + i] = v;
+            sum += v;
         }
+    }
+    if (!gn_rec) return;   // uniform over the workgroup
+    // Second pass over this thread's own outputs (program order: no barrier needed).
+    const float cnt = (float)(hi - lo);
+    const float mean = block_sum(sum, scratch) / cnt;
+    float m2 = 0.f;
+    if (VEC) {
+        for (long long i = lo / 4 + threadIdx.x; i < hi / 4; i += kThreads) {
+            const floatx4 d = reinterpret_cast<const floatx4 *>(y + base)[i] - mean;
+            m2 += (d[0] * d[0] + d[1] * d[1]) + (d[2] * d[2] + d[3] * d[3]);
+        }
+    } else {
+        for (long long i = lo + threadIdx.x; i < hi; i += kThreads) {
+            const float d = y[base + i] - mean;
+            m2 += d * d;
+        }
+    }
+    m2 = block_sum(m2, scratch);
+    if (threadIdx.x == 0) {
+        const long long nrec = (long long)gn_cpg * gridDim.x;
+        gn_rec[(long long)(o / gn_cpg) * nrec + (long long)(o % gn_cpg) * gridDim.x + blockIdx.x] =
+            floatx4{cnt, mean, m2, 0.f};
     }
 }
 
@@ -510,6 +637,16 @@ size_t conv3x3_partial_floats(int cout, int cin, int kt, int H, int W, int T) {
     return ks > 1 ? (size_t)ks * cout * T * (size_t)H * W : 0;
 }
 
+int conv3x3_gn_records(const ConvLaunch &a) {
+    if (a.cout % 32 != 0) return 0;
+    const long long plane = (long long)a.T * a.H * a.W;
+    if (conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T) > 1)
+        return (int)((a.cout / 32) * ((plane + kRedElems - 1) / kRedElems));
+    if (a.cout % kConvBM != 0 || (a.cout / 32) % 4 != 0) return 0;
+    const int TC = conv_tc(a.W), TR = kConvBN / TC;
+    return ((a.W + TC - 1) / TC) * ((a.H + TR - 1) / TR) * a.T;
+}
+
 const char *conv3x3_kernel_name(const ConvLaunch &a) {
     static const char *tcs[3] = {"32", "16", "8"};
     static const char *modes[4] = {"plain", "up2x", "denorm", "gnsilu"};
@@ -574,6 +711,18 @@ int32_t launch_conv3x3_main(const ConvLaunch &a, hipStream_t s) {
         return VAE_ERR_UNSUPPORTED;
     }
     p.gn_coef = a.gn_coef;
+    p.gn_rec = nullptr;
+    p.gn_cpg = 0;
+    p.gn_nrec = 0;
+    if (a.gn_rec && p.ksplit == 1) {
+        if (conv3x3_gn_records(a) == 0) {
+            set_error("conv3x3: GroupNorm records in the epilogue need out_channels %% 128 == 0");
+            return VAE_ERR_UNSUPPORTED;
+        }
+        p.gn_rec = a.gn_rec;
+        p.gn_cpg = a.cout / 32;
+        p.gn_nrec = (int)(grid.x * grid.z);
+    }
     const int mode = a.upsample ? MODE_UPSAMPLE : (a.denorm ? MODE_DENORM : (a.gn_coef ? MODE_GNSILU : MODE_PLAIN));
     const bool res = a.res != nullptr;
     const bool split = p.ksplit > 1;
@@ -590,15 +739,21 @@ int32_t launch_conv3x3_reduce(const ConvLaunch &a, hipStream_t s) {
     const long long part_stride = plane * a.cout;
     const bool res = a.res != nullptr;
     const dim3 rgrid((unsigned)((plane + kRedElems - 1) / kRedElems), (unsigned)a.cout);
+    floatx4 *rec = a.gn_rec;
+    const int cpg = a.cout / 32;
+    if (rec && a.cout % 32 != 0) {
+        set_error("splitk_reduce: GroupNorm records need out_channels %% 32 == 0");
+        return VAE_ERR_UNSUPPORTED;
+    }
     const bool vec = plane % 4 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(a.part) & 15) == 0 &&
                      (!res || (reinterpret_cast<uintptr_t>(a.res) & 15) == 0);
     if (vec) {
-        if (res) hipLaunchKernelGGL((splitk_reduce<true, true>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane);
-        else hipLaunchKernelGGL((splitk_reduce<true, false>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane);
+        if (res) hipLaunchKernelGGL((splitk_reduce<true, true>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane, rec, cpg);
+        else hipLaunchKernelGGL((splitk_reduce<true, false>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane, rec, cpg);
     } else {
-        if (res) hipLaunchKernelGGL((splitk_reduce<false, true>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane);
-        else hipLaunchKernelGGL((splitk_reduce<false, false>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane);
+        if (res) hipLaunchKernelGGL((splitk_reduce<false, true>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane, rec, cpg);
+        else hipLaunchKernelGGL((splitk_reduce<false, false>), rgrid, dim3(kThreads), 0, s, a.part, part_stride, ksplit, a.bias, a.res, a.y, plane, rec, cpg);
     }
     return check_launch("splitk_reduce");
 }

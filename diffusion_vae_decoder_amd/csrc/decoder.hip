@@ -233,6 +233,7 @@ struct Buffers {
     float *X, *Y, *T, *U, *S;
     float *part;   // split-K partial sums of the small convs
     float *coef;   // GroupNorm coefficients (mean, rstd*gamma, beta, -) per channel, for the next conv
+    floatx4 *rec;  // GroupNorm records a conv wrote for the normalisation of its output
     void *gn;
     void *attn;
 };
@@ -240,8 +241,19 @@ struct Buffers {
 // The chain's spatial plan for a latent of (h, w): largest activation (floats),
 // largest GroupNorm workspace, attention workspace.
 struct Plan {
-    size_t act = 0, gn = 0, attn = 0, part = 0, coef = 0;
+    size_t act = 0, gn = 0, attn = 0, part = 0, coef = 0, rec = 0;
 };
+
+ConvLaunch launch_shape(const DConv &c, long long H, long long W) {
+    ConvLaunch a{};
+    a.cin = c.cin;
+    a.cout = c.cout;
+    a.H = (int)H;
+    a.W = (int)W;
+    a.T = 1;
+    a.kt = 1;
+    return a;
+}
 
 Plan plan_for(const vae_decoder *d, int h, int w) {
     Plan p;
@@ -257,6 +269,8 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
     auto part = [&](const DConv &c, long long H, long long W) {
         const size_t n = conv3x3_partial_floats(c.cout, c.cin, 1, (int)H, (int)W, 1);
         if (n > p.part) p.part = n;
+        const size_t r = (size_t)32 * conv3x3_gn_records(launch_shape(c, H, W)) * sizeof(floatx4);
+        if (r > p.rec) p.rec = r;
     };
     long long H = h, W = w;
     act(d->latent_c, H, W);
@@ -315,10 +329,16 @@ struct Runner {
     }
 
     float *coef = nullptr;
+    // GroupNorm records of the activation rec_of (written by the last conv
+    // asked for them), consumed by the next normalisation of that activation.
+    floatx4 *rec = nullptr;
+    const float *rec_of = nullptr;
+    int rec_n = 0;
 
     void conv3(const std::string &layer, const DConv &c, const float *x, int H, int W, bool up,
-               const float *res, float *y, bool denorm = false, bool gn = false) {
+               const float *res, float *y, bool denorm = false, bool gn = false, bool stats = false) {
         if (rc != VAE_OK) return;
+        rec_of = nullptr;
         ConvLaunch a{};
         a.x = x;
         a.wpk = c.w;
@@ -337,6 +357,8 @@ struct Runner {
         a.dn_shift = d->shift;
         a.part = part;
         a.gn_coef = gn ? coef : nullptr;
+        const int nrec = stats && c.cout % 32 == 0 ? conv3x3_gn_records(a) : 0;
+        a.gn_rec = nrec > 0 ? rec : nullptr;
         const double in_elems = (double)c.cin * H * W / (up ? 4.0 : 1.0);
         const double bytes = 4.0 * (in_elems + (double)c.cout * H * W * (res ? 2.0 : 1.0));
         const int ks = conv3x3_ksplit(c.cout, c.cin, 1, H, W, 1);
@@ -345,11 +367,23 @@ struct Runner {
         if (rc != VAE_OK) return;
         rc = launch_conv3x3_main(a, s);
         end(e);
-        if (rc != VAE_OK || ks == 1) return;
-        e = begin("splitk_reduce", layer, 0.0, 4.0 * (double)c.cout * H * W * (ks + 1 + (res ? 1 : 0)));
-        if (rc != VAE_OK) return;
-        rc = launch_conv3x3_reduce(a, s);
-        end(e);
+        if (rc == VAE_OK && ks > 1) {
+            e = begin("splitk_reduce", layer, 0.0, 4.0 * (double)c.cout * H * W * (ks + 1 + (res ? 1 : 0)));
+            if (rc != VAE_OK) return;
+            rc = launch_conv3x3_reduce(a, s);
+            end(e);
+        }
+        if (rc == VAE_OK && a.gn_rec) {
+            rec_of = y;
+            rec_n = nrec;
+        }
+    }
+    // Records for x if the last conv wrote them (then they are used up).
+    const floatx4 *take_rec(const float *x, int *n) {
+        const floatx4 *r = (x == rec_of) ? rec : nullptr;
+        *n = r ? rec_n : 0;
+        rec_of = nullptr;
+        return r;
     }
     void conv1(const std::string &layer, const DConv &c, const float *x, int H, int W, float *y) {
         if (rc != VAE_OK) return;
@@ -374,42 +408,47 @@ struct Runner {
     // next conv applies the normalisation and SiLU while loading x.
     void gnc(const std::string &layer, const DNorm &n, const float *x, long long spatial, void *ws) {
         if (rc != VAE_OK) return;
-        ProfEntry *e = begin("groupnorm_stats", layer, 0.0, 4.0 * n.c * (double)spatial);
+        int nr = 0;
+        const floatx4 *r = take_rec(x, &nr);
+        ProfEntry *e = begin(r ? "groupnorm_merge" : "groupnorm_stats", layer, 0.0, r ? 0.0 : 4.0 * n.c * (double)spatial);
         if (rc != VAE_OK) return;
-        rc = launch_groupnorm_coef(x, n.c, spatial, n.g, n.b, ws, coef, s);
+        rc = launch_groupnorm_coef(x, n.c, spatial, n.g, n.b, ws, coef, s, r, nr);
         end(e);
     }
     void gn(const std::string &layer, const DNorm &n, const float *x, long long spatial, float *y, void *ws) {
         if (rc != VAE_OK) return;
+        int nr = 0;
+        const floatx4 *r = take_rec(x, &nr);
         ProfEntry *e = begin("groupnorm_silu", layer, 0.0, 8.0 * n.c * (double)spatial);
         if (rc != VAE_OK) return;
-        rc = launch_groupnorm(x, n.c, spatial, n.g, n.b, 1, nullptr, y, ws, s);
+        rc = launch_groupnorm(x, n.c, spatial, n.g, n.b, 1, nullptr, y, ws, s, r, nr);
         end(e);
     }
-    // X -> Y; uses T, U (and S for a 1x1 skip).
-    void resnet(const DRes &r, Buffers &b, int H, int W) {
+    // X -> Y; uses T, U (and S for a 1x1 skip).  out_stats: the output is
+    // normalised next, so conv2 records its GroupNorm statistics.
+    void resnet(const DRes &r, Buffers &b, int H, int W, bool out_stats) {
         const long long sp = (long long)H * W;
         if (!d->gn_fused) {
             gn(r.name + ".norm1", r.n1, b.X, sp, b.T, b.gn);
-            conv3(r.name + ".conv1", r.c1, b.T, H, W, false, nullptr, b.U);
+            conv3(r.name + ".conv1", r.c1, b.T, H, W, false, nullptr, b.U, false, false, true);
             gn(r.name + ".norm2", r.n2, b.U, sp, b.U, b.gn);
             const float *skip = b.X;
             if (r.sc.present) {
                 conv1(r.name + ".conv_shortcut", r.sc, b.X, H, W, b.S);
                 skip = b.S;
             }
-            conv3(r.name + ".conv2", r.c2, b.U, H, W, false, skip, b.Y);
+            conv3(r.name + ".conv2", r.c2, b.U, H, W, false, skip, b.Y, false, false, out_stats);
             return;
         }
         gnc(r.name + ".norm1", r.n1, b.X, sp, b.gn);
-        conv3(r.name + ".conv1", r.c1, b.X, H, W, false, nullptr, b.U, false, true);
+        conv3(r.name + ".conv1", r.c1, b.X, H, W, false, nullptr, b.U, false, true, true);
         gnc(r.name + ".norm2", r.n2, b.U, sp, b.gn);
         const float *skip = b.X;
         if (r.sc.present) {
             conv1(r.name + ".conv_shortcut", r.sc, b.X, H, W, b.S);
             skip = b.S;
         }
-        conv3(r.name + ".conv2", r.c2, b.U, H, W, false, skip, b.Y, false, true);
+        conv3(r.name + ".conv2", r.c2, b.U, H, W, false, skip, b.Y, false, true, out_stats);
     }
 };
 
@@ -495,7 +534,7 @@ int32_t vae_decoder_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, 
         return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_workspace_bytes: latent %dx%d too large", h, w);
     const Plan p = plan_for(d, h, w);
     *bytes = 5 * align256(p.act * 4) + align256(p.gn) + align256(p.attn) + align256(p.part * 4) +
-             align256(p.coef);
+             align256(p.coef) + align256(p.rec);
     return VAE_OK;
 }
 
@@ -523,12 +562,15 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
     b.part = reinterpret_cast<float *>(q);
     q += align256(pl.part * 4);
     b.coef = reinterpret_cast<float *>(q);
+    q += align256(pl.coef);
+    b.rec = reinterpret_cast<floatx4 *>(q);
 
     Runner r{d, static_cast<hipStream_t>(stream), b.part};
     r.coef = b.coef;
+    r.rec = b.rec;
     int H = h, W = w;
-    r.conv3("conv_in", d->conv_in, latent, H, W, false, nullptr, b.X, /*denorm=*/true);
-    r.resnet(d->mid0, b, H, W);
+    r.conv3("conv_in", d->conv_in, latent, H, W, false, nullptr, b.X, /*denorm=*/true, false, /*stats=*/true);
+    r.resnet(d->mid0, b, H, W, /*out_stats=*/false);   // the attention normalises its own input
     std::swap(b.X, b.Y);
     if (r.rc == VAE_OK) {
         const double n = (double)H * W, c = d->attn.c;
@@ -541,18 +583,20 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
         }
     }
     std::swap(b.X, b.Y);
-    r.resnet(d->mid1, b, H, W);
+    r.resnet(d->mid1, b, H, W, true);
     std::swap(b.X, b.Y);
     for (size_t i = 0; i < d->ups.size(); ++i) {
         const DUp &u = d->ups[i];
-        for (const DRes &res : u.res) {
-            r.resnet(res, b, H, W);
+        for (size_t j = 0; j < u.res.size(); ++j) {
+            // the last resnet before an upsample feeds a conv, not a GroupNorm
+            r.resnet(u.res[j], b, H, W, !(j + 1 == u.res.size() && u.up.present));
             std::swap(b.X, b.Y);
         }
         if (u.up.present) {
             H *= 2;
             W *= 2;
-            r.conv3("up_blocks." + std::to_string(i) + ".upsamplers.0.conv", u.up, b.X, H, W, true, nullptr, b.Y);
+            r.conv3("up_blocks." + std::to_string(i) + ".upsamplers.0.conv", u.up, b.X, H, W, true, nullptr, b.Y,
+                    false, false, true);
             std::swap(b.X, b.Y);
         }
     }

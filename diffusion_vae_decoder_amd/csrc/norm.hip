@@ -190,6 +190,54 @@ __global__ __launch_bounds__(kThreads) void gn_coef(long long gsize, int cpg, in
     }
 }
 
+// Chan et al.'s pairwise update of (count, mean, M2): the statistics of the
+// union of two disjoint sets from those of each.
+struct Moments {
+    double n, mean, m2;
+};
+__device__ inline Moments merge_moments(Moments a, Moments b) {
+    if (b.n == 0.0) return a;
+    if (a.n == 0.0) return b;
+    const double n = a.n + b.n;
+    const double d = b.mean - a.mean;
+    return {n, a.mean + d * (b.n / n), a.m2 + b.m2 + d * d * (a.n * b.n / n)};
+}
+__device__ inline Moments shfl_down_moments(Moments m, int o) {
+    return {__shfl_down(m.n, o, 64), __shfl_down(m.mean, o, 64), __shfl_down(m.m2, o, 64)};
+}
+
+// One workgroup per group merges the group's records in a fixed order (a
+// strided sequential pass per thread, then a fixed tree), and stores the
+// result in the partial-sum form gn_apply and gn_coef read with one part:
+// shift = mean, sum d = 0, sum d^2 = M2.
+__global__ __launch_bounds__(kThreads) void gn_merge(const floatx4 *__restrict__ rec, int nrec,
+                                                     double *__restrict__ part, double *__restrict__ shift_out) {
+    __shared__ double sh[3 * 4];
+    const int g = blockIdx.x;
+    const floatx4 *r = rec + (long long)g * nrec;
+    Moments m{0.0, 0.0, 0.0};
+    for (int i = threadIdx.x; i < nrec; i += kThreads) {
+        const floatx4 v = r[i];
+        m = merge_moments(m, Moments{(double)v[0], (double)v[1], (double)v[2]});
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = merge_moments(m, shfl_down_moments(m, o));
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        sh[3 * wave] = m.n;
+        sh[3 * wave + 1] = m.mean;
+        sh[3 * wave + 2] = m.m2;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        Moments t{sh[0], sh[1], sh[2]};
+        for (int w = 1; w < 4; ++w) t = merge_moments(t, Moments{sh[3 * w], sh[3 * w + 1], sh[3 * w + 2]});
+        part[2 * g] = 0.0;
+        part[2 * g + 1] = t.m2;
+        shift_out[g] = t.mean;
+    }
+}
+
 template <bool VEC, bool SILU>
 void apply2(bool res, dim3 grid, hipStream_t s, const float *x, long long spatial, int cpg,
             int parts, const double *part, const double *shifts, const float *gamma,
@@ -290,6 +338,31 @@ __global__ __launch_bounds__(kThreads) void softmax_rows_kernel(float *S, int co
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+size_t groupnorm_ws_bytes(int c, long long spatial) {
+    const long long gsize = (long long)(c / kGroups) * spatial;
+    return (size_t)kGroups * parts_for(gsize) * 2 * sizeof(double) + kGroups * sizeof(double);
+}
+
+// Statistics of x's 32 groups into ws: from the records a producer wrote
+// (one merged part per group) or from a pass over x.  Returns the parts.
+int32_t groupnorm_stats(const float *x, int c, long long spatial, void *ws, hipStream_t s, const floatx4 *rec,
+                        int nrec, int *parts_out) {
+    const long long gsize = (long long)(c / kGroups) * spatial;
+    const int parts = rec ? 1 : parts_for(gsize);
+    double *part = reinterpret_cast<double *>(ws);
+    double *shifts = part + 2 * kGroups * parts;
+    *parts_out = parts;
+    if (rec) {
+        hipLaunchKernelGGL(gn_merge, dim3(kGroups), dim3(kThreads), 0, s, rec, nrec, part, shifts);
+        return check_launch("gn_merge");
+    }
+    if (gsize % 4 == 0 && aligned16(x))
+        hipLaunchKernelGGL(gn_stats<true>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize, parts, part, shifts);
+    else
+        hipLaunchKernelGGL(gn_stats<false>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize, parts, part, shifts);
+    return check_launch("gn_stats");
+}
+
 }  // namespace
 
 size_t groupnorm_ws_bytes(int c, long long spatial) {
@@ -299,21 +372,13 @@ size_t groupnorm_ws_bytes(int c, long long spatial) {
 
 int32_t launch_groupnorm(const float *x, int c, long long spatial, const float *gamma,
                          const float *beta, int silu, const float *res, float *y, void *ws,
-                         hipStream_t s) {
+                         hipStream_t s, const floatx4 *rec, int nrec) {
     const int cpg = c / kGroups;
-    const long long gsize = (long long)cpg * spatial;
-    const int parts = parts_for(gsize);
-    double *part = reinterpret_cast<double *>(ws);
-    double *shifts = part + 2 * kGroups * parts;
-    const bool vec_stats = gsize % 4 == 0 && aligned16(x);
-    if (vec_stats)
-        hipLaunchKernelGGL(gn_stats<true>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize, parts,
-                           part, shifts);
-    else
-        hipLaunchKernelGGL(gn_stats<false>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize,
-                           parts, part, shifts);
-    int32_t rc = check_launch("gn_stats");
+    int parts = 0;
+    int32_t rc = groupnorm_stats(x, c, spatial, ws, s, rec, nrec, &parts);
     if (rc != VAE_OK) return rc;
+    const double *part = reinterpret_cast<const double *>(ws);
+    const double *shifts = part + 2 * kGroups * parts;
     const bool vec = spatial % 4 == 0 && aligned16(x) && aligned16(y) && (!res || aligned16(res));
     const dim3 grid((unsigned)((spatial + kApplyElems - 1) / kApplyElems), (unsigned)c);
     if (vec) {
@@ -327,18 +392,14 @@ int32_t launch_groupnorm(const float *x, int c, long long spatial, const float *
 }
 
 int32_t launch_groupnorm_coef(const float *x, int c, long long spatial, const float *gamma, const float *beta,
-                              void *ws, float *coef, hipStream_t s) {
+                              void *ws, float *coef, hipStream_t s, const floatx4 *rec, int nrec) {
     const int cpg = c / kGroups;
     const long long gsize = (long long)cpg * spatial;
-    const int parts = parts_for(gsize);
-    double *part = reinterpret_cast<double *>(ws);
-    double *shifts = part + 2 * kGroups * parts;
-    if (gsize % 4 == 0 && aligned16(x))
-        hipLaunchKernelGGL(gn_stats<true>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize, parts, part, shifts);
-    else
-        hipLaunchKernelGGL(gn_stats<false>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize, parts, part, shifts);
-    int32_t rc = check_launch("gn_stats");
+    int parts = 0;
+    int32_t rc = groupnorm_stats(x, c, spatial, ws, s, rec, nrec, &parts);
     if (rc != VAE_OK) return rc;
+    const double *part = reinterpret_cast<const double *>(ws);
+    const double *shifts = part + 2 * kGroups * parts;
     hipLaunchKernelGGL(gn_coef, dim3(kGroups), dim3(kThreads), 0, s, gsize, cpg, parts, part, shifts, gamma, beta, coef);
     return check_launch("gn_coef");
 }

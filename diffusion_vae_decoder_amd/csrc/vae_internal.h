@@ -42,6 +42,9 @@ struct ConvLaunch {
     float *part;           // split-K partial sums, conv3x3_partial_floats() floats (or nullptr if 0)
     const float *gn_coef;  // if set: the input is silu((x - c[0]) * c[1] + c[2]) with c = gn_coef[4*channel..]
                            // (GroupNorm + SiLU applied on load; padding stays 0)
+    floatx4 *gn_rec;       // if set: GroupNorm(32) records of y for the normalisation that follows,
+                           // [32][conv3x3_gn_records()] of (count, mean, M2, 0); M2 is the sum of
+                           // squared deviations from the record's own mean
 };
 
 // Bytes of the packed weights for a conv with `cout` x `cin` x (kt x 3 x 3).
@@ -57,6 +60,10 @@ int32_t launch_conv3x3_reduce(const ConvLaunch &a, hipStream_t s);
 // the partial-sum workspace it then needs (floats, 0 when not split).
 int conv3x3_ksplit(int cout, int cin, int kt, int H, int W, int T);
 size_t conv3x3_partial_floats(int cout, int cin, int kt, int H, int W, int T);
+// GroupNorm records per group that launch_conv3x3 writes for `a` when
+// a.gn_rec is set; 0 if this launch cannot produce them (then normalise with
+// a separate statistics pass).
+int conv3x3_gn_records(const ConvLaunch &a);
 // Name of the kernel instantiation launch_conv3x3 picks for `a`.
 const char *conv3x3_kernel_name(const ConvLaunch &a);
 
@@ -84,13 +91,17 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s);
 
 // ------------------------------------------------------------------ norm
 size_t groupnorm_ws_bytes(int c, long long spatial);
+// y = silu?(GroupNorm(x)) (+ res).  With `rec` (nrec records per group, as a
+// producer wrote them in ConvLaunch::gn_rec) the statistics are merged from
+// the records instead of a pass over x.
 int32_t launch_groupnorm(const float *x, int c, long long spatial, const float *gamma,
                          const float *beta, int silu, const float *res, float *y, void *ws,
-                         hipStream_t s);
+                         hipStream_t s, const floatx4 *rec = nullptr, int nrec = 0);
 // Statistics only: writes coef[4*c + {0,1,2}] = (mean of c's group, rstd * gamma[c], beta[c])
-// for a consumer that normalises while loading.  ws as for launch_groupnorm.
+// for a consumer that normalises while loading.  ws and rec as for launch_groupnorm.
 int32_t launch_groupnorm_coef(const float *x, int c, long long spatial, const float *gamma, const float *beta,
-                              void *ws, float *coef, hipStream_t s);
+                              void *ws, float *coef, hipStream_t s, const floatx4 *rec = nullptr,
+                              int nrec = 0);
 
 // ------------------------------------------------------------------ misc
 int32_t launch_upsample2x(const float *x, int c, int h, int w, float *y, hipStream_t s);

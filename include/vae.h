@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 2
+#define VAE_ABI_VERSION 3
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -151,6 +151,26 @@ int32_t vae_groupnorm_workspace_bytes(int32_t c, int64_t spatial, size_t *bytes)
 int32_t vae_groupnorm_silu(const float *x, int32_t c, int64_t spatial, const vae_norm *norm,
                            int32_t apply_silu, const float *residual, float *y,
                            void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace for vae_conv2d_groupnorm_silu (same arguments as
+ * vae_conv2d_workspace_bytes; kernel 3, out_channels % 32 == 0). */
+int32_t vae_conv2d_groupnorm_workspace_bytes(const vae_conv *conv, int32_t h, int32_t w, int32_t upsample2x,
+                                             size_t *bytes);
+
+/* A 3x3 convolution followed by GroupNorm(32) (+ SiLU) of its output: the
+ * conv -> norm pairs of VaeResnetRef (conv1 -> norm2, and conv2 -> the next
+ * resnet's norm1).
+ *   y = conv(u) + bias [+ residual]      exactly as vae_conv2d (kernel 3)
+ *   z = GroupNorm(y), then SiLU if apply_silu, as vae_groupnorm_silu
+ * The conv's epilogue records per-group statistics of the tiles it writes
+ * (count, mean, sum of squared deviations), so the normalisation needs no
+ * separate statistics pass over y.  norm->channels == conv->out_channels,
+ * a multiple of 32.  y may not alias x; y may alias residual; z may alias
+ * any argument (it is written last). */
+int32_t vae_conv2d_groupnorm_silu(const float *x, int32_t cin, int32_t h, int32_t w, const vae_conv *conv,
+                                  int32_t upsample2x, const float *residual, const vae_norm *norm,
+                                  int32_t apply_silu, float *y, float *z, void *ws, size_t ws_bytes,
+                                  void *stream);
 
 /* Nearest x2 upsample (VaeUpRef): y[c, Y, X] = x[c, Y/2, X/2];
  * x [c, h, w] -> y [c, 2h, 2w].  Exact copy. */

@@ -100,6 +100,38 @@ def test_conv_in_and_3d_validation(lib):
     assert lib.vae_conv3d_causal(FAKE, 64, 3, 8, 8, byref(c3), FAKE + 64, FAKE, nb.value, NULL) == VAE_ERR_INVALID_ARG
 
 
+def test_conv_groupnorm_validation(lib):
+    c = conv(128, 16, 3)
+    nb = c_size_t()
+    assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(c), 37, 45, 0, byref(nb)) == VAE_OK
+    # packed weights (4 chunks of 36 x 128), 20 tiles x 32 groups of 16-byte records, GroupNorm partials
+    assert nb.value == 4 * 36 * 128 * 4 + 20 * 32 * 16 + 32 * 16 + 32 * 8
+    c64 = conv(64, 16, 3)                        # 2 channels per group: no records, a statistics pass
+    n64 = c_size_t()
+    assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(c64), 37, 45, 0, byref(n64)) == VAE_OK
+    assert n64.value == 256 * ((4 * 36 * 128 * 4 + 255) // 256) + 32 * 16 + 32 * 8
+    assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(conv(100, 16, 3)), 8, 8, 0, byref(nb)) == VAE_ERR_UNSUPPORTED
+    assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(conv(128, 16, 1)), 8, 8, 0, byref(nb)) == VAE_ERR_UNSUPPORTED
+    n = VaeNorm(FAKE, FAKE, 128)
+    ws = c_size_t()
+    lib.vae_conv2d_groupnorm_workspace_bytes(byref(c), 8, 8, 0, byref(ws))
+
+    def call(**k):
+        a = dict(x=FAKE, cin=16, h=8, w=8, conv=byref(c), up=0, res=NULL, norm=byref(n), silu=1, y=FAKE + 4096,
+                 z=FAKE + 8192, ws=FAKE + 16384, nb=ws.value)
+        a.update(k)
+        return lib.vae_conv2d_groupnorm_silu(a["x"], a["cin"], a["h"], a["w"], a["conv"], a["up"], a["res"],
+                                             a["norm"], a["silu"], a["y"], a["z"], a["ws"], a["nb"], NULL)
+    assert call(z=NULL) == VAE_ERR_INVALID_ARG
+    assert call(norm=NULL) == VAE_ERR_INVALID_ARG
+    assert call(norm=byref(VaeNorm(FAKE, FAKE, 64))) == VAE_ERR_INVALID_ARG and "norm" in err(lib)
+    assert call(cin=15) == VAE_ERR_INVALID_ARG
+    assert call(y=FAKE) == VAE_ERR_INVALID_ARG and "alias" in err(lib)
+    assert call(nb=ws.value - 1) == VAE_ERR_WORKSPACE
+    c100 = conv(100, 16, 3)
+    assert call(conv=byref(c100), norm=byref(VaeNorm(FAKE, FAKE, 100))) == VAE_ERR_UNSUPPORTED
+
+
 def test_groupnorm_validation(lib):
     nb = c_size_t()
     assert lib.vae_groupnorm_workspace_bytes(128, 512 * 512, byref(nb)) == VAE_OK

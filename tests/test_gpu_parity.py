@@ -167,6 +167,56 @@ def test_groupnorm_in_place_and_large_mean(api):
     assert rel_err(host(t), ref) <= LAYER_TOL
 
 
+# conv -> GroupNorm(+SiLU) with the group statistics recorded by the conv:
+# in the MFMA epilogue (whole 4-channel quads per group, not K-split), in the
+# split-K reduction, or (fewer than 4 channels per group) by a separate pass.
+CONV_GN_CASES = [
+    # cin, cout, h, w, upsample, residual, silu
+    (16, 128, 37, 45, False, False, True),    # epilogue records, TC=32, ragged rows and columns
+    (16, 256, 40, 13, False, True, True),     # TC=16, 8 channels per group, residual
+    (16, 512, 50, 7, False, False, False),    # TC=8, 16 channels per group, no SiLU
+    (16, 128, 19, 21, True, True, True),      # folded upsample to 38x42 + residual
+    (64, 128, 24, 20, False, False, True),    # K-split: records from the reduction (vector path)
+    (64, 128, 23, 19, False, True, True),     # K-split, odd plane (scalar path), residual
+    (16, 64, 21, 30, False, False, True),     # 2 channels per group: separate statistics pass
+]
+
+
+@pytest.mark.parametrize("cin,cout,h,w,up,res,silu", CONV_GN_CASES)
+def test_conv_groupnorm_silu(api, cin, cout, h, w, up, res, silu):
+    H, W = (2 * h, 2 * w) if up else (h, w)
+    x = vaegen.activation(21, "xcg", (cin, h, w))
+    wt, b = conv_params(21, f"ccg{cin}_{cout}", cin, cout, 3)
+    n = vaegen.norm_params(21, "ncg", cout)
+    g, bt = n["ncg.weight"], n["ncg.bias"]
+    r = vaegen.activation(21, "rcg", (cout, H, W)) if res else None
+    y, z = api.conv2d_groupnorm_silu(dev(x), dev(wt), dev(b), dev(g), dev(bt), silu=silu, upsample2x=up,
+                                     residual=dev(r) if res else None, out=nan_like((cout, H, W)),
+                                     out_norm=nan_like((cout, H, W)))
+    yref = oracle.conv2d(oracle.upsample_nearest2x(x) if up else x, wt, b) + (r if res else 0.0)
+    zref = oracle.group_norm(yref, g, bt)
+    if silu:
+        zref = oracle.silu(zref)
+    assert rel_err(host(y), yref) <= LAYER_TOL
+    assert rel_err(host(z), zref) <= LAYER_TOL
+
+
+def test_conv_groupnorm_large_mean_in_place(api):
+    # outputs with a common offset 50x their spread: per-tile centring keeps
+    # the variance free of cancellation; z overwrites y
+    cin, cout, h, w = 16, 128, 33, 70
+    x = vaegen.activation(22, "xcm", (cin, h, w))
+    wt, b = conv_params(22, "ccm", cin, cout, 3)
+    b = (b + 50.0).astype(np.float32)
+    n = vaegen.norm_params(22, "ncm", cout)
+    t = nan_like((cout, h, w))
+    y, z = api.conv2d_groupnorm_silu(dev(x), dev(wt), dev(b), dev(n["ncm.weight"]), dev(n["ncm.bias"]),
+                                     out=t, out_norm=t)
+    assert y.data_ptr() == z.data_ptr()
+    zref = oracle.silu(oracle.group_norm(oracle.conv2d(x, wt, b), n["ncm.weight"], n["ncm.bias"]))
+    assert rel_err(host(z), zref) <= LAYER_TOL
+
+
 @pytest.mark.parametrize("c,h,w", [(128, 64, 64), (3, 5, 7), (16, 1, 1)])
 def test_upsample_exact(api, c, h, w):
     x = vaegen.activation(9, "xu2", (c, h, w))
