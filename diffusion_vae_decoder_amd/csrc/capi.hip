@@ -132,7 +132,7 @@ int32_t vae_conv2d(const float *x, int32_t cin, int32_t h, int32_t w, const vae_
         return launch_gemm(g, s);
     }
     if (conv->out_channels <= 4 && !upsample2x && !residual)
-        return launch_conv3x3_skinny(x, conv->weight, conv->bias, y, cin, conv->out_channels, h, w, s);
+        return launch_conv3x3_direct(x, conv->weight, conv->bias, y, cin, conv->out_channels, h, w, s);
     const size_t need = conv_ws(conv, 1, 1, H, W);
     if (!ws || ws_bytes < need)
         return set_error("vae_conv2d: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;

@@ -32,9 +32,9 @@
 // an LDS table.  It removes the separate normalisation pass but costs about
 // 10% of the conv on MI355X, more than that pass.
 //
-// conv3x3_skinny: the 128 -> 3 conv_out.  With 3 output channels the GEMM is
-// far too thin for MFMA; the layer is bound by reading its input, so a direct
-// FMA kernel over LDS-staged halo tiles is used instead.
+// conv3x3_direct: the 128 -> 3 conv_out.  With 3 output channels the GEMM is
+// far too thin for MFMA; a direct FMA kernel over LDS-staged halo tiles
+// streams the input once (optionally normalising it on load).
 
 #include <cstdio>
 
@@ -73,7 +73,7 @@ struct Geom {
 
 constexpr int kW4 = kCK * kConvBM / 4;                      // float4s of one weight chunk
 constexpr int kW4_PER_T = (kW4 + kThreads - 1) / kThreads;
-constexpr int kGnMaxChannels = 512;   // input channels the GroupNorm-on-load table holds
+constexpr int kGnMaxChannels = kDirectGnMaxChannels;   // input channels a GroupNorm-on-load table holds
 
 struct Params {
     const float *x, *wpk, *bias, *res;
@@ -513,87 +513,162 @@ void launch_tc(const Params &p, int mode, bool res, bool split, dim3 grid, hipSt
 }
 
 // ---------------------------------------------------------------- conv_out
-constexpr int kSkR = 8;          // tile rows
-constexpr int kSkC = 128;        // tile columns (4 per thread)
-constexpr int kSkCC = 8;         // channels per chunk
-constexpr int kSkHW = kSkC + 2;
-constexpr int kSkHP = (kSkR + 2) * kSkHW;
+// Direct 3x3 conv for a handful of output channels.  Workgroup tile: 8 rows x
+// 128 columns; thread (r, g) computes pixels 4g..4g+3 of row r for every
+// output channel.  Input channels go in chunks of 4: the chunk's halo tile
+// [4][10][128 + 2] is loaded into registers (float4 loads for the 128
+// interior columns, one scalar per row edge) while the previous chunk is
+// being used, then written to LDS.  The weights are the same for the whole
+// workgroup and are read through the scalar cache.
+constexpr int kDR = 8;                 // tile rows
+constexpr int kDC = 128;               // tile columns
+constexpr int kDCC = 4;                // input channels per chunk
+constexpr int kDRow = kDC + 8;         // LDS row: [pad x3][left][128 interior][right][pad x3]
+constexpr int kDRows = kDR + 2;
+constexpr int kDQuads = kDCC * kDRows * (kDC / 4);            // float4 items per chunk (1280)
+constexpr int kDQPerT = (kDQuads + kThreads - 1) / kThreads;  // 5
+constexpr int kDEdges = kDCC * kDRows * 2;                    // scalar edge items per chunk (80)
 
 template <int COUT, bool GN>
-__global__ __launch_bounds__(kThreads) void conv3x3_skinny(const float *__restrict__ x,
+__global__ __launch_bounds__(kThreads) void conv3x3_direct(const float *__restrict__ x,
                                                            const float *__restrict__ w,
                                                            const float *__restrict__ bias,
                                                            float *__restrict__ y, int cin, int H,
                                                            int W, int tiles_x,
                                                            const float *__restrict__ gn_coef) {
-    __shared__ float halo[kSkCC * kSkHP];
-    __shared__ float wt[COUT * kSkCC * 9];
+    __shared__ __attribute__((aligned(16))) float halo[kDCC * kDRows * kDRow];
+    __shared__ float lc[GN ? 3 * (kGnMaxChannels + kDCC) : 1];
     const int tid = threadIdx.x;
     const int ty = blockIdx.x / tiles_x, tx = blockIdx.x - (blockIdx.x / tiles_x) * tiles_x;
-    const int y0 = ty * kSkR, x0 = tx * kSkC;
-    const int r = tid >> 5, cg = tid & 31;
+    const int y0 = ty * kDR, x0 = tx * kDC;
+    const int r = tid >> 5, g = tid & 31;
     const long long plane = (long long)H * W;
+    // interior columns of this tile all inside the image and rows 16-byte aligned
+    const bool vec = (W & 3) == 0 && x0 + kDC <= W && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    const bool vec_out = (W & 3) == 0 && x0 + kDC <= W && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+    const int n_chunks = (cin + kDCC - 1) / kDCC;
+
+    if (GN) {
+        for (int e = tid; e < 3 * n_chunks * kDCC; e += kThreads) {
+            const int c = e / 3, k = e - 3 * (e / 3);
+            lc[e] = c < cin ? gn_coef[4 * c + k] : 0.f;
+        }
+    }
+
+    floatx4 q[kDQPerT];
+    float edge = 0.f;
+    auto gn = [&](float v, int c) {
+        const float *cf = lc + 3 * c;
+        const float t = (v - cf[0]) * cf[1] + cf[2];
+        return t * __builtin_amdgcn_rcpf(1.f + __expf(-t));
+    };
+    // global -> registers for chunk starting at channel c0
+    auto load = [&](int c0) {
+#pragma unroll
+        for (int j = 0; j < kDQPerT; ++j) {
+            const int k = tid + j * kThreads;
+            floatx4 v = {0.f, 0.f, 0.f, 0.f};
+            if (k < kDQuads) {
+                const int c = k / (kDRows * 32), rem = k - c * (kDRows * 32);
+                const int row = rem >> 5, qq = rem & 31;
+                const int ch = c0 + c, yy = y0 - 1 + row, xx = x0 + 4 * qq;
+                if (ch < cin && yy >= 0 && yy < H) {
+                    const float *src = x + ch * plane + (long long)yy * W + xx;
+                    if (vec) {
+                        v = *reinterpret_cast<const floatx4 *>(src);
+                        if (GN) {
+                            v[0] = gn(v[0], ch);
+                            v[1] = gn(v[1], ch);
+                            v[2] = gn(v[2], ch);
+                            v[3] = gn(v[3], ch);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (xx + e < W) v[e] = GN ? gn(src[e], ch) : src[e];
+                    }
+                }
+            }
+            q[j] = v;
+        }
+        if (tid < kDEdges) {
+            const int c = tid / (2 * kDRows), rem = tid - c * (2 * kDRows);
+            const int row = rem >> 1, side = rem & 1;
+            const int ch = c0 + c, yy = y0 - 1 + row, xx = side ? x0 + kDC : x0 - 1;
+            float v = 0.f;
+            if (ch < cin && yy >= 0 && yy < H && xx >= 0 && xx < W) {
+                v = x[ch * plane + (long long)yy * W + xx];
+                if (GN) v = gn(v, ch);
+            }
+            edge = v;
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int j = 0; j < kDQPerT; ++j) {
+            const int k = tid + j * kThreads;
+            if (k < kDQuads) {
+                const int c = k / (kDRows * 32), rem = k - c * (kDRows * 32);
+                const int row = rem >> 5, qq = rem & 31;
+                *reinterpret_cast<floatx4 *>(&halo[(c * kDRows + row) * kDRow + 4 + 4 * qq]) = q[j];
+            }
+        }
+        if (tid < kDEdges) {
+            const int c = tid / (2 * kDRows), rem = tid - c * (2 * kDRows);
+            const int row = rem >> 1, side = rem & 1;
+            halo[(c * kDRows + row) * kDRow + (side ? 4 + kDC : 3)] = edge;
+        }
+    };
 
     float acc[COUT][4];
 #pragma unroll
     for (int o = 0; o < COUT; ++o)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[o][q] = 0.f;
+        for (int e = 0; e < 4; ++e) acc[o][e] = 0.f;
 
-    for (int c0 = 0; c0 < cin; c0 += kSkCC) {
-        for (int e = tid; e < kSkCC * kSkHP; e += kThreads) {
-            const int c = e / kSkHP;
-            const int rem = e - c * kSkHP;
-            const int rr = rem / kSkHW, cc = rem - (rem / kSkHW) * kSkHW;
-            const int yy = y0 - 1 + rr, xx = x0 - 1 + cc;
-            float v = 0.f;
-            if (c0 + c < cin && yy >= 0 && yy < H && xx >= 0 && xx < W) {
-                v = x[(long long)(c0 + c) * plane + (long long)yy * W + xx];
-                if (GN) {
-                    const floatx4 cf = reinterpret_cast<const floatx4 *>(gn_coef)[c0 + c];
-                    v = (v - cf[0]) * cf[1] + cf[2];
-                    v = v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
-                }
-            }
-            halo[e] = v;
-        }
-        for (int e = tid; e < COUT * kSkCC * 9; e += kThreads) {
-            const int o = e / (kSkCC * 9);
-            const int rem = e - o * (kSkCC * 9);
-            const int c = rem / 9, tap = rem - (rem / 9) * 9;
-            wt[e] = (c0 + c < cin) ? w[((long long)o * cin + c0 + c) * 9 + tap] : 0.f;
-        }
+    if (GN) __syncthreads();   // coefficient table
+    load(0);
+    for (int cb = 0; cb < n_chunks; ++cb) {
+        const int c0 = cb * kDCC;
+        store();
         __syncthreads();
-#pragma unroll 2
-        for (int c = 0; c < kSkCC; ++c) {
+        if (cb + 1 < n_chunks) load(c0 + kDCC);
+#pragma unroll
+        for (int c = 0; c < kDCC; ++c) {
+            const int ch = c0 + c;
+            if (ch >= cin) break;
 #pragma unroll
             for (int dy = 0; dy < 3; ++dy) {
-                const float *row = &halo[c * kSkHP + (r + dy) * kSkHW + cg * 4];
-                float v[6];
+                const float *row = &halo[(c * kDRows + r + dy) * kDRow + 4 * g + 3];
+                const floatx4 mid = *reinterpret_cast<const floatx4 *>(row + 1);
+                const float v[6] = {row[0], mid[0], mid[1], mid[2], mid[3], row[5]};
 #pragma unroll
-                for (int q = 0; q < 6; ++q) v[q] = row[q];
-#pragma unroll
-                for (int dx = 0; dx < 3; ++dx) {
+                for (int dx = 0; dx < 3; ++dx)
 #pragma unroll
                     for (int o = 0; o < COUT; ++o) {
-                        const float wv = wt[(o * kSkCC + c) * 9 + dy * 3 + dx];
+                        const float wv = w[((long long)o * cin + ch) * 9 + dy * 3 + dx];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[o][q] = fmaf(wv, v[q + dx], acc[o][q]);
+                        for (int e = 0; e < 4; ++e) acc[o][e] = fmaf(wv, v[e + dx], acc[o][e]);
                     }
-                }
             }
         }
         __syncthreads();
     }
     const int yy = y0 + r;
     if (yy >= H) return;
+    const int xx = x0 + 4 * g;
 #pragma unroll
-    for (int o = 0; o < COUT; ++o)
+    for (int o = 0; o < COUT; ++o) {
+        const float b = bias[o];
+        float *dst = y + o * plane + (long long)yy * W + xx;
+        if (vec_out) {
+            *reinterpret_cast<floatx4 *>(dst) = floatx4{acc[o][0] + b, acc[o][1] + b, acc[o][2] + b, acc[o][3] + b};
+        } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int xx = x0 + cg * 4 + q;
-            if (xx < W) y[(long long)o * plane + (long long)yy * W + xx] = acc[o][q] + bias[o];
+            for (int e = 0; e < 4; ++e)
+                if (xx + e < W) dst[e] = acc[o][e] + b;
         }
+    }
 }
 
 }  // namespace
@@ -764,26 +839,30 @@ int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s) {
     return launch_conv3x3_reduce(a, s);
 }
 
-int32_t launch_conv3x3_skinny(const float *x, const float *w, const float *bias, float *y, int cin,
+int32_t launch_conv3x3_direct(const float *x, const float *w, const float *bias, float *y, int cin,
                               int cout, int H, int W, hipStream_t s, const float *gn_coef) {
-    const int tiles_x = (W + kSkC - 1) / kSkC;
-    const int tiles_y = (H + kSkR - 1) / kSkR;
+    if (gn_coef && cin > kGnMaxChannels) {
+        set_error("conv3x3_direct: GroupNorm-on-load holds at most %d input channels", kGnMaxChannels);
+        return VAE_ERR_UNSUPPORTED;
+    }
+    const int tiles_x = (W + kDC - 1) / kDC;
+    const int tiles_y = (H + kDR - 1) / kDR;
     const dim3 grid((unsigned)(tiles_x * tiles_y));
-#define VAE_SKINNY(N)                                                                                         \
-    if (gn_coef)                                                                                              \
-        hipLaunchKernelGGL((conv3x3_skinny<N, true>), grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W,   \
-                           tiles_x, gn_coef);                                                                 \
-    else                                                                                                      \
-        hipLaunchKernelGGL((conv3x3_skinny<N, false>), grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W,  \
+#define VAE_DIRECT(N)                                                                                        \
+    if (gn_coef)                                                                                             \
+        hipLaunchKernelGGL((conv3x3_direct<N, true>), grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W,  \
+                           tiles_x, gn_coef);                                                                \
+    else                                                                                                     \
+        hipLaunchKernelGGL((conv3x3_direct<N, false>), grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W, \
                            tiles_x, gn_coef);
     switch (cout) {
-        case 1: VAE_SKINNY(1) break;
-        case 2: VAE_SKINNY(2) break;
-        case 3: VAE_SKINNY(3) break;
-        case 4: VAE_SKINNY(4) break;
-        default: set_error("conv3x3_skinny: out_channels %d > 4", cout); return VAE_ERR_UNSUPPORTED;
+        case 1: VAE_DIRECT(1) break;
+        case 2: VAE_DIRECT(2) break;
+        case 3: VAE_DIRECT(3) break;
+        case 4: VAE_DIRECT(4) break;
+        default: set_error("conv3x3_direct: out_channels %d > 4", cout); return VAE_ERR_UNSUPPORTED;
     }
-#undef VAE_SKINNY
-    return check_launch("conv3x3_skinny");
+#undef VAE_DIRECT
+    return check_launch("conv3x3_direct");
 }
 }  // namespace vae

@@ -600,18 +600,21 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
             std::swap(b.X, b.Y);
         }
     }
-    // norm_out + SiLU, conv_out: the normalised input is either materialised
-    // in T or applied while conv_out loads X
-    const bool fused = d->gn_fused;
+    // norm_out + SiLU, conv_out.  A conv_out with at most 4 outputs is bound
+    // by reading its input, so it always normalises while loading (only the
+    // statistics are computed before it); a wider conv_out follows the
+    // decoder's GroupNorm mode.
+    const DConv &c = d->conv_out;
+    const bool direct = c.cout <= 4 && c.cin <= kDirectGnMaxChannels;
+    const bool fused = direct || d->gn_fused;
     const float *cin_x = fused ? b.X : b.T;
     if (fused) r.gnc("conv_norm_out", d->norm_out, b.X, (long long)H * W, b.gn);
     else r.gn("conv_norm_out", d->norm_out, b.X, (long long)H * W, b.T, b.gn);
     if (r.rc == VAE_OK) {
-        const DConv &c = d->conv_out;
         if (c.cout <= 4) {
-            ProfEntry *e = r.begin("conv3x3_skinny", "conv_out", conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
+            ProfEntry *e = r.begin("conv3x3_direct", "conv_out", conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
             if (r.rc == VAE_OK) {
-                r.rc = launch_conv3x3_skinny(cin_x, c.w, c.b, rgb, c.cin, c.cout, H, W, r.s, fused ? b.coef : nullptr);
+                r.rc = launch_conv3x3_direct(cin_x, c.w, c.b, rgb, c.cin, c.cout, H, W, r.s, fused ? b.coef : nullptr);
                 r.end(e);
             }
         } else {

@@ -67,8 +67,10 @@ int conv3x3_gn_records(const ConvLaunch &a);
 // Name of the kernel instantiation launch_conv3x3 picks for `a`.
 const char *conv3x3_kernel_name(const ConvLaunch &a);
 
-// Direct conv for out_channels <= 4 (conv_out); gn_coef as in ConvLaunch (may be nullptr).
-int32_t launch_conv3x3_skinny(const float *x, const float *w, const float *bias, float *y,
+// Direct conv for out_channels <= 4 (conv_out); gn_coef as in ConvLaunch (may be nullptr,
+// else at most kDirectGnMaxChannels input channels).
+constexpr int kDirectGnMaxChannels = 512;
+int32_t launch_conv3x3_direct(const float *x, const float *w, const float *bias, float *y,
                               int cin, int cout, int H, int W, hipStream_t s,
                               const float *gn_coef = nullptr);
 

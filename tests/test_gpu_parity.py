@@ -126,11 +126,23 @@ def test_conv1x1(api, cin, cout, h, w, res):
 
 
 @pytest.mark.parametrize("cin,cout,h,w", [(128, 3, 64, 64), (128, 3, 37, 45), (64, 1, 10, 130), (32, 4, 9, 9),
-                                          (24, 2, 16, 16)])
-def test_conv_out_skinny(api, cin, cout, h, w):
+                                          (24, 2, 16, 16), (128, 3, 40, 256), (22, 3, 17, 131)])
+def test_conv_out_direct(api, cin, cout, h, w):
     x = vaegen.activation(6, "xo", (cin, h, w))
     wt, b = conv_params(6, "co", cin, cout, 3)
     y = api.conv2d(dev(x), dev(wt), dev(b), out=nan_like((cout, h, w)))
+    assert rel_err(host(y), oracle.conv2d(x, wt, b)) <= LAYER_TOL
+
+
+def test_conv_out_direct_unaligned(api):
+    # input and output views that start one float into their allocations
+    cin, cout, h, w = 32, 3, 24, 256
+    x = vaegen.activation(6, "xa", (cin, h, w))
+    wt, b = conv_params(6, "ca", cin, cout, 3)
+    xb = torch.empty(cin * h * w + 1, dtype=torch.float32, device="cuda")
+    xb[1:].copy_(dev(x).flatten())
+    yb = torch.full((cout * h * w + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    y = api.conv2d(xb[1:].view(cin, h, w), dev(wt), dev(b), out=yb[1:].view(cout, h, w))
     assert rel_err(host(y), oracle.conv2d(x, wt, b)) <= LAYER_TOL
 
 
