@@ -2,14 +2,23 @@
 // VaeAttnRef) on x [c, n], n = h*w tokens in row-major order:
 //   xn  = GroupNorm(x)                                   (gn_stats/gn_apply)
 //   QKV = Wqkv xn + bqkv,   Wqkv = [Wq; Wk; Wv]  [3c, c]  (one GEMM, [3c, n])
-//   S   = (Q^T K) / sqrt(c)                      [n, n]   (GEMM, A read KM)
-//   P   = softmax over each row of S                      (in place)
-//   O   = V P^T                                  [c, n]   (GEMM, B read NK)
+//   St  = (K^T Q) / sqrt(c)                      [n, n]   St[u, t] = score of query t, key u
+//   P   = softmax over u of St[:, t] for every query t
+//   O   = V P^T                                  [c, n]   O[:, t] = sum_u V[:, u] P[t, u]
 //   y   = x + Wo O + bo                                   (GEMM, residual epilogue)
 // The channel-major layout of the decoder's activations makes every product a
 // plain GEMM with no transposition in memory.
 //
-// Workspace: xn [c, n] | QKV [3c, n] | S [n, n] | O [c, n] | GroupNorm partials.
+// The softmax never gets a pass of its own.  The scores are produced
+// transposed, so the 32 scores of one query in an MFMA tile sit in one lane:
+// the score GEMM's epilogue reduces them to (max, sum of exp(s - max)) per
+// query and 128-key block; softmax_merge combines the blocks of every query
+// in a fixed order into (max, 1 / sum); and the P V GEMM exponentiates and
+// scales the scores as it loads them.  The n x n score matrix is written
+// once and read once.
+//
+// Workspace: xn [c, n] | QKV [3c, n] | St [n, n] | O [c, n] |
+//            column statistics [ceil(n/128)][n] x 2 | merged [n] x 2 | GroupNorm partials.
 
 #include "vae_internal.h"
 
@@ -17,14 +26,33 @@ namespace vae {
 
 namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// stat[t] = (m, 1/l): the online-softmax combination, in block order, of the
+// blocks' (max, sum exp(s - max)) for query t.
+__global__ __launch_bounds__(256) void softmax_merge(const floatx2 *__restrict__ colstat, int blocks, int n,
+                                                     floatx2 *__restrict__ stat) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= n) return;
+    float m = -INFINITY, l = 0.f;
+    for (int b = 0; b < blocks; ++b) {
+        const floatx2 v = colstat[(long long)b * n + t];
+        const float mn = fmaxf(m, v[0]);
+        l = l * __expf(m - mn) + v[1] * __expf(v[0] - mn);
+        m = mn;
+    }
+    stat[t] = floatx2{m, 1.0f / l};
+}
 }  // namespace
 
 size_t attention_ws_bytes(int c, long long n) {
+    const long long blocks = (n + 127) / 128;
     size_t b = 0;
     b += align256((size_t)c * n * 4);        // xn
     b += align256((size_t)3 * c * n * 4);    // qkv
-    b += align256((size_t)n * n * 4);        // S
+    b += align256((size_t)n * n * 4);        // St
     b += align256((size_t)c * n * 4);        // O
+    b += align256((size_t)blocks * n * 8);   // column statistics
+    b += align256((size_t)n * 8);            // merged statistics
     b += align256(groupnorm_ws_bytes(c, n)); // partials
     return b;
 }
@@ -33,15 +61,20 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
                          const float *gn_beta, const float *wqkv, const float *bqkv,
                          const float *wo, const float *bo, float *y, void *ws, hipStream_t s) {
     const long long n = (long long)h * w;
+    const int blocks = (int)((n + 127) / 128);
     char *p = static_cast<char *>(ws);
     float *xn = reinterpret_cast<float *>(p);
     p += align256((size_t)c * n * 4);
     float *qkv = reinterpret_cast<float *>(p);
     p += align256((size_t)3 * c * n * 4);
-    float *S = reinterpret_cast<float *>(p);
+    float *St = reinterpret_cast<float *>(p);
     p += align256((size_t)n * n * 4);
     float *O = reinterpret_cast<float *>(p);
     p += align256((size_t)c * n * 4);
+    float *colstat = reinterpret_cast<float *>(p);
+    p += align256((size_t)blocks * n * 8);
+    float *stat = reinterpret_cast<float *>(p);
+    p += align256((size_t)n * 8);
     void *gnws = p;
 
     int32_t rc = launch_groupnorm(x, c, n, gn_gamma, gn_beta, /*silu=*/0, nullptr, xn, gnws, s);
@@ -57,22 +90,26 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
     if ((rc = launch_gemm(g, s)) != VAE_OK) return rc;
 
     const float *Q = qkv, *K = qkv + (size_t)c * n, *V = qkv + (size_t)2 * c * n;
-    // S[t, u] = sum_ch Q[ch, t] K[ch, u] / sqrt(c)
+    // St[u, t] = sum_ch K[ch, u] Q[ch, t] / sqrt(c), with per-(key block, query) statistics
     g = GemmLaunch{};
-    g.A = Q; g.lda = n; g.a_km = 1;
-    g.B = K; g.ldb = n; g.b_nk = 0;
-    g.C = S; g.ldc = n;
+    g.A = K; g.lda = n; g.a_km = 1;
+    g.B = Q; g.ldb = n; g.b_nk = 0;
+    g.C = St; g.ldc = n;
     g.M = (int)n; g.N = (int)n; g.K = c; g.alpha = (float)(1.0 / sqrt((double)c));
+    g.colstat = colstat;
     if ((rc = launch_gemm(g, s)) != VAE_OK) return rc;
 
-    if ((rc = launch_softmax_rows(S, (int)n, (int)n, s)) != VAE_OK) return rc;
+    hipLaunchKernelGGL(softmax_merge, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const floatx2 *>(colstat), blocks, (int)n, reinterpret_cast<floatx2 *>(stat));
+    if ((rc = check_launch("softmax_merge")) != VAE_OK) return rc;
 
-    // O[ch, t] = sum_u V[ch, u] P[t, u]
+    // O[ch, t] = sum_u V[ch, u] P[t, u], P[t, u] = exp(St[u, t] - m_t) / l_t applied on load
     g = GemmLaunch{};
     g.A = V; g.lda = n; g.a_km = 0;
-    g.B = S; g.ldb = n; g.b_nk = 1;
+    g.B = St; g.ldb = n; g.b_nk = 0;
     g.C = O; g.ldc = n;
     g.M = c; g.N = (int)n; g.K = (int)n; g.alpha = 1.f;
+    g.bsoft = stat;
     if ((rc = launch_gemm(g, s)) != VAE_OK) return rc;
 
     // y = x + Wo O + bo

@@ -1,7 +1,7 @@
 // FP32-MFMA GEMM for the decoder's dense contractions that are not 3x3
 // convolutions: the 1x1 resnet shortcut (cortiq-engine 0.7.7 `vae`,
 // VaeResnetRef), and in the mid-block attention (VaeAttnRef) the q/k/v
-// projections, q . k^T, P . v and the output projection.
+// projections, the scores k^T q, P v and the output projection.
 //
 //   C[m, n] = alpha * sum_k A(m, k) * B(k, n) + bias[m] (+ R[m, n])
 //
@@ -10,7 +10,17 @@
 // 128 x 128 outputs per 256-thread workgroup, K in chunks of 16 staged in LDS
 // as [k][m] / [k][n] rows (double-buffered); each wave computes 64 x 64 as
 // 2 x 2 v_mfma_f32_32x32x2_f32 tiles.  Lane half h of a wave carries the K
-// indices [8h, 8h + 8) of a chunk.
+// indices [8h, 8h + 8) of a chunk.  When every tile is full (M, N multiples
+// of 128, K of 16, float4-aligned operands) the operand loads walk
+// precomputed pointers with no bounds checks.
+//
+// Two attention-only variants split a row softmax across the two products
+// that surround it (the score matrix is written once and read once):
+//   - EPI_COLSTAT: besides C, each workgroup writes for every column n of its
+//     tile the (max, sum of exp(c - max)) over its valid rows m, at
+//     colstat[blockIdx.y * N + n];
+//   - B_SOFTMAX: B(k, n) (KN) is replaced on load by exp(B(k, n) - mx[n]) *
+//     inv[n] with (mx, inv) = bsoft[n], the merged statistics of column n.
 
 #include "vae_internal.h"
 
@@ -23,9 +33,13 @@ constexpr int BM = 128, BN = 128, BK = 16;
 constexpr int LD = 132;   // row stride: 8 * 132 = 1056 = 32 (mod 64), lane halves split the banks
 static_assert((8 * LD) % 64 == 32 && LD % 4 == 0, "bad LDS stride");
 
+enum { EPI_STORE = 0, EPI_COLSTAT = 1 };
+
 struct Params {
     const float *A, *B, *bias, *R;
     float *C;
+    floatx2 *colstat;
+    const floatx2 *bsoft;
     int M, N, K;
     long long lda, ldb, ldc, ldr;
     float alpha;
@@ -68,6 +82,46 @@ __device__ __attribute__((always_inline)) inline void tile_load(const float *P, 
     }
 }
 
+// Full tiles: this thread's two element pointers, advanced by a fixed stride
+// after every K chunk.
+template <bool TRANS>
+__device__ __attribute__((always_inline)) inline void tile_ptrs(const float *P, long long ld, int i0,
+                                                                const float *(&ptr)[2]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int idx = tid + q * kThreads;
+        if (!TRANS) ptr[q] = P + (long long)(idx >> 5) * ld + i0 + (idx & 31) * 4;
+        else ptr[q] = P + (long long)(i0 + (idx >> 2)) * ld + (idx & 3) * 4;
+    }
+}
+
+__device__ __attribute__((always_inline)) inline void tile_load_full(const float *(&ptr)[2], long long step,
+                                                                     floatx4 (&r)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        r[q] = *reinterpret_cast<const floatx4 *>(ptr[q]);
+        ptr[q] += step;
+    }
+}
+
+// B_SOFTMAX: this thread's four columns n0 + (tid & 31) * 4 + e are the same
+// for every chunk; entries outside the matrix become 0.
+template <bool FULL>
+__device__ __attribute__((always_inline)) inline void softmax_on_load(floatx4 (&r)[2], int k0, int n,
+                                                                      int K, int N, const float (&mx)[4],
+                                                                      const float (&inv)[4]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int k = k0 + ((threadIdx.x + q * kThreads) >> 5);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p = __expf(r[q][e] - mx[e]) * inv[e];
+            r[q][e] = (FULL || (k < K && n + e < N)) ? p : 0.f;
+        }
+    }
+}
+
 template <bool TRANS>
 __device__ __attribute__((always_inline)) inline void tile_store(float *lds, const floatx4 (&r)[2]) {
     const int tid = threadIdx.x;
@@ -85,7 +139,7 @@ __device__ __attribute__((always_inline)) inline void tile_store(float *lds, con
     }
 }
 
-template <bool A_MK, bool B_NK, bool VEC, bool RES>
+template <bool A_MK, bool B_NK, bool VEC, bool RES, bool FULL, int EPI, bool BSM>
 __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
     __shared__ __attribute__((aligned(16))) float As[2][BK * LD];
     __shared__ __attribute__((aligned(16))) float Bs[2][BK * LD];
@@ -104,9 +158,30 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    float smx[4], sinv[4];
+    const int sn = n0 + (tid & 31) * 4;
+    if (BSM) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const floatx2 st = p.bsoft[sn + e < p.N ? sn + e : p.N - 1];
+            smx[e] = st[0];
+            sinv[e] = st[1];
+        }
+    }
+
     const int n_iter = (p.K + BK - 1) / BK;
-    tile_load<A_MK, VEC>(p.A, p.lda, 0, m0, p.K, p.M, ra);
-    tile_load<B_NK, VEC>(p.B, p.ldb, 0, n0, p.K, p.N, rb);
+    const float *pa[2], *pb[2];
+    const long long sa = A_MK ? BK : BK * p.lda, sb = B_NK ? BK : BK * p.ldb;
+    if (FULL) {
+        tile_ptrs<A_MK>(p.A, p.lda, m0, pa);
+        tile_ptrs<B_NK>(p.B, p.ldb, n0, pb);
+        tile_load_full(pa, sa, ra);
+        tile_load_full(pb, sb, rb);
+    } else {
+        tile_load<A_MK, VEC>(p.A, p.lda, 0, m0, p.K, p.M, ra);
+        tile_load<B_NK, VEC>(p.B, p.ldb, 0, n0, p.K, p.N, rb);
+    }
+    if (BSM) softmax_on_load<FULL>(rb, 0, sn, p.K, p.N, smx, sinv);
     tile_store<A_MK>(As[0], ra);
     tile_store<B_NK>(Bs[0], rb);
     __syncthreads();
@@ -116,8 +191,13 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
     for (int it = 0; it < n_iter; ++it) {
         const int buf = it & 1;
         if (it + 1 < n_iter) {
-            tile_load<A_MK, VEC>(p.A, p.lda, (it + 1) * BK, m0, p.K, p.M, ra);
-            tile_load<B_NK, VEC>(p.B, p.ldb, (it + 1) * BK, n0, p.K, p.N, rb);
+            if (FULL) {
+                tile_load_full(pa, sa, ra);
+                tile_load_full(pb, sb, rb);
+            } else {
+                tile_load<A_MK, VEC>(p.A, p.lda, (it + 1) * BK, m0, p.K, p.M, ra);
+                tile_load<B_NK, VEC>(p.B, p.ldb, (it + 1) * BK, n0, p.K, p.N, rb);
+            }
         }
         const float *a = As[buf];
         const float *b = Bs[buf];
@@ -131,12 +211,15 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
             acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
         }
         if (it + 1 < n_iter) {
+            if (BSM) softmax_on_load<FULL>(rb, (it + 1) * BK, sn, p.K, p.N, smx, sinv);
             tile_store<A_MK>(As[buf ^ 1], ra);
             tile_store<B_NK>(Bs[buf ^ 1], rb);
         }
         __syncthreads();
     }
 
+    // Epilogue: D[i][j] of a 32x32 MFMA tile sits in lane j + 32*((i/4)%2),
+    // register (i%4) + 4*(i/8).
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -151,22 +234,76 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
                     if (p.bias) v += p.bias[m];
                     if (RES) v += p.R[(long long)m * p.ldr + n];
                     p.C[(long long)m * p.ldc + n] = v;
+                    acc[i][j][r] = v;
                 }
             }
         }
     }
+    if (EPI == EPI_COLSTAT) {
+        // Column statistics over this tile's valid rows.  A lane holds 32 rows
+        // of each of its two columns; the other lane half and the other row
+        // wave hold the rest.  The staging buffers are free after the last
+        // barrier of the main loop.
+        float *red = As[0];          // [2 row waves][128 columns]: max, then sum
+        float *red2 = As[0] + 256;
+        float mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (FULL || m < p.M) {
+                    mx[0] = fmaxf(mx[0], acc[i][0][r]);
+                    mx[1] = fmaxf(mx[1], acc[i][1][r]);
+                }
+            }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], 32, 64));
+        if (half == 0) {
+            red[wm * 128 + wn * 64 + l32] = mx[0];
+            red[wm * 128 + wn * 64 + 32 + l32] = mx[1];
+        }
+        __syncthreads();
+        float cm[2], sm[2] = {0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int nl = wn * 64 + j * 32 + l32;
+            cm[j] = fmaxf(red[nl], red[128 + nl]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (FULL || m < p.M) {
+                    sm[0] += __expf(acc[i][0][r] - cm[0]);
+                    sm[1] += __expf(acc[i][1][r] - cm[1]);
+                }
+            }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sm[j] += __shfl_xor(sm[j], 32, 64);
+        if (half == 0) {
+            red2[wm * 128 + wn * 64 + l32] = sm[0];
+            red2[wm * 128 + wn * 64 + 32 + l32] = sm[1];
+        }
+        __syncthreads();
+        if (tid < BN && n0 + tid < p.N)
+            p.colstat[(long long)blockIdx.y * p.N + n0 + tid] =
+                floatx2{fmaxf(red[tid], red[128 + tid]), red2[tid] + red2[128 + tid]};
+    }
 }
 
-template <bool A_MK, bool B_NK, bool VEC>
-void launch3(const Params &p, bool res, dim3 grid, hipStream_t s) {
-    if (res) hipLaunchKernelGGL((gemm_mfma<A_MK, B_NK, VEC, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((gemm_mfma<A_MK, B_NK, VEC, false>), grid, dim3(kThreads), 0, s, p);
+template <bool A_MK, bool B_NK, bool VEC, bool FULL>
+void launch4(const Params &p, bool res, dim3 grid, hipStream_t s) {
+    if (res) hipLaunchKernelGGL((gemm_mfma<A_MK, B_NK, VEC, true, FULL, EPI_STORE, false>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((gemm_mfma<A_MK, B_NK, VEC, false, FULL, EPI_STORE, false>), grid, dim3(kThreads), 0, s, p);
 }
 
 template <bool A_MK, bool B_NK>
-void launch2(const Params &p, bool vec, bool res, dim3 grid, hipStream_t s) {
-    if (vec) launch3<A_MK, B_NK, true>(p, res, grid, s);
-    else launch3<A_MK, B_NK, false>(p, res, grid, s);
+void launch2(const Params &p, bool vec, bool full, bool res, dim3 grid, hipStream_t s) {
+    if (full) launch4<A_MK, B_NK, true, true>(p, res, grid, s);
+    else if (vec) launch4<A_MK, B_NK, true, false>(p, res, grid, s);
+    else launch4<A_MK, B_NK, false, false>(p, res, grid, s);
 }
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
@@ -180,6 +317,8 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
     p.bias = g.bias;
     p.R = g.R;
     p.C = g.C;
+    p.colstat = reinterpret_cast<floatx2 *>(g.colstat);
+    p.bsoft = reinterpret_cast<const floatx2 *>(g.bsoft);
     p.M = g.M;
     p.N = g.N;
     p.K = g.K;
@@ -197,14 +336,34 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
     const int b_contig = b_nk ? g.K : g.N;
     const bool vec = a_contig % 4 == 0 && b_contig % 4 == 0 && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
                      aligned16(g.A) && aligned16(g.B);
+    const bool full = vec && g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0;
     const dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
     const bool res = g.R != nullptr;
+    if (g.colstat || g.bsoft) {
+        // the two halves of the attention softmax: scores k^T q (A = k stored KM,
+        // B = q stored KN) and P v (A = v stored MK, B = the scores stored KN)
+        if (res || b_nk || (g.colstat && g.bsoft) || (g.colstat && a_mk) || (g.bsoft && !a_mk)) {
+            set_error("gemm: unsupported softmax-split configuration");
+            return VAE_ERR_UNSUPPORTED;
+        }
+#define VAE_GEMM_SM(AMK, E, B)                                                                                 \
+    if (full) hipLaunchKernelGGL((gemm_mfma<AMK, false, true, false, true, E, B>), grid, dim3(kThreads), 0, s, p); \
+    else if (vec) hipLaunchKernelGGL((gemm_mfma<AMK, false, true, false, false, E, B>), grid, dim3(kThreads), 0, s, p); \
+    else hipLaunchKernelGGL((gemm_mfma<AMK, false, false, false, false, E, B>), grid, dim3(kThreads), 0, s, p);
+        if (g.colstat) {
+            VAE_GEMM_SM(false, EPI_COLSTAT, false)
+        } else {
+            VAE_GEMM_SM(true, EPI_STORE, true)
+        }
+#undef VAE_GEMM_SM
+        return check_launch("gemm_mfma");
+    }
     if (a_mk) {
-        if (b_nk) launch2<true, true>(p, vec, res, grid, s);
-        else launch2<true, false>(p, vec, res, grid, s);
+        if (b_nk) launch2<true, true>(p, vec, full, res, grid, s);
+        else launch2<true, false>(p, vec, full, res, grid, s);
     } else {
-        if (b_nk) launch2<false, true>(p, vec, res, grid, s);
-        else launch2<false, false>(p, vec, res, grid, s);
+        if (b_nk) launch2<false, true>(p, vec, full, res, grid, s);
+        else launch2<false, false>(p, vec, full, res, grid, s);
     }
     return check_launch("gemm_mfma");
 }

@@ -1,8 +1,7 @@
 // GroupNorm(32, eps 1e-6, affine) + SiLU (cortiq-engine 0.7.7 `vae`,
 // GroupNorm / VaeNormRef; cortiq-engine 0.8.78 vae3d.rs GroupNorm::apply for
-// the statistics: group mean and biased variance), nearest x2 upsample
-// (VaeUpRef) and the row softmax of the attention scores (vae3d.rs
-// softmax_inplace: subtract the row max, exponentiate, divide by the sum).
+// the statistics: group mean and biased variance) and nearest x2 upsample
+// (VaeUpRef).
 //
 // GroupNorm runs as two HBM-streaming kernels.  gn_stats: a grid of
 // (parts, 32 groups) workgroups each reduces one contiguous slice of a group
@@ -280,62 +279,6 @@ __global__ void upsample2x_scalar(const float *__restrict__ x, float *__restrict
     y[i] = x[(c * h + (yy >> 1)) * w + (xx >> 1)];
 }
 
-// ------------------------------------------------------------- row softmax
-__device__ inline void merge_ms(float &m, float &s, float m2, float s2) {
-    const float mn = fmaxf(m, m2);
-    const float a = (m == -INFINITY) ? 0.f : s * __expf(m - mn);
-    const float b = (m2 == -INFINITY) ? 0.f : s2 * __expf(m2 - mn);
-    m = mn;
-    s = a + b;
-}
-
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void softmax_rows_kernel(float *S, int cols) {
-    __shared__ float sm[4], ss[4];
-    float *row = S + (long long)blockIdx.x * cols;
-    float m = -INFINITY, s = 0.f;
-    if (VEC) {
-        const floatx4 *r4 = reinterpret_cast<const floatx4 *>(row);
-        for (int i = threadIdx.x; i < cols / 4; i += kThreads) {
-            const floatx4 v = r4[i];
-            const float vm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-            const float vs = __expf(v[0] - vm) + __expf(v[1] - vm) + __expf(v[2] - vm) + __expf(v[3] - vm);
-            merge_ms(m, s, vm, vs);
-        }
-    } else {
-        for (int i = threadIdx.x; i < cols; i += kThreads) merge_ms(m, s, row[i], 1.f);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
-        merge_ms(m, s, m2, s2);
-    }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        sm[wave] = m;
-        ss[wave] = s;
-    }
-    __syncthreads();
-    m = sm[0];
-    s = ss[0];
-#pragma unroll
-    for (int wv = 1; wv < 4; ++wv) merge_ms(m, s, sm[wv], ss[wv]);
-    const float inv = 1.0f / s;
-    if (VEC) {
-        floatx4 *r4 = reinterpret_cast<floatx4 *>(row);
-        for (int i = threadIdx.x; i < cols / 4; i += kThreads) {
-            floatx4 v = r4[i];
-            v[0] = __expf(v[0] - m) * inv;
-            v[1] = __expf(v[1] - m) * inv;
-            v[2] = __expf(v[2] - m) * inv;
-            v[3] = __expf(v[3] - m) * inv;
-            r4[i] = v;
-        }
-    } else {
-        for (int i = threadIdx.x; i < cols; i += kThreads) row[i] = __expf(row[i] - m) * inv;
-    }
-}
-
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 size_t groupnorm_ws_bytes(int c, long long spatial) {
@@ -418,12 +361,5 @@ int32_t launch_upsample2x(const float *x, int c, int h, int w, float *y, hipStre
     return check_launch("upsample2x");
 }
 
-int32_t launch_softmax_rows(float *S, int rows, int cols, hipStream_t s) {
-    if (cols % 4 == 0 && aligned16(S))
-        hipLaunchKernelGGL(softmax_rows_kernel<true>, dim3(rows), dim3(kThreads), 0, s, S, cols);
-    else
-        hipLaunchKernelGGL(softmax_rows_kernel<false>, dim3(rows), dim3(kThreads), 0, s, S, cols);
-    return check_launch("softmax_rows");
-}
 
 }  // namespace vae

@@ -13,6 +13,7 @@ namespace vae {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ errors
 void set_error(const char *fmt, ...);
@@ -88,6 +89,10 @@ struct GemmLaunch {
     long long lda, ldb, ldc, ldr;
     int a_km, b_nk;
     float alpha;
+    // Row softmax split over two products (attention only; see gemm.hip):
+    float *colstat;        // if set: (max, sum exp(c - max)) of each column n over each 128-row block,
+                           // [ceil(M / 128)][N] pairs; needs a_km, KN B and no residual
+    const float *bsoft;    // if set: B(k, n) -> exp(B(k, n) - bsoft[2n]) * bsoft[2n + 1]; needs MK A, KN B
 };
 int32_t launch_gemm(const GemmLaunch &g, hipStream_t s);
 
@@ -107,7 +112,6 @@ int32_t launch_groupnorm_coef(const float *x, int c, long long spatial, const fl
 
 // ------------------------------------------------------------------ misc
 int32_t launch_upsample2x(const float *x, int c, int h, int w, float *y, hipStream_t s);
-int32_t launch_softmax_rows(float *S, int rows, int cols, hipStream_t s);
 
 // Attention on x [c, n] with packed qkv weights [3c, c] and bias [3c].
 size_t attention_ws_bytes(int c, long long n);

@@ -241,10 +241,24 @@ def test_upsample_exact(api, c, h, w):
 # attention
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("c,h,w", [(512, 8, 8), (64, 7, 9), (512, 32, 32), (128, 1, 1)])
+# token counts: one partial key block (64, 63, 1), two blocks with a ragged
+# tail (156), many full blocks (1024, 4096), many blocks with a ragged tail (1640)
+@pytest.mark.parametrize("c,h,w", [(512, 8, 8), (64, 7, 9), (512, 32, 32), (128, 1, 1), (64, 12, 13),
+                                   (512, 40, 41), (32, 64, 64)])
 def test_attention(api, c, h, w):
     p = vaegen.attention_params(10, "a", c)
     x = vaegen.activation(10, "xa", (c, h, w))
+    y = api.attention(dev(x), {k: dev(v) for k, v in p.items()}, "a", out=nan_like((c, h, w)))
+    assert rel_err(host(y), oracle.attention(x, p, "a")) <= LAYER_TOL
+
+
+def test_attention_peaked_softmax(api):
+    # queries scaled up 40x: scores span hundreds, so each query's softmax is
+    # dominated by a few keys spread over different key blocks
+    c, h, w = 64, 20, 20
+    p = vaegen.attention_params(13, "a", c)
+    p["a.to_q.weight"] = (p["a.to_q.weight"] * 40.0).astype(np.float32)
+    x = vaegen.activation(13, "xp", (c, h, w))
     y = api.attention(dev(x), {k: dev(v) for k, v in p.items()}, "a", out=nan_like((c, h, w)))
     assert rel_err(host(y), oracle.attention(x, p, "a")) <= LAYER_TOL
 
