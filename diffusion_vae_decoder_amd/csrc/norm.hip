@@ -189,51 +189,50 @@ __global__ __launch_bounds__(kThreads) void gn_coef(long long gsize, int cpg, in
     }
 }
 
-// Chan et al.'s pairwise update of (count, mean, M2): the statistics of the
-// union of two disjoint sets from those of each.
-struct Moments {
-    double n, mean, m2;
-};
-__device__ inline Moments merge_moments(Moments a, Moments b) {
-    if (b.n == 0.0) return a;
-    if (a.n == 0.0) return b;
-    const double n = a.n + b.n;
-    const double d = b.mean - a.mean;
-    return {n, a.mean + d * (b.n / n), a.m2 + b.m2 + d * d * (a.n * b.n / n)};
-}
-__device__ inline Moments shfl_down_moments(Moments m, int o) {
-    return {__shfl_down(m.n, o, 64), __shfl_down(m.mean, o, 64), __shfl_down(m.m2, o, 64)};
-}
-
-// One workgroup per group merges the group's records in a fixed order (a
-// strided sequential pass per thread, then a fixed tree), and stores the
-// result in the partial-sum form gn_apply and gn_coef read with one part:
-// shift = mean, sum d = 0, sum d^2 = M2.
+// One workgroup per group merges the group's records (count n, mean m, M2)
+// into float64 sums S0 = sum n, S1 = sum n m and S2 = sum (M2 + n m^2), in a
+// fixed order (a strided pass per thread, then a fixed tree), and stores
+// them in the partial-sum form gn_apply and gn_coef read with one part:
+// shift = S1 / S0, sum d = 0, sum d^2 = S2 - S1^2 / S0.  The records' own
+// centring keeps M2 accurate in float32; the float64 sums then lose nothing
+// to cancellation unless the mean exceeds the spread by ~1e6.
 __global__ __launch_bounds__(kThreads) void gn_merge(const floatx4 *__restrict__ rec, int nrec,
                                                      double *__restrict__ part, double *__restrict__ shift_out) {
     __shared__ double sh[3 * 4];
     const int g = blockIdx.x;
     const floatx4 *r = rec + (long long)g * nrec;
-    Moments m{0.0, 0.0, 0.0};
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+#pragma unroll 4
     for (int i = threadIdx.x; i < nrec; i += kThreads) {
         const floatx4 v = r[i];
-        m = merge_moments(m, Moments{(double)v[0], (double)v[1], (double)v[2]});
+        const double n = v[0], m = v[1];
+        s0 += n;
+        s1 += n * m;
+        s2 += (double)v[2] + n * m * m;
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = merge_moments(m, shfl_down_moments(m, o));
+    for (int o = 32; o > 0; o >>= 1) {
+        s0 += __shfl_down(s0, o, 64);
+        s1 += __shfl_down(s1, o, 64);
+        s2 += __shfl_down(s2, o, 64);
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) {
-        sh[3 * wave] = m.n;
-        sh[3 * wave + 1] = m.mean;
-        sh[3 * wave + 2] = m.m2;
+        sh[3 * wave] = s0;
+        sh[3 * wave + 1] = s1;
+        sh[3 * wave + 2] = s2;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        Moments t{sh[0], sh[1], sh[2]};
-        for (int w = 1; w < 4; ++w) t = merge_moments(t, Moments{sh[3 * w], sh[3 * w + 1], sh[3 * w + 2]});
+        const double n = (sh[0] + sh[3]) + (sh[6] + sh[9]);
+        const double t1 = (sh[1] + sh[4]) + (sh[7] + sh[10]);
+        const double t2 = (sh[2] + sh[5]) + (sh[8] + sh[11]);
+        const double mean = t1 / n;
+        double m2 = t2 - t1 * mean;
+        if (m2 < 0.0) m2 = 0.0;
         part[2 * g] = 0.0;
-        part[2 * g + 1] = t.m2;
-        shift_out[g] = t.mean;
+        part[2 * g + 1] = m2;
+        shift_out[g] = mean;
     }
 }
 
