@@ -18,7 +18,8 @@
 // once and read once.
 //
 // Workspace: xn [c, n] | QKV [3c, n] | St [n, n] | O [c, n] |
-//            column statistics [ceil(n/128)][n] x 2 | merged [n] x 2 | GroupNorm partials.
+//            column statistics [ceil(n/128)][n] x 2 | merged [n] x 2 | GroupNorm partials |
+//            K-split partial sums of the small products.
 
 #include "vae_internal.h"
 
@@ -26,6 +27,15 @@ namespace vae {
 
 namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t split_floats(int c, long long n) {
+    size_t f = gemm_partial_floats(3 * c, (int)n, c, false);
+    const size_t pv = gemm_partial_floats(c, (int)n, (int)n, false);
+    const size_t out = gemm_partial_floats(c, (int)n, c, false);
+    if (pv > f) f = pv;
+    if (out > f) f = out;
+    return f;
+}
 
 // stat[t] = (m, 1/l): the online-softmax combination, in block order, of the
 // blocks' (max, sum exp(s - max)) for query t.
@@ -53,7 +63,8 @@ size_t attention_ws_bytes(int c, long long n) {
     b += align256((size_t)c * n * 4);        // O
     b += align256((size_t)blocks * n * 8);   // column statistics
     b += align256((size_t)n * 8);            // merged statistics
-    b += align256(groupnorm_ws_bytes(c, n)); // partials
+    b += align256(groupnorm_ws_bytes(c, n)); // GroupNorm partials
+    b += align256(split_floats(c, n) * 4);   // K-split partial sums
     return b;
 }
 
@@ -76,6 +87,8 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
     float *stat = reinterpret_cast<float *>(p);
     p += align256((size_t)n * 8);
     void *gnws = p;
+    p += align256(groupnorm_ws_bytes(c, n));
+    float *part = reinterpret_cast<float *>(p);
 
     int32_t rc = launch_groupnorm(x, c, n, gn_gamma, gn_beta, /*silu=*/0, nullptr, xn, gnws, s);
     if (rc != VAE_OK) return rc;
@@ -87,6 +100,7 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
     g.bias = bqkv; g.R = nullptr;
     g.C = qkv; g.ldc = n;
     g.M = 3 * c; g.N = (int)n; g.K = c; g.alpha = 1.f;
+    g.part = part;
     if ((rc = launch_gemm(g, s)) != VAE_OK) return rc;
 
     const float *Q = qkv, *K = qkv + (size_t)c * n, *V = qkv + (size_t)2 * c * n;
@@ -110,6 +124,7 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
     g.C = O; g.ldc = n;
     g.M = c; g.N = (int)n; g.K = (int)n; g.alpha = 1.f;
     g.bsoft = stat;
+    g.part = part;
     if ((rc = launch_gemm(g, s)) != VAE_OK) return rc;
 
     // y = x + Wo O + bo
@@ -119,6 +134,7 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
     g.bias = bo; g.R = x; g.ldr = n;
     g.C = y; g.ldc = n;
     g.M = c; g.N = (int)n; g.K = c; g.alpha = 1.f;
+    g.part = part;
     return launch_gemm(g, s);
 }
 

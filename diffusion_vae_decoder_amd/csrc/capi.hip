@@ -3,6 +3,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 
 #include "vae_internal.h"
@@ -79,7 +80,11 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Workspace of a 3x3 conv producing [cout, T, H, W]: the repacked weights, then
 // the split-K partial sums (if the shape is split).
 size_t conv_ws(const vae_conv *c, int kt, int T, int H, int W) {
-    if (c->kernel == 1) return 0;
+    if (c->kernel == 1) return gemm_partial_floats(c->out_channels, H * W, c->in_channels, false) * sizeof(float);
+    if (kt == 1 && c->out_channels <= 4)   // direct kernel (or, with upsample / residual, the implicit GEMM)
+        return std::max(conv3x3_direct_partial_floats(c->out_channels, c->in_channels, H, W) * sizeof(float),
+                        align256(conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float)) +
+                            conv3x3_partial_floats(c->out_channels, c->in_channels, kt, H, W, T) * sizeof(float));
     return align256(conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float)) +
            conv3x3_partial_floats(c->out_channels, c->in_channels, kt, H, W, T) * sizeof(float);
 }
@@ -129,11 +134,19 @@ int32_t vae_conv2d(const float *x, int32_t cin, int32_t h, int32_t w, const vae_
         g.bias = conv->bias; g.R = residual; g.ldr = (long long)h * w;
         g.C = y; g.ldc = (long long)h * w;
         g.M = conv->out_channels; g.N = h * w; g.K = cin; g.alpha = 1.f;
+        const size_t need = conv_ws(conv, 1, 1, h, w);
+        if (need && (!ws || ws_bytes < need))
+            return set_error("vae_conv2d: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
+        g.part = static_cast<float *>(ws);
         return launch_gemm(g, s);
     }
-    if (conv->out_channels <= 4 && !upsample2x && !residual)
-        return launch_conv3x3_direct(x, conv->weight, conv->bias, y, cin, conv->out_channels, h, w, s);
     const size_t need = conv_ws(conv, 1, 1, H, W);
+    if (conv->out_channels <= 4 && !upsample2x && !residual) {
+        if (need && (!ws || ws_bytes < need))
+            return set_error("vae_conv2d: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
+        return launch_conv3x3_direct(x, conv->weight, conv->bias, y, cin, conv->out_channels, h, w, s, nullptr,
+                                     static_cast<float *>(ws));
+    }
     if (!ws || ws_bytes < need)
         return set_error("vae_conv2d: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
     if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 1, static_cast<float *>(ws), s))) return rc;

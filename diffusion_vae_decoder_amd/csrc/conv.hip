@@ -529,13 +529,17 @@ constexpr int kDQuads = kDCC * kDRows * (kDC / 4);            // float4 items pe
 constexpr int kDQPerT = (kDQuads + kThreads - 1) / kThreads;  // 5
 constexpr int kDEdges = kDCC * kDRows * 2;                    // scalar edge items per chunk (80)
 
+// blockIdx.y = split: with several splits, split s sums the chunks
+// [s * n / splits, (s + 1) * n / splits) into part[s] (no bias) and
+// splitk_reduce adds the splits in order.
 template <int COUT, bool GN>
 __global__ __launch_bounds__(kThreads) void conv3x3_direct(const float *__restrict__ x,
                                                            const float *__restrict__ w,
                                                            const float *__restrict__ bias,
                                                            float *__restrict__ y, int cin, int H,
                                                            int W, int tiles_x,
-                                                           const float *__restrict__ gn_coef) {
+                                                           const float *__restrict__ gn_coef,
+                                                           float *__restrict__ part) {
     __shared__ __attribute__((aligned(16))) float halo[kDCC * kDRows * kDRow];
     __shared__ float lc[GN ? 3 * (kGnMaxChannels + kDCC) : 1];
     const int tid = threadIdx.x;
@@ -545,8 +549,11 @@ __global__ __launch_bounds__(kThreads) void conv3x3_direct(const float *__restri
     const long long plane = (long long)H * W;
     // interior columns of this tile all inside the image and rows 16-byte aligned
     const bool vec = (W & 3) == 0 && x0 + kDC <= W && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-    const bool vec_out = (W & 3) == 0 && x0 + kDC <= W && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+    const bool vec_out = (W & 3) == 0 && x0 + kDC <= W &&
+                         (reinterpret_cast<uintptr_t>(part ? part : y) & 15) == 0;
     const int n_chunks = (cin + kDCC - 1) / kDCC;
+    const int cb0 = (int)((long long)blockIdx.y * n_chunks / gridDim.y);
+    const int cb1 = (int)((long long)(blockIdx.y + 1) * n_chunks / gridDim.y);
 
     if (GN) {
         for (int e = tid; e < 3 * n_chunks * kDCC; e += kThreads) {
@@ -627,12 +634,12 @@ __global__ __launch_bounds__(kThreads) void conv3x3_direct(const float *__restri
         for (int e = 0; e < 4; ++e) acc[o][e] = 0.f;
 
     if (GN) __syncthreads();   // coefficient table
-    load(0);
-    for (int cb = 0; cb < n_chunks; ++cb) {
+    load(cb0 * kDCC);
+    for (int cb = cb0; cb < cb1; ++cb) {
         const int c0 = cb * kDCC;
         store();
         __syncthreads();
-        if (cb + 1 < n_chunks) load(c0 + kDCC);
+        if (cb + 1 < cb1) load(c0 + kDCC);
 #pragma unroll
         for (int c = 0; c < kDCC; ++c) {
             const int ch = c0 + c;
@@ -657,10 +664,11 @@ __global__ __launch_bounds__(kThreads) void conv3x3_direct(const float *__restri
     const int yy = y0 + r;
     if (yy >= H) return;
     const int xx = x0 + 4 * g;
+    float *out = part ? part + (long long)blockIdx.y * COUT * plane : y;
 #pragma unroll
     for (int o = 0; o < COUT; ++o) {
-        const float b = bias[o];
-        float *dst = y + o * plane + (long long)yy * W + xx;
+        const float b = part ? 0.f : bias[o];
+        float *dst = out + o * plane + (long long)yy * W + xx;
         if (vec_out) {
             *reinterpret_cast<floatx4 *>(dst) = floatx4{acc[o][0] + b, acc[o][1] + b, acc[o][2] + b, acc[o][3] + b};
         } else {
@@ -839,22 +847,47 @@ int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s) {
     return launch_conv3x3_reduce(a, s);
 }
 
+namespace {
+constexpr int kDirectSlots = 1024;   // about 4 conv_out workgroups per CU
+}
+
+int conv3x3_direct_splits(int cin, int H, int W) {
+    const long long tiles = (long long)((W + kDC - 1) / kDC) * ((H + kDR - 1) / kDR);
+    const int n_chunks = (cin + kDCC - 1) / kDCC;
+    if (tiles * 2 >= kDirectSlots) return 1;
+    long long s = (kDirectSlots + tiles - 1) / tiles;
+    if (s > n_chunks / 4) s = n_chunks / 4;   // each split keeps >= 4 chunks (16 channels)
+    if (s > 16) s = 16;
+    return s < 2 ? 1 : (int)s;
+}
+
+size_t conv3x3_direct_partial_floats(int cout, int cin, int H, int W) {
+    const int sp = conv3x3_direct_splits(cin, H, W);
+    return sp > 1 ? (size_t)sp * cout * H * W : 0;
+}
+
 int32_t launch_conv3x3_direct(const float *x, const float *w, const float *bias, float *y, int cin,
-                              int cout, int H, int W, hipStream_t s, const float *gn_coef) {
+                              int cout, int H, int W, hipStream_t s, const float *gn_coef, float *part) {
     if (gn_coef && cin > kGnMaxChannels) {
         set_error("conv3x3_direct: GroupNorm-on-load holds at most %d input channels", kGnMaxChannels);
         return VAE_ERR_UNSUPPORTED;
     }
+    const int splits = conv3x3_direct_splits(cin, H, W);
+    if (splits > 1 && !part) {
+        set_error("conv3x3_direct: a split shape needs a partial-sum workspace");
+        return VAE_ERR_WORKSPACE;
+    }
+    float *pp = splits > 1 ? part : nullptr;
     const int tiles_x = (W + kDC - 1) / kDC;
     const int tiles_y = (H + kDR - 1) / kDR;
-    const dim3 grid((unsigned)(tiles_x * tiles_y));
+    const dim3 grid((unsigned)(tiles_x * tiles_y), (unsigned)splits);
 #define VAE_DIRECT(N)                                                                                        \
     if (gn_coef)                                                                                             \
         hipLaunchKernelGGL((conv3x3_direct<N, true>), grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W,  \
-                           tiles_x, gn_coef);                                                                \
+                           tiles_x, gn_coef, pp);                                                            \
     else                                                                                                     \
         hipLaunchKernelGGL((conv3x3_direct<N, false>), grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W, \
-                           tiles_x, gn_coef);
+                           tiles_x, gn_coef, pp);
     switch (cout) {
         case 1: VAE_DIRECT(1) break;
         case 2: VAE_DIRECT(2) break;
@@ -863,6 +896,18 @@ int32_t launch_conv3x3_direct(const float *x, const float *w, const float *bias,
         default: set_error("conv3x3_direct: out_channels %d > 4", cout); return VAE_ERR_UNSUPPORTED;
     }
 #undef VAE_DIRECT
-    return check_launch("conv3x3_direct");
+    int32_t rc = check_launch("conv3x3_direct");
+    if (rc != VAE_OK || splits == 1) return rc;
+    const long long plane = (long long)H * W;
+    const dim3 rgrid((unsigned)((plane + kRedElems - 1) / kRedElems), (unsigned)cout);
+    const bool vec = plane % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(part) & 15) == 0;
+    if (vec)
+        hipLaunchKernelGGL((splitk_reduce<true, false>), rgrid, dim3(kThreads), 0, s, part, plane * cout, splits,
+                           bias, nullptr, y, plane, nullptr, 0);
+    else
+        hipLaunchKernelGGL((splitk_reduce<false, false>), rgrid, dim3(kThreads), 0, s, part, plane * cout, splits,
+                           bias, nullptr, y, plane, nullptr, 0);
+    return check_launch("splitk_reduce");
 }
 }  // namespace vae

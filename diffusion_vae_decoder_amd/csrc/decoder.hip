@@ -277,6 +277,10 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
     act(d->conv_in.cout, H, W);
     part(d->conv_in, H, W);
     auto res = [&](const DRes &r) {
+        if (r.sc.present) {
+            const size_t n = gemm_partial_floats(r.sc.cout, (int)(H * W), r.sc.cin, false);
+            if (n > p.part) p.part = n;
+        }
         gn(r.c1.cin, H, W);
         gn(r.c1.cout, H, W);
         act(r.c1.cin, H, W);
@@ -297,6 +301,12 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
         }
     }
     gn(d->norm_out.c, H, W);
+    if (d->conv_out.cout <= 4) {
+        const size_t n = conv3x3_direct_partial_floats(d->conv_out.cout, d->conv_out.cin, (int)H, (int)W);
+        if (n > p.part) p.part = n;
+    } else {
+        part(d->conv_out, H, W);
+    }
     return p;
 }
 
@@ -399,6 +409,7 @@ struct Runner {
         g.N = H * W;
         g.K = c.cin;
         g.alpha = 1.f;
+        g.part = part;
         ProfEntry *e = begin("gemm_mfma", layer, conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
         if (rc != VAE_OK) return;
         rc = launch_gemm(g, s);
@@ -614,7 +625,8 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
         if (c.cout <= 4) {
             ProfEntry *e = r.begin("conv3x3_direct", "conv_out", conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
             if (r.rc == VAE_OK) {
-                r.rc = launch_conv3x3_direct(cin_x, c.w, c.b, rgb, c.cin, c.cout, H, W, r.s, fused ? b.coef : nullptr);
+                r.rc = launch_conv3x3_direct(cin_x, c.w, c.b, rgb, c.cin, c.cout, H, W, r.s, fused ? b.coef : nullptr,
+                                             b.part);
                 r.end(e);
             }
         } else {

@@ -14,6 +14,10 @@
 // of 128, K of 16, float4-aligned operands) the operand loads walk
 // precomputed pointers with no bounds checks.
 //
+// Problems whose tiles cannot fill the GPU (the small attentions) split K
+// into ranges of at least 8 chunks; each split stores raw partial sums and
+// gemm_splitk_reduce adds them in split order with alpha, bias and residual.
+//
 // Two attention-only variants split a row softmax across the two products
 // that surround it (the score matrix is written once and read once):
 //   - EPI_COLSTAT: besides C, each workgroup writes for every column n of its
@@ -40,7 +44,8 @@ struct Params {
     float *C;
     floatx2 *colstat;
     const floatx2 *bsoft;
-    int M, N, K;
+    float *part;       // split K: partial sums [ksplit][M][N]
+    int M, N, K, ksplit;
     long long lda, ldb, ldc, ldr;
     float alpha;
 };
@@ -139,7 +144,7 @@ __device__ __attribute__((always_inline)) inline void tile_store(float *lds, con
     }
 }
 
-template <bool A_MK, bool B_NK, bool VEC, bool RES, bool FULL, int EPI, bool BSM>
+template <bool A_MK, bool B_NK, bool VEC, bool RES, bool FULL, int EPI, bool BSM, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
     __shared__ __attribute__((aligned(16))) float As[2][BK * LD];
     __shared__ __attribute__((aligned(16))) float Bs[2][BK * LD];
@@ -169,19 +174,30 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
         }
     }
 
-    const int n_iter = (p.K + BK - 1) / BK;
+    // K chunks [c0, c1) of this workgroup (all of them unless K is split)
+    const int n_chunks = (p.K + BK - 1) / BK;
+    const int split = SPLIT ? blockIdx.z : 0;
+    const int c0 = SPLIT ? (int)((long long)split * n_chunks / p.ksplit) : 0;
+    const int c1 = SPLIT ? (int)((long long)(split + 1) * n_chunks / p.ksplit) : n_chunks;
+    const int n_iter = c1 - c0;
+    const int kb = c0 * BK;
     const float *pa[2], *pb[2];
     const long long sa = A_MK ? BK : BK * p.lda, sb = B_NK ? BK : BK * p.ldb;
     if (FULL) {
         tile_ptrs<A_MK>(p.A, p.lda, m0, pa);
         tile_ptrs<B_NK>(p.B, p.ldb, n0, pb);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            pa[q] += (long long)c0 * sa;
+            pb[q] += (long long)c0 * sb;
+        }
         tile_load_full(pa, sa, ra);
         tile_load_full(pb, sb, rb);
     } else {
-        tile_load<A_MK, VEC>(p.A, p.lda, 0, m0, p.K, p.M, ra);
-        tile_load<B_NK, VEC>(p.B, p.ldb, 0, n0, p.K, p.N, rb);
+        tile_load<A_MK, VEC>(p.A, p.lda, kb, m0, p.K, p.M, ra);
+        tile_load<B_NK, VEC>(p.B, p.ldb, kb, n0, p.K, p.N, rb);
     }
-    if (BSM) softmax_on_load<FULL>(rb, 0, sn, p.K, p.N, smx, sinv);
+    if (BSM) softmax_on_load<FULL>(rb, kb, sn, p.K, p.N, smx, sinv);
     tile_store<A_MK>(As[0], ra);
     tile_store<B_NK>(Bs[0], rb);
     __syncthreads();
@@ -195,8 +211,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
                 tile_load_full(pa, sa, ra);
                 tile_load_full(pb, sb, rb);
             } else {
-                tile_load<A_MK, VEC>(p.A, p.lda, (it + 1) * BK, m0, p.K, p.M, ra);
-                tile_load<B_NK, VEC>(p.B, p.ldb, (it + 1) * BK, n0, p.K, p.N, rb);
+                tile_load<A_MK, VEC>(p.A, p.lda, kb + (it + 1) * BK, m0, p.K, p.M, ra);
+                tile_load<B_NK, VEC>(p.B, p.ldb, kb + (it + 1) * BK, n0, p.K, p.N, rb);
             }
         }
         const float *a = As[buf];
@@ -211,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
             acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
         }
         if (it + 1 < n_iter) {
-            if (BSM) softmax_on_load<FULL>(rb, (it + 1) * BK, sn, p.K, p.N, smx, sinv);
+            if (BSM) softmax_on_load<FULL>(rb, kb + (it + 1) * BK, sn, p.K, p.N, smx, sinv);
             tile_store<A_MK>(As[buf ^ 1], ra);
             tile_store<B_NK>(Bs[buf ^ 1], rb);
         }
@@ -229,7 +245,9 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                if (m < p.M) {
+                if (m < p.M && SPLIT) {
+                    p.part[((long long)split * p.M + m) * p.N + n] = acc[i][j][r];
+                } else if (m < p.M) {
                     float v = p.alpha * acc[i][j][r];
                     if (p.bias) v += p.bias[m];
                     if (RES) v += p.R[(long long)m * p.ldr + n];
@@ -293,10 +311,25 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
     }
 }
 
+// C[m, n] = alpha * sum_s part[s, m, n] (split order) + bias[m] (+ R[m, n]).
+__global__ __launch_bounds__(kThreads) void gemm_splitk_reduce(Params p) {
+    const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+    const long long mn = (long long)p.M * p.N;
+    if (i >= mn) return;
+    const int m = (int)(i / p.N), n = (int)(i - (long long)m * p.N);
+    float t = 0.f;
+    for (int sp = 0; sp < p.ksplit; ++sp) t += p.part[sp * mn + i];
+    float v = p.alpha * t;
+    if (p.bias) v += p.bias[m];
+    if (p.R) v += p.R[(long long)m * p.ldr + n];
+    p.C[(long long)m * p.ldc + n] = v;
+}
+
 template <bool A_MK, bool B_NK, bool VEC, bool FULL>
 void launch4(const Params &p, bool res, dim3 grid, hipStream_t s) {
-    if (res) hipLaunchKernelGGL((gemm_mfma<A_MK, B_NK, VEC, true, FULL, EPI_STORE, false>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((gemm_mfma<A_MK, B_NK, VEC, false, FULL, EPI_STORE, false>), grid, dim3(kThreads), 0, s, p);
+    if (p.ksplit > 1) hipLaunchKernelGGL((gemm_mfma<A_MK, B_NK, VEC, false, FULL, EPI_STORE, false, true>), grid, dim3(kThreads), 0, s, p);
+    else if (res) hipLaunchKernelGGL((gemm_mfma<A_MK, B_NK, VEC, true, FULL, EPI_STORE, false, false>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((gemm_mfma<A_MK, B_NK, VEC, false, FULL, EPI_STORE, false, false>), grid, dim3(kThreads), 0, s, p);
 }
 
 template <bool A_MK, bool B_NK>
@@ -308,7 +341,24 @@ void launch2(const Params &p, bool vec, bool full, bool res, dim3 grid, hipStrea
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
+constexpr int kSlots = 256 * 3;   // CUs x resident GEMM workgroups per CU
+
 }  // namespace
+
+int gemm_ksplit(int M, int N, int K, bool colstat) {
+    const long long tiles = (long long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (colstat || tiles * 2 >= kSlots) return 1;
+    const int n_chunks = (K + BK - 1) / BK;
+    long long s = (kSlots + tiles - 1) / tiles;
+    if (s > n_chunks / 8) s = n_chunks / 8;   // each split keeps >= 8 K chunks
+    if (s > 16) s = 16;
+    return s < 2 ? 1 : (int)s;
+}
+
+size_t gemm_partial_floats(int M, int N, int K, bool colstat) {
+    const int s = gemm_ksplit(M, N, K, colstat);
+    return s > 1 ? (size_t)s * M * N : 0;
+}
 
 int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
     Params p;
@@ -318,6 +368,12 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
     p.R = g.R;
     p.C = g.C;
     p.colstat = reinterpret_cast<floatx2 *>(g.colstat);
+    p.part = g.part;
+    p.ksplit = gemm_ksplit(g.M, g.N, g.K, g.colstat != nullptr);
+    if (p.ksplit > 1 && !g.part) {
+        set_error("gemm: a K-split shape needs a partial-sum workspace");
+        return VAE_ERR_WORKSPACE;
+    }
     p.bsoft = reinterpret_cast<const floatx2 *>(g.bsoft);
     p.M = g.M;
     p.N = g.N;
@@ -337,7 +393,7 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
     const bool vec = a_contig % 4 == 0 && b_contig % 4 == 0 && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
                      aligned16(g.A) && aligned16(g.B);
     const bool full = vec && g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0;
-    const dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
+    const dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)p.ksplit);
     const bool res = g.R != nullptr;
     if (g.colstat || g.bsoft) {
         // the two halves of the attention softmax: scores k^T q (A = k stored KM,
@@ -346,26 +402,30 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
             set_error("gemm: unsupported softmax-split configuration");
             return VAE_ERR_UNSUPPORTED;
         }
-#define VAE_GEMM_SM(AMK, E, B)                                                                                 \
-    if (full) hipLaunchKernelGGL((gemm_mfma<AMK, false, true, false, true, E, B>), grid, dim3(kThreads), 0, s, p); \
-    else if (vec) hipLaunchKernelGGL((gemm_mfma<AMK, false, true, false, false, E, B>), grid, dim3(kThreads), 0, s, p); \
-    else hipLaunchKernelGGL((gemm_mfma<AMK, false, false, false, false, E, B>), grid, dim3(kThreads), 0, s, p);
+#define VAE_GEMM_SM(AMK, E, B, S)                                                                                 \
+    if (full) hipLaunchKernelGGL((gemm_mfma<AMK, false, true, false, true, E, B, S>), grid, dim3(kThreads), 0, s, p); \
+    else if (vec) hipLaunchKernelGGL((gemm_mfma<AMK, false, true, false, false, E, B, S>), grid, dim3(kThreads), 0, s, p); \
+    else hipLaunchKernelGGL((gemm_mfma<AMK, false, false, false, false, E, B, S>), grid, dim3(kThreads), 0, s, p);
         if (g.colstat) {
-            VAE_GEMM_SM(false, EPI_COLSTAT, false)
+            VAE_GEMM_SM(false, EPI_COLSTAT, false, false)
+        } else if (p.ksplit > 1) {
+            VAE_GEMM_SM(true, EPI_STORE, true, true)
         } else {
-            VAE_GEMM_SM(true, EPI_STORE, true)
+            VAE_GEMM_SM(true, EPI_STORE, true, false)
         }
 #undef VAE_GEMM_SM
-        return check_launch("gemm_mfma");
-    }
-    if (a_mk) {
+    } else if (a_mk) {
         if (b_nk) launch2<true, true>(p, vec, full, res, grid, s);
         else launch2<true, false>(p, vec, full, res, grid, s);
     } else {
         if (b_nk) launch2<false, true>(p, vec, full, res, grid, s);
         else launch2<false, false>(p, vec, full, res, grid, s);
     }
-    return check_launch("gemm_mfma");
+    int32_t rc = check_launch("gemm_mfma");
+    if (rc != VAE_OK || p.ksplit == 1) return rc;
+    const long long mn = (long long)g.M * g.N;
+    hipLaunchKernelGGL(gemm_splitk_reduce, dim3((unsigned)((mn + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, p);
+    return check_launch("gemm_splitk_reduce");
 }
 
 }  // namespace vae

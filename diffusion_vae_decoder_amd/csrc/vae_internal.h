@@ -71,9 +71,12 @@ const char *conv3x3_kernel_name(const ConvLaunch &a);
 // Direct conv for out_channels <= 4 (conv_out); gn_coef as in ConvLaunch (may be nullptr,
 // else at most kDirectGnMaxChannels input channels).
 constexpr int kDirectGnMaxChannels = 512;
+// Shapes with too few tiles split the input channels; the partial sums then
+// need conv3x3_direct_partial_floats() floats in `part`.
 int32_t launch_conv3x3_direct(const float *x, const float *w, const float *bias, float *y,
                               int cin, int cout, int H, int W, hipStream_t s,
-                              const float *gn_coef = nullptr);
+                              const float *gn_coef, float *part);
+size_t conv3x3_direct_partial_floats(int cout, int cin, int H, int W);
 
 // ------------------------------------------------------------------ GEMM
 // C[m, n] = alpha * sum_k A(m, k) B(k, n) + bias[m] (+ R[m, n]).
@@ -93,8 +96,13 @@ struct GemmLaunch {
     float *colstat;        // if set: (max, sum exp(c - max)) of each column n over each 128-row block,
                            // [ceil(M / 128)][N] pairs; needs a_km, KN B and no residual
     const float *bsoft;    // if set: B(k, n) -> exp(B(k, n) - bsoft[2n]) * bsoft[2n + 1]; needs MK A, KN B
+    float *part;           // K-split partial sums, gemm_partial_floats() floats (nullptr if 0); C's ldc must be N
 };
 int32_t launch_gemm(const GemmLaunch &g, hipStream_t s);
+// K-split factor launch_gemm uses (1 = none; never with colstat) and the
+// partial-sum floats it then needs.
+int gemm_ksplit(int M, int N, int K, bool colstat);
+size_t gemm_partial_floats(int M, int N, int K, bool colstat);
 
 // ------------------------------------------------------------------ norm
 size_t groupnorm_ws_bytes(int c, long long spatial);

@@ -114,7 +114,8 @@ int32_t vae_abi_version(void);
 /* Workspace (device bytes) needed by vae_conv2d / vae_conv_in for `conv` on an
  * input of h x w (upsampled to 2h x 2w when upsample2x): the weights repacked
  * for the kernel and, for shapes too small to fill the GPU, the partial sums
- * of a K-split.  0 for kernel-1 convs. */
+ * of a split along K (input channels x taps).  Kernel-1 convs and convs with
+ * at most 4 outputs need only the partial sums (0 for large images). */
 int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, int32_t h, int32_t w, int32_t upsample2x,
                                    size_t *bytes);
 

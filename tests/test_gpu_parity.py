@@ -126,8 +126,10 @@ def test_conv1x1(api, cin, cout, h, w, res):
 
 
 @pytest.mark.parametrize("cin,cout,h,w", [(128, 3, 64, 64), (128, 3, 37, 45), (64, 1, 10, 130), (32, 4, 9, 9),
-                                          (24, 2, 16, 16), (128, 3, 40, 256), (22, 3, 17, 131)])
+                                          (24, 2, 16, 16), (128, 3, 40, 256), (22, 3, 17, 131),
+                                          (32, 3, 256, 2048)])
 def test_conv_out_direct(api, cin, cout, h, w):
+    # small images split the input channels across workgroups; the last case is big enough not to
     x = vaegen.activation(6, "xo", (cin, h, w))
     wt, b = conv_params(6, "co", cin, cout, 3)
     y = api.conv2d(dev(x), dev(wt), dev(b), out=nan_like((cout, h, w)))
