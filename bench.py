@@ -17,6 +17,9 @@ the device and the latent already resident in HBM.  Default workload: latent
                FP32 matrix peak
   cpu_baseline the float64 oracle timed on this host on a bounded sample of
                the same workload (conv_in + the first mid resnet at latent 128x128)
+  secondary    the 256x256 decode (latent [16,32,32])
+  sweep        the single-layer sweep at full size (3x3 and 1x1 convs,
+               GroupNorm+SiLU) and a standalone nearest-x2 upsample
 """
 from __future__ import annotations
 
@@ -48,6 +51,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the second decode size (keeps profiler summaries to one workload)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the single-layer sweep")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the decodes, run one plain device copy of this many MiB "
@@ -115,6 +119,55 @@ def cpu_baseline(seed: int, h: int) -> dict:
             "seconds": dt, "repetitions": reps,
             "sample": f"float64 oracle on conv_in + mid_block.resnets.0 of the latent [16,{h},{h}] decode "
                       f"({flops / 1e9:.1f} GFLOP per repetition, repeated for >= 10 s)"}
+
+
+def sweep(args) -> dict:
+    """The single-layer sweep at its full sizes through the per-layer entry
+    points (each call includes its weight repack), plus a standalone nearest-x2
+    upsample.  W warm-ups, then K timed calls bracketed by events."""
+    import torch
+    from diffusion_vae_decoder_amd import api
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    out = {}
+    for cin, cout, k, h in [(512, 512, 3, 128), (256, 256, 3, 256), (128, 128, 3, 512), (256, 128, 3, 512),
+                            (256, 128, 1, 512)]:
+        x = torch.from_numpy(vaegen.activation(args.seed, f"sweep.x{cin}_{h}", (cin, h, h))).cuda()
+        prm = vaegen.conv_params(args.seed, "sweep.c", cin, cout, k)
+        w, b = (torch.from_numpy(prm["sweep.c." + n]).cuda() for n in ("weight", "bias"))
+        y = torch.empty((cout, h, h), device="cuda")
+        ms = timed(lambda: api.conv2d(x, w, b, out=y))
+        fl = 2.0 * cin * cout * k * k * h * h
+        out[f"conv{k}x{k} {cin}->{cout} @{h}x{h}"] = {
+            "ms": ms, "tflops": fl / ms / 1e9, "frac_fp32_mfma_peak": fl / ms / 1e9 / PEAK_FP32_MFMA_TFLOPS}
+        del x, y
+    c, h = 128, 512
+    x = torch.from_numpy(vaegen.activation(args.seed, "sweep.gn", (c, h, h))).cuda()
+    nrm = vaegen.norm_params(args.seed, "sweep.n", c)
+    g, bt = (torch.from_numpy(nrm["sweep.n." + n]).cuda() for n in ("weight", "bias"))
+    y = torch.empty_like(x)
+    ms = timed(lambda: api.groupnorm_silu(x, g, bt, out=y))
+    by = 2.0 * c * h * h * 4
+    out[f"groupnorm_silu [{c},{h},{h}]"] = {"ms": ms, "gbs": by / ms / 1e6, "frac_hbm": by / ms / 1e6 / PEAK_HBM_GBS,
+                                            "note": "statistics pass + apply pass; 2 algorithmic units of traffic"}
+    c, h = 256, 512
+    x = torch.from_numpy(vaegen.activation(args.seed, "sweep.up", (c, h, h))).cuda()
+    y = torch.empty((c, 2 * h, 2 * h), device="cuda")
+    ms = timed(lambda: api.upsample_nearest2x(x, out=y))
+    by = 5.0 * c * h * h * 4
+    out[f"upsample_nearest2x [{c},{h},{h}]"] = {"ms": ms, "gbs": by / ms / 1e6, "frac_hbm": by / ms / 1e6 / PEAK_HBM_GBS}
+    return out
 
 
 def secondary(dec, args, h2: int) -> dict:
@@ -228,6 +281,8 @@ def main():
     # secondary: the other decode size the metric names (after the timed region)
     if not args.no_secondary:
         out["secondary"] = secondary(dec, args, 32 if h != 32 else 128)
+    if not args.no_sweep:
+        out["sweep"] = sweep(args)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")

@@ -397,25 +397,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 }
 
 // Packed layout: [ob][dt][cb][k = c_local * 9 + tap][m], m in [0, 128);
-// zero where the output channel or input channel is out of range.
-__global__ void pack_conv3x3_kernel(const float *__restrict__ w, float *__restrict__ dst, int cout,
-                                    int cin, int kt, int n_cb, long long total) {
-    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= total) return;
-    const int m = (int)(idx % kConvBM);
-    long long rest = idx / kConvBM;
-    const int k = (int)(rest % kCK);
-    rest /= kCK;
-    const int cb = (int)(rest % n_cb);
-    rest /= n_cb;
-    const int dt = (int)(rest % kt);
-    const int ob = (int)(rest / kt);
-    const int o = ob * kConvBM + m;
-    const int c = cb * kConvCC + k / 9;
-    const int tap = k % 9;
-    float v = 0.f;
-    if (o < cout && c < cin) v = w[(((long long)o * cin + c) * kt + dt) * 9 + tap];
-    dst[idx] = v;
+// zero where the output channel or input channel is out of range.  One
+// workgroup per chunk (ob, dt, cb): the 128 output channels' 36 weights are
+// read along their rows (contiguous in [cout, cin, (kt,) 3, 3]) into LDS and
+// written back transposed, so both sides are coalesced.
+constexpr int kPackLd = kCK + 1;   // odd row stride: the transposed LDS reads hit distinct banks
+__global__ __launch_bounds__(kThreads) void pack_conv3x3_kernel(const float *__restrict__ w, float *__restrict__ dst,
+                                                                int cout, int cin, int kt, int n_cb) {
+    __shared__ float t[kConvBM * kPackLd];
+    const int cb = blockIdx.x, dt = blockIdx.y, ob = blockIdx.z;
+    for (int e = threadIdx.x; e < kConvBM * kCK; e += kThreads) {
+        const int m = e / kCK, k = e - (e / kCK) * kCK;
+        const int o = ob * kConvBM + m, c = cb * kConvCC + k / 9, tap = k % 9;
+        float v = 0.f;
+        if (o < cout && c < cin) v = w[(((long long)o * cin + c) * kt + dt) * 9 + tap];
+        t[m * kPackLd + k] = v;
+    }
+    __syncthreads();
+    float *out = dst + (((long long)ob * kt + dt) * n_cb + cb) * (kCK * kConvBM);
+    for (int e = threadIdx.x; e < kCK * kConvBM; e += kThreads) {
+        const int k = e / kConvBM, m = e - (e / kConvBM) * kConvBM;
+        out[e] = t[m * kPackLd + k];
+    }
 }
 
 // y[o, :] = bias[o] + sum_s part[s, o, :] (+ res[o, :]), summed in split order.
@@ -689,11 +692,9 @@ size_t conv3x3_packed_floats(int cout, int cin, int kt) {
 
 int32_t pack_conv3x3(const float *w, int cout, int cin, int kt, float *dst, hipStream_t s) {
     const int n_cb = (cin + kConvCC - 1) / kConvCC;
-    const long long total = (long long)conv3x3_packed_floats(cout, cin, kt);
-    const int threads = 256;
-    const long long blocks = (total + threads - 1) / threads;
-    hipLaunchKernelGGL(pack_conv3x3_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, w, dst,
-                       cout, cin, kt, n_cb, total);
+    const int n_ob = (cout + kConvBM - 1) / kConvBM;
+    hipLaunchKernelGGL(pack_conv3x3_kernel, dim3((unsigned)n_cb, (unsigned)kt, (unsigned)n_ob), dim3(kThreads), 0, s,
+                       w, dst, cout, cin, kt, n_cb);
     return check_launch("pack_conv3x3");
 }
 
