@@ -13,10 +13,13 @@ from .vae_oracle import (  # noqa: F401
     conv3d_causal,
     conv3d_causal_at,
     decode,
+    decode_causal3d,
     denormalize,
     group_norm,
     group_norm_silu,
+    pointwise_conv,
     resnet,
+    resnet_causal3d,
     silu,
     softmax_rows,
     upsample_nearest2x,

@@ -28,7 +28,11 @@ document with its reason):
     norm of the decoder;
   * the causal 3-D stack pads time at the front with two copies of frame 0,
     GroupNorm statistics span (C/32 channels) x T x H x W, and the residual
-    add follows the second layer's GroupNorm+SiLU.
+    add follows the second layer's GroupNorm+SiLU;
+  * the causal 3-D decoder is the decoder chain with every 3x3 conv a causal
+    3x3x3 conv, attention over all positions of the clip and upsampling in
+    height and width only (the pages name the 3-D causal conv and its time
+    padding, nothing more).
 """
 from __future__ import annotations
 
@@ -268,6 +272,62 @@ def causal_stack(x, p: dict, layers: int = 4) -> np.ndarray:
             h = group_norm_silu(h, p[f"stack.{j}.norm.weight"], p[f"stack.{j}.norm.bias"])
         x = x + h
     return x
+
+
+# ---------------------------------------------------------------------------
+# the causal 3-D decoder
+# ---------------------------------------------------------------------------
+
+def pointwise_conv(x, w, b) -> np.ndarray:
+    """A 1x1 (or 1x1x1) convolution of ``x[C, ...]``:
+    ``y[o, ...] = b[o] + sum_c w[o, c] x[c, ...]`` (the channel-changing skip
+    of a resnet, [vae-doc] VaeResnetRef)."""
+    x = _f64(x)
+    c = x.shape[0]
+    w2 = _f64(w).reshape(w.shape[0], c)
+    y = (w2 @ x.reshape(c, -1)).reshape((w.shape[0],) + x.shape[1:])
+    return y + _f64(b).reshape((-1,) + (1,) * (x.ndim - 1))
+
+
+def resnet_causal3d(x, p: dict, prefix: str) -> np.ndarray:
+    """The resnet of ``resnet`` on a video ``x[C, T, H, W]`` with causal 3-D
+    convs ([handoff] "The CPU VAE code": LTX's decoder is a 3-D causal conv
+    decode); GroupNorm statistics span (C/32) x T x H x W."""
+    x = _f64(x)
+    h = group_norm_silu(x, p[prefix + ".norm1.weight"], p[prefix + ".norm1.bias"])
+    h = conv3d_causal(h, p[prefix + ".conv1.weight"], p[prefix + ".conv1.bias"])
+    h = group_norm_silu(h, p[prefix + ".norm2.weight"], p[prefix + ".norm2.bias"])
+    h = conv3d_causal(h, p[prefix + ".conv2.weight"], p[prefix + ".conv2.bias"])
+    if prefix + ".conv_shortcut.weight" in p:
+        skip = pointwise_conv(x, p[prefix + ".conv_shortcut.weight"], p[prefix + ".conv_shortcut.bias"])
+    else:
+        skip = x
+    return skip + h
+
+
+def decode_causal3d(z, p: dict, scaling_factor: float, shift_factor: float,
+                    resnets_per_block: int = 3) -> np.ndarray:
+    """The decoder chain of ``decode`` on a video latent ``z[16, T, h, w]``
+    with every 3x3 conv a causal 3x3x3 conv (time front-padded with two copies
+    of frame 0; [handoff] "The CPU VAE code", "GPU plan"): the mid attention
+    runs over all T*h*w positions (row-major over t, y, x), upsampling is
+    nearest x2 in height and width only, and the output is ``[3, T, 8h, 8w]``.
+    """
+    x = conv3d_causal(denormalize(z, scaling_factor, shift_factor), p["conv_in.weight"], p["conv_in.bias"])
+    x = resnet_causal3d(x, p, "mid_block.resnets.0")
+    c, t, h, w = x.shape
+    x = attention(x.reshape(c, t * h, w), p, "mid_block.attentions.0").reshape(c, t, h, w)
+    x = resnet_causal3d(x, p, "mid_block.resnets.1")
+    i = 0
+    while f"up_blocks.{i}.resnets.0.conv1.weight" in p:
+        for j in range(resnets_per_block):
+            x = resnet_causal3d(x, p, f"up_blocks.{i}.resnets.{j}")
+        up = f"up_blocks.{i}.upsamplers.0.conv"
+        if up + ".weight" in p:
+            x = conv3d_causal(upsample_nearest2x(x), p[up + ".weight"], p[up + ".bias"])
+        i += 1
+    x = group_norm_silu(x, p["conv_norm_out.weight"], p["conv_norm_out.bias"])
+    return conv3d_causal(x, p["conv_out.weight"], p["conv_out.bias"])
 
 
 # ---------------------------------------------------------------------------

@@ -516,3 +516,97 @@ def test_causal_stack_matches_torch():
             cur = F.silu(F.group_norm(cur, 32, T[f"stack.{j}.norm.weight"], T[f"stack.{j}.norm.bias"], eps=1e-6))[0]
         h = h + cur
     assert np.allclose(oracle.causal_stack(x, p), h.numpy(), atol=1e-11, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# the causal 3-D decoder
+# ---------------------------------------------------------------------------
+
+def small_decoder3d(seed):
+    return vaegen.decoder_params(seed, widths=(64, 64, 32, 32), latent_channels=4, dims=3)
+
+
+def test_pointwise_conv_is_the_1x1_conv():
+    x = rand(12, 5, 7)
+    w, b = rand(9, 12, 1, 1), rand(9)
+    assert np.allclose(oracle.pointwise_conv(x, w, b), oracle.conv2d(x, w, b), atol=1e-13)
+    x4 = rand(12, 3, 5, 7)
+    y4 = oracle.pointwise_conv(x4, w[..., None], b)
+    for t in range(3):
+        assert np.allclose(y4[:, t], oracle.conv2d(x4[:, t], w, b), atol=1e-13)
+
+
+def test_decode_causal3d_single_frame_is_the_2d_decode():
+    # one frame: the front padding repeats that frame, so every causal conv is a
+    # 2-D conv with the time taps summed, and the 1x1x1 skips are 1x1 convs
+    p3 = small_decoder3d(5)
+    p2 = {}
+    for k, v in p3.items():
+        if v.ndim == 5:
+            v = v.astype(np.float64).sum(axis=2) if v.shape[2] == 3 else v[:, :, 0]
+        p2[k] = v
+    z = vaegen.normal(5, "z3", (4, 1, 3, 2))
+    y3 = oracle.decode_causal3d(z, p3, 0.5, 0.1)
+    y2 = oracle.decode(z[:, 0], p2, 0.5, 0.1)
+    assert y3.shape == (3, 1, 24, 16)
+    assert np.allclose(y3[:, 0], y2, atol=1e-10, rtol=0)
+
+
+def test_decode_causal3d_repeated_frame():
+    # a clip that repeats one frame: every layer keeps the frames equal (the
+    # causal window sees copies of frame 0, the GroupNorm statistics and the
+    # attention's key set are those of one frame, duplicated)
+    p3 = small_decoder3d(6)
+    z1 = vaegen.normal(6, "z3", (4, 1, 2, 3))
+    y1 = oracle.decode_causal3d(z1, p3, 0.5, 0.1)
+    y3 = oracle.decode_causal3d(np.concatenate([z1] * 3, axis=1), p3, 0.5, 0.1)
+    assert y3.shape == (3, 3, 16, 24)
+    for t in range(3):
+        assert np.allclose(y3[:, t], y1[:, 0], atol=1e-10, rtol=0)
+
+
+def test_decode_causal3d_matches_torch_composition():
+    p = small_decoder3d(7)
+    z = vaegen.normal(7, "z3", (4, 3, 2, 3))
+    T = {k: t64(v) for k, v in p.items()}
+
+    def gn(x, pre):
+        return F.group_norm(x, 32, T[pre + ".weight"], T[pre + ".bias"], eps=1e-6)
+
+    def cv(x, pre):
+        w = T[pre + ".weight"]
+        if w.shape[2] == 1:
+            return F.conv3d(x, w, T[pre + ".bias"])
+        front = x[:, :, :1].expand(-1, -1, 2, -1, -1)
+        return F.conv3d(torch.cat([front, x], 2), w, T[pre + ".bias"], padding=(0, 1, 1))
+
+    def res(x, pre):
+        h = cv(F.silu(gn(x, pre + ".norm1")), pre + ".conv1")
+        h = cv(F.silu(gn(h, pre + ".norm2")), pre + ".conv2")
+        s = cv(x, pre + ".conv_shortcut") if pre + ".conv_shortcut.weight" in T else x
+        return s + h
+
+    def attn(x, pre):
+        c = x.shape[1]
+        tok = gn(x, pre + ".group_norm")[0].reshape(c, -1).T
+        q = F.linear(tok, T[pre + ".to_q.weight"], T[pre + ".to_q.bias"])
+        k = F.linear(tok, T[pre + ".to_k.weight"], T[pre + ".to_k.bias"])
+        v = F.linear(tok, T[pre + ".to_v.weight"], T[pre + ".to_v.bias"])
+        o = F.scaled_dot_product_attention(q[None], k[None], v[None], scale=c ** -0.5)[0]
+        o = F.linear(o, T[pre + ".to_out.0.weight"], T[pre + ".to_out.0.bias"])
+        return x + o.T.reshape(x.shape)
+
+    x = t64(z)[None] / 0.5 + 0.1
+    x = cv(x, "conv_in")
+    x = res(x, "mid_block.resnets.0")
+    x = attn(x, "mid_block.attentions.0")
+    x = res(x, "mid_block.resnets.1")
+    for i in range(4):
+        for j in range(3):
+            x = res(x, f"up_blocks.{i}.resnets.{j}")
+        if i < 3:
+            x = cv(F.interpolate(x, scale_factor=(1, 2, 2), mode="nearest"), f"up_blocks.{i}.upsamplers.0.conv")
+    x = cv(F.silu(gn(x, "conv_norm_out")), "conv_out")[0].numpy()
+    y = oracle.decode_causal3d(z, p, 0.5, 0.1)
+    assert y.shape == (3, 3, 16, 24)
+    assert np.allclose(y, x, atol=1e-10, rtol=0)

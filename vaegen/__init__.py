@@ -148,14 +148,14 @@ def linear_params(seed: int, prefix: str, cin: int, cout: int) -> dict:
     }
 
 
-def resnet_params(seed: int, prefix: str, cin: int, cout: int) -> dict:
+def resnet_params(seed: int, prefix: str, cin: int, cout: int, dims: int = 2) -> dict:
     p = {}
     p.update(norm_params(seed, prefix + ".norm1", cin))
-    p.update(conv_params(seed, prefix + ".conv1", cin, cout, 3))
+    p.update(conv_params(seed, prefix + ".conv1", cin, cout, 3, dims))
     p.update(norm_params(seed, prefix + ".norm2", cout))
-    p.update(conv_params(seed, prefix + ".conv2", cout, cout, 3))
+    p.update(conv_params(seed, prefix + ".conv2", cout, cout, 3, dims))
     if cin != cout:
-        p.update(conv_params(seed, prefix + ".conv_shortcut", cin, cout, 1))
+        p.update(conv_params(seed, prefix + ".conv_shortcut", cin, cout, 1, dims))
     return p
 
 
@@ -171,28 +171,35 @@ def decoder_params(seed: int = 0,
                    widths=DECODER_WIDTHS,
                    latent_channels: int = LATENT_CHANNELS,
                    out_channels: int = OUT_CHANNELS,
-                   resnets_per_block: int = RESNETS_PER_UP_BLOCK) -> dict:
-    """All decoder tensors, diffusers names, f32 numpy arrays."""
+                   resnets_per_block: int = RESNETS_PER_UP_BLOCK, dims: int = 2) -> dict:
+    """All decoder tensors, diffusers names, f32 numpy arrays.  ``dims=3``
+    gives the causal 3-D decoder: every conv kernel gets a time axis
+    (3x3x3, and 1x1x1 for the skips), fan-in counted over all its taps."""
     c0 = widths[0]
     p = {}
-    p.update(conv_params(seed, "conv_in", latent_channels, c0, 3))
-    p.update(resnet_params(seed, "mid_block.resnets.0", c0, c0))
+    p.update(conv_params(seed, "conv_in", latent_channels, c0, 3, dims))
+    p.update(resnet_params(seed, "mid_block.resnets.0", c0, c0, dims))
     p.update(attention_params(seed, "mid_block.attentions.0", c0))
-    p.update(resnet_params(seed, "mid_block.resnets.1", c0, c0))
+    p.update(resnet_params(seed, "mid_block.resnets.1", c0, c0, dims))
     prev = c0
     for i, c in enumerate(widths):
         for j in range(resnets_per_block):
-            p.update(resnet_params(seed, f"up_blocks.{i}.resnets.{j}", prev if j == 0 else c, c))
+            p.update(resnet_params(seed, f"up_blocks.{i}.resnets.{j}", prev if j == 0 else c, c, dims))
         prev = c
         if i + 1 < len(widths):
-            p.update(conv_params(seed, f"up_blocks.{i}.upsamplers.0.conv", c, c, 3))
+            p.update(conv_params(seed, f"up_blocks.{i}.upsamplers.0.conv", c, c, 3, dims))
     p.update(norm_params(seed, "conv_norm_out", prev))
-    p.update(conv_params(seed, "conv_out", prev, out_channels, 3))
+    p.update(conv_params(seed, "conv_out", prev, out_channels, 3, dims))
     return p
 
 
 def latent(seed: int, h: int, w: int, channels: int = LATENT_CHANNELS) -> np.ndarray:
     return normal(seed, "latent", (channels, h, w))
+
+
+def latent3d(seed: int, t: int, h: int, w: int, channels: int = LATENT_CHANNELS) -> np.ndarray:
+    """A video latent [channels, t, h, w] for the causal 3-D decoder."""
+    return normal(seed, "latent3d", (channels, t, h, w))
 
 
 def activation(seed: int, name: str, shape) -> np.ndarray:
