@@ -16,7 +16,7 @@ VAE_ERR_INVALID_ARG = -1
 VAE_ERR_UNSUPPORTED = -2
 VAE_ERR_WORKSPACE = -3
 VAE_ERR_HIP = -4
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class VaeConv(ctypes.Structure):
@@ -82,6 +82,11 @@ SIGNATURES = {
     "vae_decoder_create": (c_int32, [POINTER(c_void_p), POINTER(VaeWeights), c_void_p, c_size_t, c_void_p]),
     "vae_decoder_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_size_t)]),
     "vae_decode": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "vae_decoder3d_pack_bytes": (c_int32, [POINTER(VaeWeights), POINTER(c_size_t)]),
+    "vae_decoder3d_create": (c_int32, [POINTER(c_void_p), POINTER(VaeWeights), c_void_p, c_size_t, c_void_p]),
+    "vae_decoder3d_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(c_size_t)]),
+    "vae_decode3d": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_size_t,
+                               c_void_p]),
     "vae_decoder_output_shape": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32),
                                            POINTER(c_int32)]),
     "vae_decoder_destroy": (None, [c_void_p]),

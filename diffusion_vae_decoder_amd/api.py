@@ -214,10 +214,13 @@ class Decoder:
 
     ``params`` maps diffusers tensor names (conv_in.*, mid_block.*,
     up_blocks.*, conv_norm_out.*, conv_out.*) to float32 GPU tensors.  The
-    library copies them once into its own packed buffer.
+    library copies them once into its own packed buffer.  With ``causal3d``
+    the same chain decodes video latents ``[c, t, h, w]`` (``vae_decode3d``):
+    the 3x3 conv weights are ``[cout, cin, 3, 3, 3]`` causal kernels.
     """
 
-    def __init__(self, params: Dict[str, torch.Tensor], scaling_factor: float, shift_factor: float):
+    def __init__(self, params: Dict[str, torch.Tensor], scaling_factor: float, shift_factor: float,
+                 causal3d: bool = False):
         lib = _lib_()
         self._lib = lib
         p = params
@@ -259,13 +262,16 @@ class Decoder:
         w = VaeWeights(conv("conv_in"), resnet("mid_block.resnets.0"), attn, resnet("mid_block.resnets.1"),
                        len(ups), ups_arr, norm("conv_norm_out"), conv("conv_out"), float(scaling_factor),
                        float(shift_factor))
+        self.causal3d = bool(causal3d)
         nb = c_size_t()
-        check(lib.vae_decoder_pack_bytes(byref(w), byref(nb)))
+        pack_bytes = lib.vae_decoder3d_pack_bytes if self.causal3d else lib.vae_decoder_pack_bytes
+        create = lib.vae_decoder3d_create if self.causal3d else lib.vae_decoder_create
+        check(pack_bytes(byref(w), byref(nb)))
         device = p["conv_in.weight"].device
         self.device = device
         self.pack = torch.empty(nb.value, dtype=torch.uint8, device=device)
         handle = c_void_p()
-        check(lib.vae_decoder_create(byref(handle), byref(w), self.pack.data_ptr(), nb.value, _stream()))
+        check(create(byref(handle), byref(w), self.pack.data_ptr(), nb.value, _stream()))
         self._h = handle
         self.latent_channels = p["conv_in.weight"].shape[1]
         self._ws: Optional[torch.Tensor] = None
@@ -275,21 +281,34 @@ class Decoder:
         check(self._lib.vae_decoder_output_shape(self._h, h, w, byref(c), byref(ho), byref(wo)))
         return c.value, ho.value, wo.value
 
-    def workspace_bytes(self, h: int, w: int) -> int:
+    def workspace_bytes(self, h: int, w: int, t: Optional[int] = None) -> int:
         nb = c_size_t()
-        check(self._lib.vae_decoder_workspace_bytes(self._h, h, w, byref(nb)))
+        if self.causal3d:
+            check(self._lib.vae_decoder3d_workspace_bytes(self._h, 1 if t is None else t, h, w, byref(nb)))
+        else:
+            check(self._lib.vae_decoder_workspace_bytes(self._h, h, w, byref(nb)))
         return nb.value
 
     def decode(self, latent: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """latent [c, h, w] -> rgb [3, 8h, 8w]; for a 3-D decoder [c, t, h, w] -> [3, t, 8h, 8w]."""
         _dev(latent, "latent")
-        c, h, w = latent.shape
-        nb = self.workspace_bytes(h, w)
+        if self.causal3d:
+            c, t, h, w = latent.shape
+        else:
+            c, h, w = latent.shape
+            t = None
+        nb = self.workspace_bytes(h, w, t)
         if self._ws is None or self._ws.numel() < nb:
             self._ws = torch.empty(nb, dtype=torch.uint8, device=latent.device)
         co, ho, wo = self.output_shape(h, w)
-        rgb = torch.empty((co, ho, wo), dtype=torch.float32, device=latent.device) if out is None else _dev(out, "out")
-        check(self._lib.vae_decode(self._h, latent.data_ptr(), h, w, rgb.data_ptr(), self._ws.data_ptr(),
-                                   self._ws.numel(), _stream()))
+        shape = (co, ho, wo) if t is None else (co, t, ho, wo)
+        rgb = _out(out, shape, latent.device)
+        if self.causal3d:
+            check(self._lib.vae_decode3d(self._h, latent.data_ptr(), t, h, w, rgb.data_ptr(), self._ws.data_ptr(),
+                                         self._ws.numel(), _stream()))
+        else:
+            check(self._lib.vae_decode(self._h, latent.data_ptr(), h, w, rgb.data_ptr(), self._ws.data_ptr(),
+                                       self._ws.numel(), _stream()))
         return rgb
 
     def set_groupnorm_fusion(self, on: bool) -> None:

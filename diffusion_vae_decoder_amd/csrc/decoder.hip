@@ -3,6 +3,13 @@
 // mid attention -> mid resnet -> up blocks (resnets, then nearest x2 folded
 // into the upsample conv) -> GroupNorm + SiLU -> conv_out.
 //
+// The causal 3-D decoder (VAE decode -> GPU handoff, "The CPU VAE code": the
+// LTX decoder is a 3-D causal conv decode) is the same chain on a clip
+// [c, T, h, w]: every 3x3 conv becomes a causal 3x3x3 conv (time front-padded
+// with two copies of frame 0), GroupNorm spans (C/32) x T x H x W, the
+// attention runs over all T*H*W positions and upsampling is spatial only.
+// It runs on the same kernels with three time taps and T frames.
+//
 // vae_decoder_create copies every weight once into the caller's `pack`
 // buffer (3x3 weights already in the conv kernel's layout, q/k/v
 // concatenated), so a decode launches kernels only.  All activations live in
@@ -61,6 +68,7 @@ struct Packer {
     char *dst;
     size_t off = 0;
     hipStream_t s;
+    int kt = 1;   // time taps of the 3x3 convs (3: causal 3-D)
     int32_t rc = VAE_OK;
 
     const float *take(size_t floats) {
@@ -86,8 +94,8 @@ struct Packer {
         if (c.kernel == 3 && raw3) {
             d.w = copy(c.weight, (size_t)c.out_channels * c.in_channels * 9);
         } else if (c.kernel == 3) {
-            const float *p = take(conv3x3_packed_floats(c.out_channels, c.in_channels, 1));
-            if (dst && rc == VAE_OK) rc = pack_conv3x3(c.weight, c.out_channels, c.in_channels, 1, const_cast<float *>(p), s);
+            const float *p = take(conv3x3_packed_floats(c.out_channels, c.in_channels, kt));
+            if (dst && rc == VAE_OK) rc = pack_conv3x3(c.weight, c.out_channels, c.in_channels, kt, const_cast<float *>(p), s);
             d.w = p;
         } else {
             d.w = copy(c.weight, (size_t)c.out_channels * c.in_channels);
@@ -220,6 +228,8 @@ struct vae_decoder {
     DConv conv_out;
     float scaling = 1.f, shift = 0.f;
     int latent_c = 0;
+    int kt = 1;              // 3: the causal 3-D decoder
+    bool direct_out = false; // conv_out kept raw for the direct kernel
     bool gn_fused = false;   // GroupNorm + SiLU applied while the consuming conv loads its input
     // profiling
     bool profiling = false;
@@ -244,32 +254,34 @@ struct Plan {
     size_t act = 0, gn = 0, attn = 0, part = 0, coef = 0, rec = 0;
 };
 
-ConvLaunch launch_shape(const DConv &c, long long H, long long W) {
+ConvLaunch launch_shape(const DConv &c, long long H, long long W, int T, int kt) {
     ConvLaunch a{};
     a.cin = c.cin;
     a.cout = c.cout;
     a.H = (int)H;
     a.W = (int)W;
-    a.T = 1;
-    a.kt = 1;
+    a.T = T;
+    a.kt = kt;
     return a;
 }
 
-Plan plan_for(const vae_decoder *d, int h, int w) {
+// Sizes for a clip of T frames (T = 1 for images).
+Plan plan_for(const vae_decoder *d, int T, int h, int w) {
     Plan p;
+    const int kt = d->kt;
     auto act = [&](long long c, long long H, long long W) {
-        const size_t n = (size_t)(c * H * W);
+        const size_t n = (size_t)(c * T * H * W);
         if (n > p.act) p.act = n;
     };
     auto gn = [&](long long c, long long H, long long W) {
-        const size_t b = groupnorm_ws_bytes((int)c, H * W);
+        const size_t b = groupnorm_ws_bytes((int)c, (long long)T * H * W);
         if (b > p.gn) p.gn = b;
         if ((size_t)c * 16 > p.coef) p.coef = (size_t)c * 16;
     };
     auto part = [&](const DConv &c, long long H, long long W) {
-        const size_t n = conv3x3_partial_floats(c.cout, c.cin, 1, (int)H, (int)W, 1);
+        const size_t n = conv3x3_partial_floats(c.cout, c.cin, kt, (int)H, (int)W, T);
         if (n > p.part) p.part = n;
-        const size_t r = (size_t)32 * conv3x3_gn_records(launch_shape(c, H, W)) * sizeof(floatx4);
+        const size_t r = (size_t)32 * conv3x3_gn_records(launch_shape(c, H, W, T, kt)) * sizeof(floatx4);
         if (r > p.rec) p.rec = r;
     };
     long long H = h, W = w;
@@ -278,7 +290,7 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
     part(d->conv_in, H, W);
     auto res = [&](const DRes &r) {
         if (r.sc.present) {
-            const size_t n = gemm_partial_floats(r.sc.cout, (int)(H * W), r.sc.cin, false);
+            const size_t n = gemm_partial_floats(r.sc.cout, (int)(T * H * W), r.sc.cin, false);
             if (n > p.part) p.part = n;
         }
         gn(r.c1.cin, H, W);
@@ -289,7 +301,7 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
         part(r.c2, H, W);
     };
     res(d->mid0);
-    p.attn = attention_ws_bytes(d->attn.c, H * W);
+    p.attn = attention_ws_bytes(d->attn.c, (long long)T * H * W);
     res(d->mid1);
     for (const DUp &u : d->ups) {
         for (const DRes &r : u.res) res(r);
@@ -301,7 +313,7 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
         }
     }
     gn(d->norm_out.c, H, W);
-    if (d->conv_out.cout <= 4) {
+    if (d->direct_out) {
         const size_t n = conv3x3_direct_partial_floats(d->conv_out.cout, d->conv_out.cin, (int)H, (int)W);
         if (n > p.part) p.part = n;
     } else {
@@ -310,12 +322,16 @@ Plan plan_for(const vae_decoder *d, int h, int w) {
     return p;
 }
 
-double conv_flops(const DConv &c, long long H, long long W) { return 2.0 * c.cout * c.cin * c.k * c.k * (double)(H * W); }
+// Algorithmic FLOPs of a conv over an H x W frame (times the time taps for 3x3 kernels).
+double conv_flops(const DConv &c, long long H, long long W, int kt) {
+    return 2.0 * c.cout * c.cin * c.k * c.k * (c.k == 3 ? kt : 1) * (double)(H * W);
+}
 
 struct Runner {
     vae_decoder *d;
     hipStream_t s;
     float *part = nullptr;
+    int T = 1;   // frames
     int32_t rc = VAE_OK;
 
     ProfEntry *begin(const char *kernel, const std::string &layer, double flops, double bytes) {
@@ -359,8 +375,8 @@ struct Runner {
         a.cout = c.cout;
         a.H = H;
         a.W = W;
-        a.T = 1;
-        a.kt = 1;
+        a.T = T;
+        a.kt = d->kt;
         a.upsample = up ? 1 : 0;
         a.denorm = denorm ? 1 : 0;
         a.dn_scale = d->scaling;
@@ -369,16 +385,17 @@ struct Runner {
         a.gn_coef = gn ? coef : nullptr;
         const int nrec = stats && c.cout % 32 == 0 ? conv3x3_gn_records(a) : 0;
         a.gn_rec = nrec > 0 ? rec : nullptr;
-        const double in_elems = (double)c.cin * H * W / (up ? 4.0 : 1.0);
-        const double bytes = 4.0 * (in_elems + (double)c.cout * H * W * (res ? 2.0 : 1.0));
-        const int ks = conv3x3_ksplit(c.cout, c.cin, 1, H, W, 1);
-        ProfEntry *e = begin(conv3x3_kernel_name(a), layer, conv_flops(c, H, W),
-                             ks > 1 ? 4.0 * (in_elems + (double)c.cout * H * W * ks) : bytes);
+        const double in_elems = (double)c.cin * T * H * W / (up ? 4.0 : 1.0);
+        const double out_elems = (double)c.cout * T * H * W;
+        const double bytes = 4.0 * (in_elems + out_elems * (res ? 2.0 : 1.0));
+        const int ks = conv3x3_ksplit(c.cout, c.cin, d->kt, H, W, T);
+        ProfEntry *e = begin(conv3x3_kernel_name(a), layer, conv_flops(c, H, W, d->kt) * T,
+                             ks > 1 ? 4.0 * (in_elems + out_elems * ks) : bytes);
         if (rc != VAE_OK) return;
         rc = launch_conv3x3_main(a, s);
         end(e);
         if (rc == VAE_OK && ks > 1) {
-            e = begin("splitk_reduce", layer, 0.0, 4.0 * (double)c.cout * H * W * (ks + 1 + (res ? 1 : 0)));
+            e = begin("splitk_reduce", layer, 0.0, 4.0 * out_elems * (ks + 1 + (res ? 1 : 0)));
             if (rc != VAE_OK) return;
             rc = launch_conv3x3_reduce(a, s);
             end(e);
@@ -400,17 +417,18 @@ struct Runner {
         GemmLaunch g{};
         g.A = c.w;
         g.lda = c.cin;
+        const long long n = (long long)T * H * W;
         g.B = x;
-        g.ldb = (long long)H * W;
+        g.ldb = n;
         g.bias = c.b;
         g.C = y;
-        g.ldc = (long long)H * W;
+        g.ldc = n;
         g.M = c.cout;
-        g.N = H * W;
+        g.N = (int)n;
         g.K = c.cin;
         g.alpha = 1.f;
         g.part = part;
-        ProfEntry *e = begin("gemm_mfma", layer, conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
+        ProfEntry *e = begin("gemm_mfma", layer, conv_flops(c, H, W, 1) * T, 4.0 * (c.cin + c.cout) * (double)n);
         if (rc != VAE_OK) return;
         rc = launch_gemm(g, s);
         end(e);
@@ -438,7 +456,7 @@ struct Runner {
     // X -> Y; uses T, U (and S for a 1x1 skip).  out_stats: the output is
     // normalised next, so conv2 records its GroupNorm statistics.
     void resnet(const DRes &r, Buffers &b, int H, int W, bool out_stats) {
-        const long long sp = (long long)H * W;
+        const long long sp = (long long)T * H * W;
         if (!d->gn_fused) {
             gn(r.name + ".norm1", r.n1, b.X, sp, b.T, b.gn);
             conv3(r.name + ".conv1", r.c1, b.T, H, W, false, nullptr, b.U, false, false, true);
@@ -465,13 +483,14 @@ struct Runner {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int32_t vae_decoder_pack_bytes(const vae_weights *w, size_t *bytes) {
+int32_t pack_bytes_kt(const vae_weights *w, int kt, size_t *bytes, const char *who) {
     int32_t rc = validate(w);
     if (rc) return rc;
-    if (!bytes) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_pack_bytes: bytes is NULL");
+    if (!bytes) return fail(VAE_ERR_INVALID_ARG, "%s: bytes is NULL", who);
     Packer p{nullptr, 0, nullptr};
+    p.kt = kt;
     p.conv(w->conv_in);
     p.resnet(w->mid_res0, "");
     p.attn(w->mid_attn);
@@ -481,23 +500,26 @@ int32_t vae_decoder_pack_bytes(const vae_weights *w, size_t *bytes) {
         if (w->ups[i].upsample.weight) p.conv(w->ups[i].upsample);
     }
     p.norm(w->norm_out);
-    p.conv(w->conv_out, w->conv_out.out_channels <= 4);
+    p.conv(w->conv_out, kt == 1 && w->conv_out.out_channels <= 4);
     *bytes = p.off;
     return VAE_OK;
 }
 
-int32_t vae_decoder_create(vae_decoder **out, const vae_weights *w, void *pack, size_t pack_bytes, void *stream) {
-    if (!out) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: out is NULL");
+int32_t create_kt(vae_decoder **out, const vae_weights *w, int kt, void *pack, size_t pack_bytes, void *stream,
+                  const char *who) {
+    if (!out) return fail(VAE_ERR_INVALID_ARG, "%s: out is NULL", who);
     *out = nullptr;
     size_t need = 0;
-    int32_t rc = vae_decoder_pack_bytes(w, &need);
+    int32_t rc = pack_bytes_kt(w, kt, &need, who);
     if (rc) return rc;
-    if (!pack || pack_bytes < need)
-        return fail(VAE_ERR_WORKSPACE, "vae_decoder_create: pack buffer %zu bytes < %zu", pack_bytes, need);
+    if (!pack || pack_bytes < need) return fail(VAE_ERR_WORKSPACE, "%s: pack buffer %zu bytes < %zu", who, pack_bytes, need);
     if (reinterpret_cast<uintptr_t>(pack) & 255)
-        return fail(VAE_ERR_INVALID_ARG, "vae_decoder_create: pack buffer must be 256-byte aligned");
+        return fail(VAE_ERR_INVALID_ARG, "%s: pack buffer must be 256-byte aligned", who);
     vae_decoder *d = new vae_decoder();
+    d->kt = kt;
+    d->direct_out = kt == 1 && w->conv_out.out_channels <= 4;
     Packer p{static_cast<char *>(pack), 0, static_cast<hipStream_t>(stream)};
+    p.kt = kt;
     d->conv_in = p.conv(w->conv_in);
     d->mid0 = p.resnet(w->mid_res0, "mid_block.resnets.0");
     d->attn = p.attn(w->mid_attn);
@@ -510,7 +532,7 @@ int32_t vae_decoder_create(vae_decoder **out, const vae_weights *w, void *pack, 
         d->ups.push_back(u);
     }
     d->norm_out = p.norm(w->norm_out);
-    d->conv_out = p.conv(w->conv_out, w->conv_out.out_channels <= 4);
+    d->conv_out = p.conv(w->conv_out, d->direct_out);
     d->scaling = w->scaling_factor;
     d->shift = w->shift_factor;
     d->latent_c = w->conv_in.in_channels;
@@ -522,41 +544,28 @@ int32_t vae_decoder_create(vae_decoder **out, const vae_weights *w, void *pack, 
     return VAE_OK;
 }
 
-int32_t vae_decoder_output_shape(const vae_decoder *d, int32_t h, int32_t w, int32_t *c, int32_t *ho, int32_t *wo) {
-    if (!d || !c || !ho || !wo) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_output_shape: NULL pointer");
-    long long H = h, W = w;
-    for (const DUp &u : d->ups)
-        if (u.up.present) {
-            H *= 2;
-            W *= 2;
-        }
-    *c = d->conv_out.cout;
-    *ho = (int32_t)H;
-    *wo = (int32_t)W;
-    return VAE_OK;
-}
-
-int32_t vae_decoder_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, size_t *bytes) {
-    if (!d || !bytes) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_workspace_bytes: NULL pointer");
-    if (h <= 0 || w <= 0) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_workspace_bytes: sizes must be positive");
+int32_t workspace_bytes_t(const vae_decoder *d, int T, int h, int w, size_t *bytes, const char *who) {
+    if (!d || !bytes) return fail(VAE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+    if (T <= 0 || h <= 0 || w <= 0) return fail(VAE_ERR_INVALID_ARG, "%s: sizes must be positive", who);
     int32_t c, ho, wo;
     vae_decoder_output_shape(d, h, w, &c, &ho, &wo);
-    if ((long long)ho * wo > (1LL << 30) || (long long)h * w > (1LL << 20))
-        return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_workspace_bytes: latent %dx%d too large", h, w);
-    const Plan p = plan_for(d, h, w);
+    if ((long long)T * ho * wo > (1LL << 30) || (long long)T * h * w > (1LL << 20))
+        return fail(VAE_ERR_UNSUPPORTED, "%s: latent %dx%dx%d too large", who, T, h, w);
+    if (T > 65535) return fail(VAE_ERR_UNSUPPORTED, "%s: %d frames exceed the grid limit", who, T);
+    const Plan p = plan_for(d, T, h, w);
     *bytes = 5 * align256(p.act * 4) + align256(p.gn) + align256(p.attn) + align256(p.part * 4) +
              align256(p.coef) + align256(p.rec);
     return VAE_OK;
 }
 
-int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, float *rgb, void *ws, size_t ws_bytes,
-                   void *stream) {
-    if (!d || !latent || !rgb) return fail(VAE_ERR_INVALID_ARG, "vae_decode: NULL pointer");
+int32_t decode_t(vae_decoder *d, const float *latent, int T, int h, int w, float *rgb, void *ws, size_t ws_bytes,
+                 void *stream, const char *who) {
+    if (!d || !latent || !rgb) return fail(VAE_ERR_INVALID_ARG, "%s: NULL pointer", who);
     size_t need = 0;
-    int32_t rc = vae_decoder_workspace_bytes(d, h, w, &need);
+    int32_t rc = workspace_bytes_t(d, T, h, w, &need, who);
     if (rc) return rc;
-    if (!ws || ws_bytes < need) return fail(VAE_ERR_WORKSPACE, "vae_decode: workspace %zu bytes < %zu", ws_bytes, need);
-    const Plan pl = plan_for(d, h, w);
+    if (!ws || ws_bytes < need) return fail(VAE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", who, ws_bytes, need);
+    const Plan pl = plan_for(d, T, h, w);
     char *base = static_cast<char *>(ws);
     const size_t a = align256(pl.act * 4);
     Buffers b;
@@ -577,6 +586,7 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
     b.rec = reinterpret_cast<floatx4 *>(q);
 
     Runner r{d, static_cast<hipStream_t>(stream), b.part};
+    r.T = T;
     r.coef = b.coef;
     r.rec = b.rec;
     int H = h, W = w;
@@ -584,11 +594,12 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
     r.resnet(d->mid0, b, H, W, /*out_stats=*/false);   // the attention normalises its own input
     std::swap(b.X, b.Y);
     if (r.rc == VAE_OK) {
-        const double n = (double)H * W, c = d->attn.c;
+        // tokens: the T*H*W positions, row-major over (t, y, x)
+        const double n = (double)T * H * W, c = d->attn.c;
         ProfEntry *e = r.begin("attention", "mid_block.attentions.0", 8.0 * n * c * c + 4.0 * n * n * c,
                                4.0 * (2.0 * c * n + 2.0 * n * n));
         if (r.rc == VAE_OK) {
-            r.rc = launch_attention(b.X, d->attn.c, H, W, d->attn.n.g, d->attn.n.b, d->attn.wqkv, d->attn.bqkv,
+            r.rc = launch_attention(b.X, d->attn.c, T * H, W, d->attn.n.g, d->attn.n.b, d->attn.wqkv, d->attn.bqkv,
                                     d->attn.wo, d->attn.bo, b.Y, b.attn, r.s);
             r.end(e);
         }
@@ -612,18 +623,19 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
         }
     }
     // norm_out + SiLU, conv_out.  A conv_out with at most 4 outputs is bound
-    // by reading its input, so it always normalises while loading (only the
-    // statistics are computed before it); a wider conv_out follows the
-    // decoder's GroupNorm mode.
+    // by reading its input, so it normalises while loading (only the
+    // statistics are computed before it): the direct kernel for images, the
+    // implicit GEMM with three time taps for clips.  A wider conv_out follows
+    // the decoder's GroupNorm mode.
     const DConv &c = d->conv_out;
-    const bool direct = c.cout <= 4 && c.cin <= kDirectGnMaxChannels;
-    const bool fused = direct || d->gn_fused;
+    const long long sp = (long long)T * H * W;
+    const bool fused = (c.cout <= 4 && c.cin <= kDirectGnMaxChannels) || d->gn_fused;
     const float *cin_x = fused ? b.X : b.T;
-    if (fused) r.gnc("conv_norm_out", d->norm_out, b.X, (long long)H * W, b.gn);
-    else r.gn("conv_norm_out", d->norm_out, b.X, (long long)H * W, b.T, b.gn);
+    if (fused) r.gnc("conv_norm_out", d->norm_out, b.X, sp, b.gn);
+    else r.gn("conv_norm_out", d->norm_out, b.X, sp, b.T, b.gn);
     if (r.rc == VAE_OK) {
-        if (c.cout <= 4) {
-            ProfEntry *e = r.begin("conv3x3_direct", "conv_out", conv_flops(c, H, W), 4.0 * (c.cin + c.cout) * (double)H * W);
+        if (d->direct_out) {
+            ProfEntry *e = r.begin("conv3x3_direct", "conv_out", conv_flops(c, H, W, 1), 4.0 * (c.cin + c.cout) * (double)H * W);
             if (r.rc == VAE_OK) {
                 r.rc = launch_conv3x3_direct(cin_x, c.w, c.b, rgb, c.cin, c.cout, H, W, r.s, fused ? b.coef : nullptr,
                                              b.part);
@@ -634,6 +646,62 @@ int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, fl
         }
     }
     return r.rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vae_decoder_pack_bytes(const vae_weights *w, size_t *bytes) {
+    return pack_bytes_kt(w, 1, bytes, "vae_decoder_pack_bytes");
+}
+
+int32_t vae_decoder_create(vae_decoder **out, const vae_weights *w, void *pack, size_t pack_bytes, void *stream) {
+    return create_kt(out, w, 1, pack, pack_bytes, stream, "vae_decoder_create");
+}
+
+int32_t vae_decoder3d_pack_bytes(const vae_weights *w, size_t *bytes) {
+    return pack_bytes_kt(w, 3, bytes, "vae_decoder3d_pack_bytes");
+}
+
+int32_t vae_decoder3d_create(vae_decoder **out, const vae_weights *w, void *pack, size_t pack_bytes, void *stream) {
+    return create_kt(out, w, 3, pack, pack_bytes, stream, "vae_decoder3d_create");
+}
+
+int32_t vae_decoder_output_shape(const vae_decoder *d, int32_t h, int32_t w, int32_t *c, int32_t *ho, int32_t *wo) {
+    if (!d || !c || !ho || !wo) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_output_shape: NULL pointer");
+    long long H = h, W = w;
+    for (const DUp &u : d->ups)
+        if (u.up.present) {
+            H *= 2;
+            W *= 2;
+        }
+    *c = d->conv_out.cout;
+    *ho = (int32_t)H;
+    *wo = (int32_t)W;
+    return VAE_OK;
+}
+
+int32_t vae_decoder_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, size_t *bytes) {
+    if (d && d->kt != 1) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_workspace_bytes: a 3-D decoder; use vae_decoder3d_workspace_bytes");
+    return workspace_bytes_t(d, 1, h, w, bytes, "vae_decoder_workspace_bytes");
+}
+
+int32_t vae_decoder3d_workspace_bytes(const vae_decoder *d, int32_t t, int32_t h, int32_t w, size_t *bytes) {
+    if (d && d->kt != 3) return fail(VAE_ERR_INVALID_ARG, "vae_decoder3d_workspace_bytes: not a 3-D decoder");
+    return workspace_bytes_t(d, t, h, w, bytes, "vae_decoder3d_workspace_bytes");
+}
+
+int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, float *rgb, void *ws, size_t ws_bytes,
+                   void *stream) {
+    if (d && d->kt != 1) return fail(VAE_ERR_INVALID_ARG, "vae_decode: a 3-D decoder; use vae_decode3d");
+    return decode_t(d, latent, 1, h, w, rgb, ws, ws_bytes, stream, "vae_decode");
+}
+
+int32_t vae_decode3d(vae_decoder *d, const float *latent, int32_t t, int32_t h, int32_t w, float *rgb, void *ws,
+                     size_t ws_bytes, void *stream) {
+    if (d && d->kt != 3) return fail(VAE_ERR_INVALID_ARG, "vae_decode3d: not a 3-D decoder");
+    return decode_t(d, latent, t, h, w, rgb, ws, ws_bytes, stream, "vae_decode3d");
 }
 
 void vae_decoder_destroy(vae_decoder *d) {

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 3
+#define VAE_ABI_VERSION 4
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -227,6 +227,25 @@ int32_t vae_decoder_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, 
  * time on different streams (they share the handle's profiling state). */
 int32_t vae_decode(vae_decoder *d, const float *latent, int32_t h, int32_t w, float *rgb,
                    void *ws, size_t ws_bytes, void *stream);
+
+/* The causal 3-D decoder (VAE decode -> GPU handoff, "The CPU VAE code": the
+ * LTX decoder is a 3-D causal conv decode, causal padding on time).  The same
+ * chain and the same vae_weights layout, read as a video decoder: every
+ * kernel-3 conv holds [cout, cin, 3, 3, 3] weights and runs as a causal
+ * 3x3x3 conv (time front-padded with two copies of frame 0, h and w
+ * zero-padded), kernel-1 convs are 1x1x1 ([cout, cin]); GroupNorm statistics
+ * span (C/32) x T x H x W; the mid attention runs over all t*h*w positions
+ * (row-major over t, y, x); upsampling doubles h and w only.  The handle is
+ * used with vae_decoder3d_workspace_bytes / vae_decode3d (the 2-D calls
+ * reject it and vice versa); destroy, output shape, GroupNorm mode and
+ * profiling calls are shared. */
+int32_t vae_decoder3d_pack_bytes(const vae_weights *w, size_t *bytes);
+int32_t vae_decoder3d_create(vae_decoder **out, const vae_weights *w, void *pack, size_t pack_bytes,
+                             void *stream);
+int32_t vae_decoder3d_workspace_bytes(const vae_decoder *d, int32_t t, int32_t h, int32_t w, size_t *bytes);
+/* latent [latent_channels, t, h, w] -> rgb [out_channels, t, 8h, 8w]. */
+int32_t vae_decode3d(vae_decoder *d, const float *latent, int32_t t, int32_t h, int32_t w, float *rgb,
+                     void *ws, size_t ws_bytes, void *stream);
 
 /* Output spatial scale of the chain (8 for four up blocks) and its channels. */
 int32_t vae_decoder_output_shape(const vae_decoder *d, int32_t h, int32_t w, int32_t *c,

@@ -212,3 +212,17 @@ def test_decoder_pack_and_validation(lib):
     assert lib.vae_decoder_pack_bytes(byref(w6), byref(nb)) == VAE_ERR_INVALID_ARG
     assert lib.vae_decode(NULL, FAKE, 8, 8, FAKE, FAKE, 1, NULL) == VAE_ERR_INVALID_ARG
     assert lib.vae_decoder_set_profiling(NULL, 1) == VAE_ERR_INVALID_ARG
+
+
+def test_decoder3d_pack_and_validation(lib):
+    w, keep = fake_weights()
+    n2, n3 = c_size_t(), c_size_t()
+    assert lib.vae_decoder_pack_bytes(byref(w), byref(n2)) == VAE_OK
+    assert lib.vae_decoder3d_pack_bytes(byref(w), byref(n3)) == VAE_OK, err(lib)
+    # three time taps per 3x3 conv: about three times the 3x3 weights (and conv_out packed too)
+    assert 2.7 * n2.value < n3.value < 3.1 * n2.value
+    h = c_void_p()
+    assert lib.vae_decoder3d_create(byref(h), byref(w), FAKE, n3.value - 1, NULL) == VAE_ERR_WORKSPACE
+    assert lib.vae_decode3d(NULL, FAKE, 2, 8, 8, FAKE, FAKE, 1, NULL) == VAE_ERR_INVALID_ARG
+    nb = c_size_t()
+    assert lib.vae_decoder3d_workspace_bytes(NULL, 2, 8, 8, byref(nb)) == VAE_ERR_INVALID_ARG

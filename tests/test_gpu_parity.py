@@ -8,6 +8,7 @@ Bars (per layer): max|gpu - ref| / max|ref| <= 1e-4 over the layer output.
 End to end (RGB): cosine >= 0.99999 and max|gpu - ref| <= 1e-3 * max|ref|.
 Exact copies (upsample) must be bit-identical.
 """
+import ctypes
 import math
 import os
 
@@ -371,3 +372,50 @@ def test_decode_is_deterministic(decoder):
     a = decoder.decode(z).cpu()
     b = decoder.decode(z).cpu()
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# the causal 3-D decoder
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def params3d():
+    return vaegen.decoder_params(0, dims=3)
+
+
+@pytest.fixture(scope="module")
+def decoder3d(api, params3d):
+    d = api.Decoder({k: dev(v) for k, v in params3d.items()}, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR,
+                    causal3d=True)
+    yield d
+    d.close()
+
+
+# clips: one frame, three frames, a ragged spatial size over two frames
+@pytest.mark.parametrize("t,h,w", [(1, 4, 4), (3, 4, 4), (2, 5, 3)])
+def test_decode_causal3d(decoder3d, params3d, t, h, w):
+    z = vaegen.latent3d(2, t, h, w)
+    rgb = decoder3d.decode(dev(z), out=nan_like((3, t, 8 * h, 8 * w)))
+    ref = oracle.decode_causal3d(z, params3d, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    cos, mx = rgb_metrics(host(rgb), ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
+def test_decode_causal3d_with_groupnorm_on_load(decoder3d, params3d):
+    z = vaegen.latent3d(3, 2, 4, 4)
+    decoder3d.set_groupnorm_fusion(True)
+    try:
+        got = host(decoder3d.decode(dev(z), out=nan_like((3, 2, 32, 32))))
+    finally:
+        decoder3d.set_groupnorm_fusion(False)
+    ref = oracle.decode_causal3d(z, params3d, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    cos, mx = rgb_metrics(got, ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
+def test_decode_causal3d_rejects_2d_calls(api, decoder3d, decoder):
+    lib = api._lib_()
+    nb = ctypes.c_size_t()
+    assert lib.vae_decoder_workspace_bytes(decoder3d._h, 4, 4, ctypes.byref(nb)) != 0
+    assert lib.vae_decoder3d_workspace_bytes(decoder._h, 1, 4, 4, ctypes.byref(nb)) != 0
+    assert "3-D" in lib.vae_last_error().decode()
