@@ -20,6 +20,8 @@ the device and the latent already resident in HBM.  Default workload: latent
   secondary    the 256x256 decode (latent [16,32,32])
   sweep        the single-layer sweep at full size (3x3 and 1x1 convs,
                GroupNorm+SiLU) and a standalone nearest-x2 upsample
+  stack3d      the causal 3-D conv stack on [128,17,256,256]
+  decode3d     the causal 3-D decoder on a latent [16,17,32,32]
 """
 from __future__ import annotations
 
@@ -52,6 +54,7 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the second decode size (keeps profiler summaries to one workload)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the single-layer sweep")
+    ap.add_argument("--no-3d", action="store_true", help="skip the causal 3-D stack and decode")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the decodes, run one plain device copy of this many MiB "
@@ -170,6 +173,73 @@ def sweep(args) -> dict:
     return out
 
 
+def stack3d(args) -> dict:
+    """The causal 3-D conv stack at full size: x [128,17,256,256], four
+    (3x3x3 causal conv -> GroupNorm32+SiLU) layers with the residual added
+    after every second layer, through the per-layer entry points."""
+    import torch
+    from diffusion_vae_decoder_amd import api
+    c, t, h = 128, 17, 256
+    p = {k: torch.from_numpy(v).cuda() for k, v in vaegen.causal_stack_params(args.seed, c=c).items()}
+    x0 = torch.from_numpy(vaegen.activation(args.seed, "stack3d.x", (c, t, h, h))).cuda()
+    bufs = [torch.empty_like(x0) for _ in range(3)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+
+    def step(e=None):
+        # x1 = x0 + L1(L0(x0)) in B, then x2 = x1 + L3(L2(x1)) in C; A holds the first layer of a pair
+        A, B, C = bufs
+        plan = [(x0, A, None, 0), (A, B, x0, 1), (B, A, None, 2), (A, C, B, 3)]
+        for k, (src, dst, res, j) in enumerate(plan):
+            if e: e[2 * k].record()
+            api.conv3d_causal(src, p[f"stack.{j}.conv.weight"], p[f"stack.{j}.conv.bias"], out=dst)
+            if e: e[2 * k + 1].record()
+            api.groupnorm_silu(dst, p[f"stack.{j}.norm.weight"], p[f"stack.{j}.norm.bias"], residual=res, out=dst)
+        return C
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    conv_ms = sum(ev[i][2 * k].elapsed_time(ev[i][2 * k + 1]) for i in range(args.steps) for k in range(4)) / args.steps
+    fl = 4 * 2.0 * c * c * 27 * t * h * h
+    return {"workload": f"causal 3-D conv stack, x [{c},{t},{h},{h}], 4 x (3x3x3 conv + GroupNorm32+SiLU)",
+            "ms_per_step": ms, "tflops": fl / ms / 1e9, "conv_ms": conv_ms, "conv_tflops": fl / conv_ms / 1e9,
+            "conv_frac_fp32_mfma_peak": fl / conv_ms / 1e9 / PEAK_FP32_MFMA_TFLOPS,
+            "note": "each conv call includes its weight repack"}
+
+
+def decode3d(args, t: int = 17, h: int = 32) -> dict:
+    """The causal 3-D decoder on a latent [16, t, h, h] -> RGB [3, t, 8h, 8h]."""
+    import torch
+    from diffusion_vae_decoder_amd import api
+    prm = vaegen.decoder_params(args.seed, dims=3)
+    dec = api.Decoder({k: torch.from_numpy(v).cuda() for k, v in prm.items()}, vaegen.SCALING_FACTOR,
+                      vaegen.SHIFT_FACTOR, causal3d=True)
+    z = torch.from_numpy(vaegen.latent3d(args.seed, t, h, h)).cuda()
+    rgb = torch.empty((3, t, 8 * h, 8 * h), device="cuda")
+    for _ in range(max(args.warmup, 1)):
+        dec.decode(z, out=rgb)
+    dec.set_profiling(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dec.decode(z, out=rgb)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    recs = dec.profile()
+    dec.set_profiling(False)
+    dec.close()
+    conv = [r for r in recs if r["kernel"].startswith("conv3x3_mfma")]
+    conv_tf = sum(r["flops"] for r in conv) / (sum(r["ms"] for r in conv) / 1e3) / 1e12
+    return {"workload": f"causal 3-D decode, latent [16,{t},{h},{h}] -> RGB [3,{t},{8 * h},{8 * h}]",
+            "ms_per_step": ms, "tflops": sum(r["flops"] for r in recs) / args.steps / (ms / 1e3) / 1e12,
+            "conv3x3x3_tflops": conv_tf, "conv3x3x3_frac_fp32_mfma_peak": conv_tf / PEAK_FP32_MFMA_TFLOPS}
+
+
 def secondary(dec, args, h2: int) -> dict:
     """W warm-ups then K timed decodes of a latent [16,h2,h2], per-launch events on."""
     import torch
@@ -283,6 +353,9 @@ def main():
         out["secondary"] = secondary(dec, args, 32 if h != 32 else 128)
     if not args.no_sweep:
         out["sweep"] = sweep(args)
+    if not args.no_3d:
+        out["stack3d"] = stack3d(args)
+        out["decode3d"] = decode3d(args)
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
