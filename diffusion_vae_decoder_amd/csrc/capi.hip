@@ -82,7 +82,7 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 size_t conv_ws(const vae_conv *c, int kt, int T, int H, int W) {
     if (c->kernel == 1) return gemm_partial_floats(c->out_channels, H * W, c->in_channels, false) * sizeof(float);
     if (kt == 1 && c->out_channels <= 4)   // direct kernel (or, with upsample / residual, the implicit GEMM)
-        return std::max(conv3x3_direct_partial_floats(c->out_channels, c->in_channels, H, W) * sizeof(float),
+        return std::max(conv3x3_direct_partial_floats(c->out_channels, c->in_channels, 1, H, W, 1) * sizeof(float),
                         align256(conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float)) +
                             conv3x3_partial_floats(c->out_channels, c->in_channels, kt, H, W, T) * sizeof(float));
     return align256(conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float)) +

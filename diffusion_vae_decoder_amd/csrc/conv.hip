@@ -32,9 +32,8 @@
 // an LDS table.  It removes the separate normalisation pass but costs about
 // 10% of the conv on MI355X, more than that pass.
 //
-// conv3x3_direct: the 128 -> 3 conv_out.  With 3 output channels the GEMM is
-// far too thin for MFMA; a direct FMA kernel over LDS-staged halo tiles
-// streams the input once (optionally normalising it on load).
+// The decoder's conv_out (3 output channels) runs on conv3x3_direct in
+// conv_direct.hip.
 
 #include <cstdio>
 
@@ -515,173 +514,6 @@ void launch_tc(const Params &p, int mode, bool res, bool split, dim3 grid, hipSt
     }
 }
 
-// ---------------------------------------------------------------- conv_out
-// Direct 3x3 conv for a handful of output channels.  Workgroup tile: 8 rows x
-// 128 columns; thread (r, g) computes pixels 4g..4g+3 of row r for every
-// output channel.  Input channels go in chunks of 4: the chunk's halo tile
-// [4][10][128 + 2] is loaded into registers (float4 loads for the 128
-// interior columns, one scalar per row edge) while the previous chunk is
-// being used, then written to LDS.  The weights are the same for the whole
-// workgroup and are read through the scalar cache.
-constexpr int kDR = 8;                 // tile rows
-constexpr int kDC = 128;               // tile columns
-constexpr int kDCC = 4;                // input channels per chunk
-constexpr int kDRow = kDC + 8;         // LDS row: [pad x3][left][128 interior][right][pad x3]
-constexpr int kDRows = kDR + 2;
-constexpr int kDQuads = kDCC * kDRows * (kDC / 4);            // float4 items per chunk (1280)
-constexpr int kDQPerT = (kDQuads + kThreads - 1) / kThreads;  // 5
-constexpr int kDEdges = kDCC * kDRows * 2;                    // scalar edge items per chunk (80)
-
-// blockIdx.y = split: with several splits, split s sums the chunks
-// [s * n / splits, (s + 1) * n / splits) into part[s] (no bias) and
-// splitk_reduce adds the splits in order.
-template <int COUT, bool GN>
-__global__ __launch_bounds__(kThreads) void conv3x3_direct(const float *__restrict__ x,
-                                                           const float *__restrict__ w,
-                                                           const float *__restrict__ bias,
-                                                           float *__restrict__ y, int cin, int H,
-                                                           int W, int tiles_x,
-                                                           const float *__restrict__ gn_coef,
-                                                           float *__restrict__ part) {
-    __shared__ __attribute__((aligned(16))) float halo[kDCC * kDRows * kDRow];
-    __shared__ float lc[GN ? 3 * (kGnMaxChannels + kDCC) : 1];
-    const int tid = threadIdx.x;
-    const int ty = blockIdx.x / tiles_x, tx = blockIdx.x - (blockIdx.x / tiles_x) * tiles_x;
-    const int y0 = ty * kDR, x0 = tx * kDC;
-    const int r = tid >> 5, g = tid & 31;
-    const long long plane = (long long)H * W;
-    // interior columns of this tile all inside the image and rows 16-byte aligned
-    const bool vec = (W & 3) == 0 && x0 + kDC <= W && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-    const bool vec_out = (W & 3) == 0 && x0 + kDC <= W &&
-                         (reinterpret_cast<uintptr_t>(part ? part : y) & 15) == 0;
-    const int n_chunks = (cin + kDCC - 1) / kDCC;
-    const int cb0 = (int)((long long)blockIdx.y * n_chunks / gridDim.y);
-    const int cb1 = (int)((long long)(blockIdx.y + 1) * n_chunks / gridDim.y);
-
-    if (GN) {
-        for (int e = tid; e < 3 * n_chunks * kDCC; e += kThreads) {
-            const int c = e / 3, k = e - 3 * (e / 3);
-            lc[e] = c < cin ? gn_coef[4 * c + k] : 0.f;
-        }
-    }
-
-    floatx4 q[kDQPerT];
-    float edge = 0.f;
-    auto gn = [&](float v, int c) {
-        const float *cf = lc + 3 * c;
-        const float t = (v - cf[0]) * cf[1] + cf[2];
-        return t * __builtin_amdgcn_rcpf(1.f + __expf(-t));
-    };
-    // global -> registers for chunk starting at channel c0
-    auto load = [&](int c0) {
-#pragma unroll
-        for (int j = 0; j < kDQPerT; ++j) {
-            const int k = tid + j * kThreads;
-            floatx4 v = {0.f, 0.f, 0.f, 0.f};
-            if (k < kDQuads) {
-                const int c = k / (kDRows * 32), rem = k - c * (kDRows * 32);
-                const int row = rem >> 5, qq = rem & 31;
-                const int ch = c0 + c, yy = y0 - 1 + row, xx = x0 + 4 * qq;
-                if (ch < cin && yy >= 0 && yy < H) {
-                    const float *src = x + ch * plane + (long long)yy * W + xx;
-                    if (vec) {
-                        v = *reinterpret_cast<const floatx4 *>(src);
-                        if (GN) {
-                            v[0] = gn(v[0], ch);
-                            v[1] = gn(v[1], ch);
-                            v[2] = gn(v[2], ch);
-                            v[3] = gn(v[3], ch);
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (xx + e < W) v[e] = GN ? gn(src[e], ch) : src[e];
-                    }
-                }
-            }
-            q[j] = v;
-        }
-        if (tid < kDEdges) {
-            const int c = tid / (2 * kDRows), rem = tid - c * (2 * kDRows);
-            const int row = rem >> 1, side = rem & 1;
-            const int ch = c0 + c, yy = y0 - 1 + row, xx = side ? x0 + kDC : x0 - 1;
-            float v = 0.f;
-            if (ch < cin && yy >= 0 && yy < H && xx >= 0 && xx < W) {
-                v = x[ch * plane + (long long)yy * W + xx];
-                if (GN) v = gn(v, ch);
-            }
-            edge = v;
-        }
-    };
-    auto store = [&]() {
-#pragma unroll
-        for (int j = 0; j < kDQPerT; ++j) {
-            const int k = tid + j * kThreads;
-            if (k < kDQuads) {
-                const int c = k / (kDRows * 32), rem = k - c * (kDRows * 32);
-                const int row = rem >> 5, qq = rem & 31;
-                *reinterpret_cast<floatx4 *>(&halo[(c * kDRows + row) * kDRow + 4 + 4 * qq]) = q[j];
-            }
-        }
-        if (tid < kDEdges) {
-            const int c = tid / (2 * kDRows), rem = tid - c * (2 * kDRows);
-            const int row = rem >> 1, side = rem & 1;
-            halo[(c * kDRows + row) * kDRow + (side ? 4 + kDC : 3)] = edge;
-        }
-    };
-
-    float acc[COUT][4];
-#pragma unroll
-    for (int o = 0; o < COUT; ++o)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[o][e] = 0.f;
-
-    if (GN) __syncthreads();   // coefficient table
-    load(cb0 * kDCC);
-    for (int cb = cb0; cb < cb1; ++cb) {
-        const int c0 = cb * kDCC;
-        store();
-        __syncthreads();
-        if (cb + 1 < cb1) load(c0 + kDCC);
-#pragma unroll
-        for (int c = 0; c < kDCC; ++c) {
-            const int ch = c0 + c;
-            if (ch >= cin) break;
-#pragma unroll
-            for (int dy = 0; dy < 3; ++dy) {
-                const float *row = &halo[(c * kDRows + r + dy) * kDRow + 4 * g + 3];
-                const floatx4 mid = *reinterpret_cast<const floatx4 *>(row + 1);
-                const float v[6] = {row[0], mid[0], mid[1], mid[2], mid[3], row[5]};
-#pragma unroll
-                for (int dx = 0; dx < 3; ++dx)
-#pragma unroll
-                    for (int o = 0; o < COUT; ++o) {
-                        const float wv = w[((long long)o * cin + ch) * 9 + dy * 3 + dx];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[o][e] = fmaf(wv, v[e + dx], acc[o][e]);
-                    }
-            }
-        }
-        __syncthreads();
-    }
-    const int yy = y0 + r;
-    if (yy >= H) return;
-    const int xx = x0 + 4 * g;
-    float *out = part ? part + (long long)blockIdx.y * COUT * plane : y;
-#pragma unroll
-    for (int o = 0; o < COUT; ++o) {
-        const float b = part ? 0.f : bias[o];
-        float *dst = out + o * plane + (long long)yy * W + xx;
-        if (vec_out) {
-            *reinterpret_cast<floatx4 *>(dst) = floatx4{acc[o][0] + b, acc[o][1] + b, acc[o][2] + b, acc[o][3] + b};
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (xx + e < W) dst[e] = acc[o][e] + b;
-        }
-    }
-}
-
 }  // namespace
 
 size_t conv3x3_packed_floats(int cout, int cin, int kt) {
@@ -848,67 +680,18 @@ int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s) {
     return launch_conv3x3_reduce(a, s);
 }
 
-namespace {
-constexpr int kDirectSlots = 1024;   // about 4 conv_out workgroups per CU
-}
-
-int conv3x3_direct_splits(int cin, int H, int W) {
-    const long long tiles = (long long)((W + kDC - 1) / kDC) * ((H + kDR - 1) / kDR);
-    const int n_chunks = (cin + kDCC - 1) / kDCC;
-    if (tiles * 2 >= kDirectSlots) return 1;
-    long long s = (kDirectSlots + tiles - 1) / tiles;
-    if (s > n_chunks / 4) s = n_chunks / 4;   // each split keeps >= 4 chunks (16 channels)
-    if (s > 16) s = 16;
-    return s < 2 ? 1 : (int)s;
-}
-
-size_t conv3x3_direct_partial_floats(int cout, int cin, int H, int W) {
-    const int sp = conv3x3_direct_splits(cin, H, W);
-    return sp > 1 ? (size_t)sp * cout * H * W : 0;
-}
-
-int32_t launch_conv3x3_direct(const float *x, const float *w, const float *bias, float *y, int cin,
-                              int cout, int H, int W, hipStream_t s, const float *gn_coef, float *part) {
-    if (gn_coef && cin > kGnMaxChannels) {
-        set_error("conv3x3_direct: GroupNorm-on-load holds at most %d input channels", kGnMaxChannels);
-        return VAE_ERR_UNSUPPORTED;
-    }
-    const int splits = conv3x3_direct_splits(cin, H, W);
-    if (splits > 1 && !part) {
-        set_error("conv3x3_direct: a split shape needs a partial-sum workspace");
-        return VAE_ERR_WORKSPACE;
-    }
-    float *pp = splits > 1 ? part : nullptr;
-    const int tiles_x = (W + kDC - 1) / kDC;
-    const int tiles_y = (H + kDR - 1) / kDR;
-    const dim3 grid((unsigned)(tiles_x * tiles_y), (unsigned)splits);
-#define VAE_DIRECT(N)                                                                                        \
-    if (gn_coef)                                                                                             \
-        hipLaunchKernelGGL((conv3x3_direct<N, true>), grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W,  \
-                           tiles_x, gn_coef, pp);                                                            \
-    else                                                                                                     \
-        hipLaunchKernelGGL((conv3x3_direct<N, false>), grid, dim3(kThreads), 0, s, x, w, bias, y, cin, H, W, \
-                           tiles_x, gn_coef, pp);
-    switch (cout) {
-        case 1: VAE_DIRECT(1) break;
-        case 2: VAE_DIRECT(2) break;
-        case 3: VAE_DIRECT(3) break;
-        case 4: VAE_DIRECT(4) break;
-        default: set_error("conv3x3_direct: out_channels %d > 4", cout); return VAE_ERR_UNSUPPORTED;
-    }
-#undef VAE_DIRECT
-    int32_t rc = check_launch("conv3x3_direct");
-    if (rc != VAE_OK || splits == 1) return rc;
-    const long long plane = (long long)H * W;
-    const dim3 rgrid((unsigned)((plane + kRedElems - 1) / kRedElems), (unsigned)cout);
+int32_t launch_rows_reduce(const float *part, long long part_stride, int splits, const float *bias, float *y,
+                           long long plane, int rows, hipStream_t s) {
+    const dim3 rgrid((unsigned)((plane + kRedElems - 1) / kRedElems), (unsigned)rows);
     const bool vec = plane % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(part) & 15) == 0;
+                     (reinterpret_cast<uintptr_t>(part) & 15) == 0 && part_stride % 4 == 0;
     if (vec)
-        hipLaunchKernelGGL((splitk_reduce<true, false>), rgrid, dim3(kThreads), 0, s, part, plane * cout, splits,
+        hipLaunchKernelGGL((splitk_reduce<true, false>), rgrid, dim3(kThreads), 0, s, part, part_stride, splits,
                            bias, nullptr, y, plane, nullptr, 0);
     else
-        hipLaunchKernelGGL((splitk_reduce<false, false>), rgrid, dim3(kThreads), 0, s, part, plane * cout, splits,
+        hipLaunchKernelGGL((splitk_reduce<false, false>), rgrid, dim3(kThreads), 0, s, part, part_stride, splits,
                            bias, nullptr, y, plane, nullptr, 0);
     return check_launch("splitk_reduce");
 }
+
 }  // namespace vae

@@ -92,7 +92,7 @@ struct Packer {
         d.cin = c.in_channels;
         d.k = c.kernel;
         if (c.kernel == 3 && raw3) {
-            d.w = copy(c.weight, (size_t)c.out_channels * c.in_channels * 9);
+            d.w = copy(c.weight, (size_t)c.out_channels * c.in_channels * 9 * kt);
         } else if (c.kernel == 3) {
             const float *p = take(conv3x3_packed_floats(c.out_channels, c.in_channels, kt));
             if (dst && rc == VAE_OK) rc = pack_conv3x3(c.weight, c.out_channels, c.in_channels, kt, const_cast<float *>(p), s);
@@ -314,7 +314,7 @@ Plan plan_for(const vae_decoder *d, int T, int h, int w) {
     }
     gn(d->norm_out.c, H, W);
     if (d->direct_out) {
-        const size_t n = conv3x3_direct_partial_floats(d->conv_out.cout, d->conv_out.cin, (int)H, (int)W);
+        const size_t n = conv3x3_direct_partial_floats(d->conv_out.cout, d->conv_out.cin, kt, (int)H, (int)W, T);
         if (n > p.part) p.part = n;
     } else {
         part(d->conv_out, H, W);
@@ -500,7 +500,7 @@ int32_t pack_bytes_kt(const vae_weights *w, int kt, size_t *bytes, const char *w
         if (w->ups[i].upsample.weight) p.conv(w->ups[i].upsample);
     }
     p.norm(w->norm_out);
-    p.conv(w->conv_out, kt == 1 && w->conv_out.out_channels <= 4);
+    p.conv(w->conv_out, w->conv_out.out_channels <= 4);
     *bytes = p.off;
     return VAE_OK;
 }
@@ -517,7 +517,7 @@ int32_t create_kt(vae_decoder **out, const vae_weights *w, int kt, void *pack, s
         return fail(VAE_ERR_INVALID_ARG, "%s: pack buffer must be 256-byte aligned", who);
     vae_decoder *d = new vae_decoder();
     d->kt = kt;
-    d->direct_out = kt == 1 && w->conv_out.out_channels <= 4;
+    d->direct_out = w->conv_out.out_channels <= 4;
     Packer p{static_cast<char *>(pack), 0, static_cast<hipStream_t>(stream)};
     p.kt = kt;
     d->conv_in = p.conv(w->conv_in);
@@ -623,10 +623,9 @@ int32_t decode_t(vae_decoder *d, const float *latent, int T, int h, int w, float
         }
     }
     // norm_out + SiLU, conv_out.  A conv_out with at most 4 outputs is bound
-    // by reading its input, so it normalises while loading (only the
-    // statistics are computed before it): the direct kernel for images, the
-    // implicit GEMM with three time taps for clips.  A wider conv_out follows
-    // the decoder's GroupNorm mode.
+    // by reading its input: the direct kernel (three time taps for clips)
+    // normalises while loading, so only the statistics are computed before
+    // it.  A wider conv_out follows the decoder's GroupNorm mode.
     const DConv &c = d->conv_out;
     const long long sp = (long long)T * H * W;
     const bool fused = (c.cout <= 4 && c.cin <= kDirectGnMaxChannels) || d->gn_fused;
@@ -635,10 +634,11 @@ int32_t decode_t(vae_decoder *d, const float *latent, int T, int h, int w, float
     else r.gn("conv_norm_out", d->norm_out, b.X, sp, b.T, b.gn);
     if (r.rc == VAE_OK) {
         if (d->direct_out) {
-            ProfEntry *e = r.begin("conv3x3_direct", "conv_out", conv_flops(c, H, W, 1), 4.0 * (c.cin + c.cout) * (double)H * W);
+            ProfEntry *e = r.begin("conv3x3_direct", "conv_out", conv_flops(c, H, W, d->kt) * T,
+                                   4.0 * (c.cin + c.cout) * (double)T * H * W);
             if (r.rc == VAE_OK) {
                 r.rc = launch_conv3x3_direct(cin_x, c.w, c.b, rgb, c.cin, c.cout, H, W, r.s, fused ? b.coef : nullptr,
-                                             b.part);
+                                             b.part, T, d->kt);
                 r.end(e);
             }
         } else {

@@ -68,15 +68,21 @@ int conv3x3_gn_records(const ConvLaunch &a);
 // Name of the kernel instantiation launch_conv3x3 picks for `a`.
 const char *conv3x3_kernel_name(const ConvLaunch &a);
 
+// y[o, :] = bias[o] + sum_s part[s * part_stride + o * plane + :] over `splits`
+// partial-sum slices, in slice order, for `rows` rows of `plane` elements.
+int32_t launch_rows_reduce(const float *part, long long part_stride, int splits, const float *bias, float *y,
+                           long long plane, int rows, hipStream_t s);
+
 // Direct conv for out_channels <= 4 (conv_out); gn_coef as in ConvLaunch (may be nullptr,
 // else at most kDirectGnMaxChannels input channels).
 constexpr int kDirectGnMaxChannels = 512;
 // Shapes with too few tiles split the input channels; the partial sums then
-// need conv3x3_direct_partial_floats() floats in `part`.
+// need conv3x3_direct_partial_floats() floats in `part`.  kt = 3: the causal
+// 3x3x3 conv of a clip of T frames, weights [cout, cin, 3, 3, 3].
 int32_t launch_conv3x3_direct(const float *x, const float *w, const float *bias, float *y,
                               int cin, int cout, int H, int W, hipStream_t s,
-                              const float *gn_coef, float *part);
-size_t conv3x3_direct_partial_floats(int cout, int cin, int H, int W);
+                              const float *gn_coef, float *part, int T = 1, int kt = 1);
+size_t conv3x3_direct_partial_floats(int cout, int cin, int kt, int H, int W, int T);
 
 // ------------------------------------------------------------------ GEMM
 // C[m, n] = alpha * sum_k A(m, k) B(k, n) + bias[m] (+ R[m, n]).
