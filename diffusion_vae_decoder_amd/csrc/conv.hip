@@ -97,32 +97,64 @@ __device__ __attribute__((always_inline)) inline __amdgpu_buffer_rsrc_t make_rsr
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Global -> registers: chunk `it` = (time tap dt, channel block cb) of the
-// packed weights and of the input halo.  The halo buffer range covers only the
-// chunk's valid channels, so channels past cin and padding positions (offset
-// kOOB) both read as 0 with no branch.
+// The K chunk a workgroup stages next: time tap dt, channel block cb, the
+// chunk's packed weights and its first input channel in the time tap's
+// frame.  Advanced by additions only; the frame is recomputed when the time
+// tap changes (at most kt - 1 times).
+struct Cursor {
+    int dt, cb;
+    const float *w;    // packed weight chunk
+    const float *x;    // input channel cb * 4 of frame max(frame + dt - (kt - 1), 0)
+};
+
+__device__ __attribute__((always_inline)) inline const float *frame_base(const Params &p, int frame, int dt) {
+    int fr = frame + dt - (p.kt - 1);
+    fr = fr < 0 ? 0 : fr;
+    return p.x + (long long)fr * p.in_fstride;
+}
+
+__device__ __attribute__((always_inline)) inline Cursor cursor_at(const Params &p, const float *wbase, int it,
+                                                                 int frame) {
+    Cursor c;
+    c.dt = it / p.n_cb;
+    c.cb = it - c.dt * p.n_cb;
+    c.w = wbase + (size_t)it * (kCK * kConvBM);
+    c.x = frame_base(p, frame, c.dt) + (long long)c.cb * kConvCC * p.in_cstride;
+    return c;
+}
+
+__device__ __attribute__((always_inline)) inline void cursor_next(const Params &p, int frame, Cursor &c) {
+    c.w += kCK * kConvBM;
+    if (++c.cb == p.n_cb) {
+        c.cb = 0;
+        ++c.dt;
+        c.x = frame_base(p, frame, c.dt);
+    } else {
+        c.x += kConvCC * p.in_cstride;
+    }
+}
+
+// Global -> registers: the chunk at cursor `cur` of the packed weights and of
+// the input halo.  The halo buffer range covers only the chunk's valid
+// channels, so channels past cin and padding positions (offset kOOB) both
+// read as 0 with no branch.
 template <int TC, int MODE>
 __device__ __attribute__((always_inline)) inline void stage_load(
-    const Params &p, const float *wbase, int it, int frame, const int (&h_boff)[Geom<TC>::HALO_PER_T],
+    const Params &p, const Cursor &cur, const int (&h_boff)[Geom<TC>::HALO_PER_T],
     const int (&h_c)[Geom<TC>::HALO_PER_T], floatx4 (&wreg)[kW4_PER_T],
     float (&xreg)[Geom<TC>::HALO_PER_T], bool (&vmask)[Geom<TC>::HALO_PER_T]) {
     using G = Geom<TC>;
     const int tid = threadIdx.x;
-    const int dt = it / p.n_cb;
-    const int cb = it - dt * p.n_cb;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wbase + (size_t)it * (kCK * kConvBM), kCK * kConvBM * 4);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(cur.w, kCK * kConvBM * 4);
 #pragma unroll
     for (int i = 0; i < kW4_PER_T; ++i) {
         const int idx = tid + i * kThreads;
         if (kW4 % kThreads == 0 || (i + 1) * kThreads <= kW4 || idx < kW4)
             wreg[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(wr, idx * 16, 0, 0));
     }
-    int fr = frame + dt - (p.kt - 1);
-    fr = fr < 0 ? 0 : fr;
-    const int c0 = cb * kConvCC;
+    const int c0 = cur.cb * kConvCC;
     const int nc = p.cin - c0 < kConvCC ? p.cin - c0 : kConvCC;
-    const float *xs = p.x + (long long)fr * p.in_fstride + (long long)c0 * p.in_cstride;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(xs, (unsigned)(nc * p.in_cstride * 4));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(cur.x, (unsigned)(nc * p.in_cstride * 4));
 #pragma unroll
     for (int i = 0; i < G::HALO_PER_T; ++i) {
         float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xr, h_boff[i], 0, 0));
@@ -263,13 +295,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    stage_load<TC, MODE>(p, wbase, it0, frame, h_boff, h_c, wreg, xreg, vmask);
-    stage_store<TC, MODE>(lds_w[0], lds_x[0], h_lds, wreg, xreg, vmask, h_c, lds_c, (it0 % p.n_cb) * kConvCC);
+    Cursor cur = cursor_at(p, wbase, it0, frame);
+    stage_load<TC, MODE>(p, cur, h_boff, h_c, wreg, xreg, vmask);
+    stage_store<TC, MODE>(lds_w[0], lds_x[0], h_lds, wreg, xreg, vmask, h_c, lds_c, cur.cb * kConvCC);
     __syncthreads();
 
     for (int it = it0; it < it1; ++it) {
         const int buf = (it - it0) & 1;
-        if (it + 1 < it1) stage_load<TC, MODE>(p, wbase, it + 1, frame, h_boff, h_c, wreg, xreg, vmask);
+        if (it + 1 < it1) {
+            cursor_next(p, frame, cur);
+            stage_load<TC, MODE>(p, cur, h_boff, h_c, wreg, xreg, vmask);
+        }
         const float *A = lds_w[buf];
         const float *B = lds_x[buf];
 #pragma unroll
@@ -285,7 +321,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
             acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
         }
-        if (it + 1 < it1) stage_store<TC, MODE>(lds_w[buf ^ 1], lds_x[buf ^ 1], h_lds, wreg, xreg, vmask, h_c, lds_c, ((it + 1) % p.n_cb) * kConvCC);
+        if (it + 1 < it1) stage_store<TC, MODE>(lds_w[buf ^ 1], lds_x[buf ^ 1], h_lds, wreg, xreg, vmask, h_c, lds_c, cur.cb * kConvCC);
         __syncthreads();
     }
 
