@@ -334,8 +334,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const int n = wn * 64 + j * 32 + l32;
         pv[j] = y0 + n / TC < p.H && x0 + (n - (n / TC) * TC) < p.W;
     }
+    // Per 32-row half of the wave's block, the residual (conv2 of a resnet)
+    // is read first, 32 values with no branch (positions outside the image
+    // read an in-bounds neighbour and are never stored), then added and stored.
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+        float rv[2][16];
+        if (RES && !SPLIT) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int n = wn * 64 + j * 32 + l32;
+                const int yy = min(y0 + n / TC, p.H - 1), xx = min(x0 + (n - (n / TC) * TC), p.W - 1);
+                const long long sp = fo + (long long)yy * p.W + xx;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int o = min(ob * kConvBM + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3), p.cout - 1);
+                    rv[j][r] = p.res[(long long)o * p.out_cstride + sp];
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             if (!pv[j]) continue;
@@ -351,7 +368,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                         p.part[split * p.part_stride + off] = acc[i][j][r];
                     } else {
                         float v = acc[i][j][r] + p.bias[o];
-                        if (RES) v += p.res[off];
+                        if (RES) v += rv[j][r];
                         p.y[off] = v;
                         acc[i][j][r] = v;
                     }
