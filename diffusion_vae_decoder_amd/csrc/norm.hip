@@ -280,11 +280,6 @@ __global__ void upsample2x_scalar(const float *__restrict__ x, float *__restrict
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-size_t groupnorm_ws_bytes(int c, long long spatial) {
-    const long long gsize = (long long)(c / kGroups) * spatial;
-    return (size_t)kGroups * parts_for(gsize) * 2 * sizeof(double) + kGroups * sizeof(double);
-}
-
 // Statistics of x's 32 groups into ws: from the records a producer wrote
 // (one merged part per group) or from a pass over x.  Returns the parts.
 int32_t groupnorm_stats(const float *x, int c, long long spatial, void *ws, hipStream_t s, const floatx4 *rec,
