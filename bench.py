@@ -240,6 +240,24 @@ def decode3d(args, t: int = 17, h: int = 32) -> dict:
             "conv3x3x3_tflops": conv_tf, "conv3x3x3_frac_fp32_mfma_peak": conv_tf / PEAK_FP32_MFMA_TFLOPS}
 
 
+def graph_replay_ms(dec, z, steps: int, warmup: int) -> float:
+    """Wall ms per decode with the decoder's HIP-graph replay on (no events)."""
+    import torch
+    out = torch.empty(dec.output_shape(z.shape[-2], z.shape[-1]), device="cuda") if z.dim() == 3 else None
+    dec.set_graph(True)
+    try:
+        for _ in range(max(warmup, 1)):
+            out = dec.decode(z, out=out)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            dec.decode(z, out=out)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+    finally:
+        dec.set_graph(False)
+
+
 def secondary(dec, args, h2: int) -> dict:
     """W warm-ups then K timed decodes of a latent [16,h2,h2], per-launch events on."""
     import torch
@@ -258,7 +276,7 @@ def secondary(dec, args, h2: int) -> dict:
     c2 = [r for r in recs2 if r["kernel"].startswith("conv3x3_mfma")]
     c2_tf = sum(r["flops"] for r in c2) / (sum(r["ms"] for r in c2) / 1e3) / 1e12
     return {"workload": f"decode latent [16,{h2},{h2}] -> RGB [3,{8 * h2},{8 * h2}]",
-            "ms_per_step": ms2,
+            "ms_per_step": ms2, "ms_per_step_graph_replay": graph_replay_ms(dec, z2, args.steps, args.warmup),
             "tflops": sum(r["flops"] for r in recs2) / args.steps / (ms2 / 1e3) / 1e12,
             "conv3x3_tflops": c2_tf, "conv3x3_frac_fp32_mfma_peak": c2_tf / PEAK_FP32_MFMA_TFLOPS}
 
@@ -348,6 +366,7 @@ def main():
         "roofline": roof,
         "kernels": breakdown,
     }
+    out["ms_per_step_graph_replay"] = graph_replay_ms(dec, z, args.steps, args.warmup)
     # secondary: the other decode size the metric names (after the timed region)
     if not args.no_secondary:
         out["secondary"] = secondary(dec, args, 32 if h != 32 else 128)

@@ -16,7 +16,7 @@ VAE_ERR_INVALID_ARG = -1
 VAE_ERR_UNSUPPORTED = -2
 VAE_ERR_WORKSPACE = -3
 VAE_ERR_HIP = -4
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class VaeConv(ctypes.Structure):
@@ -91,6 +91,7 @@ SIGNATURES = {
                                            POINTER(c_int32)]),
     "vae_decoder_destroy": (None, [c_void_p]),
     "vae_decoder_set_groupnorm_fusion": (c_int32, [c_void_p, c_int32]),
+    "vae_decoder_set_graph": (c_int32, [c_void_p, c_int32]),
     "vae_decoder_set_profiling": (c_int32, [c_void_p, c_int32]),
     "vae_decoder_profile": (c_int32, [c_void_p, POINTER(VaeProfRecord), c_int32, POINTER(c_int32)]),
 }

@@ -315,6 +315,10 @@ class Decoder:
         """Apply GroupNorm + SiLU while each conv loads its input (off by default)."""
         check(self._lib.vae_decoder_set_groupnorm_fusion(self._h, int(bool(on))))
 
+    def set_graph(self, on: bool) -> None:
+        """Replay decodes with the same buffers and sizes from a captured HIP graph."""
+        check(self._lib.vae_decoder_set_graph(self._h, int(bool(on))))
+
     def set_profiling(self, on: bool) -> None:
         check(self._lib.vae_decoder_set_profiling(self._h, int(bool(on))))
 

@@ -231,6 +231,18 @@ struct vae_decoder {
     int kt = 1;              // 3: the causal 3-D decoder
     bool direct_out = false; // conv_out kept raw for the direct kernel
     bool gn_fused = false;   // GroupNorm + SiLU applied while the consuming conv loads its input
+    // HIP-graph replay of the decode's launch sequence (vae_decoder_set_graph)
+    struct Graph {
+        bool on = false;
+        hipGraphExec_t exec = nullptr;
+        const float *latent = nullptr;
+        float *rgb = nullptr;
+        void *ws = nullptr;
+        size_t ws_bytes = 0;
+        int T = 0, h = 0, w = 0;
+        hipStream_t stream = nullptr;
+        bool gn_fused = false;
+    } graph;
     // profiling
     bool profiling = false;
     std::vector<ProfEntry> prof;
@@ -558,13 +570,8 @@ int32_t workspace_bytes_t(const vae_decoder *d, int T, int h, int w, size_t *byt
     return VAE_OK;
 }
 
-int32_t decode_t(vae_decoder *d, const float *latent, int T, int h, int w, float *rgb, void *ws, size_t ws_bytes,
-                 void *stream, const char *who) {
-    if (!d || !latent || !rgb) return fail(VAE_ERR_INVALID_ARG, "%s: NULL pointer", who);
-    size_t need = 0;
-    int32_t rc = workspace_bytes_t(d, T, h, w, &need, who);
-    if (rc) return rc;
-    if (!ws || ws_bytes < need) return fail(VAE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", who, ws_bytes, need);
+// Enqueues every launch of one decode on `stream` (arguments validated).
+int32_t run_chain(vae_decoder *d, const float *latent, int T, int h, int w, float *rgb, void *ws, void *stream) {
     const Plan pl = plan_for(d, T, h, w);
     char *base = static_cast<char *>(ws);
     const size_t a = align256(pl.act * 4);
@@ -648,6 +655,56 @@ int32_t decode_t(vae_decoder *d, const float *latent, int T, int h, int w, float
     return r.rc;
 }
 
+int32_t decode_t(vae_decoder *d, const float *latent, int T, int h, int w, float *rgb, void *ws, size_t ws_bytes,
+                 void *stream, const char *who) {
+    if (!d || !latent || !rgb) return fail(VAE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+    size_t need = 0;
+    int32_t rc = workspace_bytes_t(d, T, h, w, &need, who);
+    if (rc) return rc;
+    if (!ws || ws_bytes < need) return fail(VAE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", who, ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    vae_decoder::Graph &g = d->graph;
+    bool graph = g.on && !d->profiling && s != nullptr;
+    if (graph) {
+        // a caller that is capturing this stream itself gets the plain launches
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if ((rc = hip_status(hipStreamIsCapturing(s, &cs), "hipStreamIsCapturing"))) return rc;
+        graph = cs == hipStreamCaptureStatusNone;
+    }
+    if (!graph) return run_chain(d, latent, T, h, w, rgb, ws, stream);
+    const bool hit = g.exec && g.latent == latent && g.rgb == rgb && g.ws == ws && g.ws_bytes == ws_bytes &&
+                     g.T == T && g.h == h && g.w == w && g.stream == s && g.gn_fused == d->gn_fused;
+    if (!hit) {
+        if (g.exec) {
+            (void)hipGraphExecDestroy(g.exec);
+            g.exec = nullptr;
+        }
+        if ((rc = hip_status(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture")))
+            return rc;
+        const int32_t chain_rc = run_chain(d, latent, T, h, w, rgb, ws, stream);
+        hipGraph_t graph_def = nullptr;
+        rc = hip_status(hipStreamEndCapture(s, &graph_def), "hipStreamEndCapture");
+        if (chain_rc == VAE_OK && rc == VAE_OK)
+            rc = hip_status(hipGraphInstantiate(&g.exec, graph_def, nullptr, nullptr, 0), "hipGraphInstantiate");
+        if (graph_def) (void)hipGraphDestroy(graph_def);
+        if (chain_rc != VAE_OK) return chain_rc;
+        if (rc != VAE_OK) {
+            g.exec = nullptr;
+            return rc;
+        }
+        g.latent = latent;
+        g.rgb = rgb;
+        g.ws = ws;
+        g.ws_bytes = ws_bytes;
+        g.T = T;
+        g.h = h;
+        g.w = w;
+        g.stream = s;
+        g.gn_fused = d->gn_fused;
+    }
+    return hip_status(hipGraphLaunch(g.exec, s), "hipGraphLaunch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -704,8 +761,20 @@ int32_t vae_decode3d(vae_decoder *d, const float *latent, int32_t t, int32_t h, 
     return decode_t(d, latent, t, h, w, rgb, ws, ws_bytes, stream, "vae_decode3d");
 }
 
+int32_t vae_decoder_set_graph(vae_decoder *d, int32_t on) {
+    if (!d) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_set_graph: NULL decoder");
+    d->graph.on = on != 0;
+    if (!d->graph.on && d->graph.exec) {
+        int32_t rc = hip_status(hipGraphExecDestroy(d->graph.exec), "hipGraphExecDestroy");
+        d->graph.exec = nullptr;
+        if (rc) return rc;
+    }
+    return VAE_OK;
+}
+
 void vae_decoder_destroy(vae_decoder *d) {
     if (!d) return;
+    if (d->graph.exec) (void)hipGraphExecDestroy(d->graph.exec);
     for (ProfEntry &e : d->prof) {
         if (e.start) (void)hipEventDestroy(e.start);
         if (e.stop) (void)hipEventDestroy(e.stop);

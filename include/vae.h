@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 4
+#define VAE_ABI_VERSION 5
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -260,6 +260,17 @@ void vae_decoder_destroy(vae_decoder *d);
  * faster, so the default is off.  VAE_ERR_UNSUPPORTED if a normalised conv
  * has more than 512 input channels. */
 int32_t vae_decoder_set_groupnorm_fusion(vae_decoder *d, int32_t on);
+
+/* on != 0: vae_decode / vae_decode3d capture their launch sequence into a HIP
+ * graph on the first call with a given (latent, rgb, workspace, sizes,
+ * stream, GroupNorm mode) and replay the graph on later calls with the same
+ * arguments; other arguments capture a new graph (one is cached).  The
+ * graph reads the buffers when it runs, so new contents in the same buffers
+ * are decoded; the caller keeps them allocated while the graph is cached (or
+ * turns graphs off, which frees it).  Plain launches are used while
+ * profiling, on the null stream, and while the caller captures the stream
+ * itself.  Off by default. */
+int32_t vae_decoder_set_graph(vae_decoder *d, int32_t on);
 
 /* ------------------------------------------------------------- profiling */
 

@@ -419,3 +419,39 @@ def test_decode_causal3d_rejects_2d_calls(api, decoder3d, decoder):
     assert lib.vae_decoder_workspace_bytes(decoder3d._h, 4, 4, ctypes.byref(nb)) != 0
     assert lib.vae_decoder3d_workspace_bytes(decoder._h, 1, 4, 4, ctypes.byref(nb)) != 0
     assert "3-D" in lib.vae_last_error().decode()
+
+
+def test_decode_graph_replay_matches_eager(decoder):
+    # two latents through one input buffer: every replay is bit-identical to the
+    # eager decode of the buffer's current contents, with eager work in between
+    z1, z2 = dev(vaegen.latent(7, 16, 16)), dev(vaegen.latent(8, 16, 16))
+    e1, e2 = decoder.decode(z1).cpu(), decoder.decode(z2).cpu()
+    zin = torch.empty_like(z1)
+    out = torch.empty((3, 128, 128), dtype=torch.float32, device="cuda")
+    decoder.set_graph(True)
+    try:
+        for _ in range(3):
+            zin.copy_(z1)
+            decoder.decode(zin, out=out)
+            assert torch.equal(out.cpu(), e1)
+            torch.cuda.synchronize()
+            _ = (torch.randn(4096, device="cuda") * 2).sum().item()
+            zin.copy_(z2)
+            decoder.decode(zin, out=out)
+            assert torch.equal(out.cpu(), e2)
+    finally:
+        decoder.set_graph(False)
+
+
+def test_decode3d_graph_replay_matches_eager(decoder3d):
+    z = dev(vaegen.latent3d(9, 2, 4, 4))
+    e = decoder3d.decode(z).cpu()
+    out = torch.empty((3, 2, 32, 32), dtype=torch.float32, device="cuda")
+    decoder3d.set_graph(True)
+    try:
+        for _ in range(3):
+            decoder3d.decode(z, out=out)
+            assert torch.equal(out.cpu(), e)
+            torch.cuda.synchronize()
+    finally:
+        decoder3d.set_graph(False)
