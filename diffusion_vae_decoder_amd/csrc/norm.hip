@@ -23,6 +23,7 @@ constexpr int kGroups = 32;
 constexpr int kMaxParts = 64;
 constexpr long long kPartElems = 16384;   // group elements per stats workgroup, at least
 constexpr int kApplyElems = 4096;         // elements per apply workgroup (16 per thread)
+constexpr int kInlineRecords = 512;       // producer records per group an apply workgroup merges itself
 
 int parts_for(long long gsize) {
     long long p = (gsize + kPartElems - 1) / kPartElems;
@@ -90,30 +91,48 @@ __global__ __launch_bounds__(kThreads) void gn_stats(const float *__restrict__ x
     }
 }
 
+// With `rec` set (a short list of producer records per group) each workgroup
+// merges its group's records itself, as gn_merge does, instead of reading
+// merged partials.
 template <bool VEC, bool SILU, bool RES>
 __global__ __launch_bounds__(kThreads) void gn_apply(const float *x, long long spatial, int cpg,
                                                      int parts, const double *__restrict__ part,
                                                      const double *__restrict__ shifts,
                                                      const float *__restrict__ gamma,
                                                      const float *__restrict__ beta,
-                                                     const float *res, float *y) {
+                                                     const float *res, float *y,
+                                                     const floatx4 *__restrict__ rec, int nrec) {
     __shared__ double scratch[8];
     __shared__ float stat[2];
     const int c = blockIdx.y;
     const int g = c / cpg;
     double s1 = 0.0, s2 = 0.0;
-    if (threadIdx.x < parts) {
+    if (rec) {
+        for (int i = threadIdx.x; i < nrec; i += kThreads) {
+            const floatx4 v = rec[(long long)g * nrec + i];
+            const double n = v[0], m = v[1];
+            s1 += n * m;
+            s2 += (double)v[2] + n * m * m;
+        }
+    } else if (threadIdx.x < parts) {
         s1 = part[2 * ((long long)g * parts + threadIdx.x)];
         s2 = part[2 * ((long long)g * parts + threadIdx.x) + 1];
     }
     block_sum2(s1, s2, scratch);
     if (threadIdx.x == 0) {
         const double n = (double)spatial * cpg;
-        const double md = s1 / n;
-        double var = s2 / n - md * md;
+        double mean, var;
+        if (rec) {   // s1 = sum n m, s2 = sum (M2 + n m^2) over the records
+            mean = s1 / n;
+            var = (s2 - s1 * mean) / n;
+        } else {     // shifted sums d = x - shift
+            const double md = s1 / n;
+            var = s2 / n - md * md;
+            mean = shifts[g] + md;
+        }
         if (var < 0.0) var = 0.0;
         const double rstd = 1.0 / sqrt(var + 1e-6);
-        stat[0] = (float)(shifts[g] + md);
+        stat[0] = (float)mean;
         stat[1] = (float)(rstd * (double)gamma[c]);
     }
     __syncthreads();
@@ -239,13 +258,13 @@ __global__ __launch_bounds__(kThreads) void gn_merge(const floatx4 *__restrict__
 template <bool VEC, bool SILU>
 void apply2(bool res, dim3 grid, hipStream_t s, const float *x, long long spatial, int cpg,
             int parts, const double *part, const double *shifts, const float *gamma,
-            const float *beta, const float *r, float *y) {
+            const float *beta, const float *r, float *y, const floatx4 *rec, int nrec) {
     if (res)
         hipLaunchKernelGGL((gn_apply<VEC, SILU, true>), grid, dim3(kThreads), 0, s, x, spatial, cpg,
-                           parts, part, shifts, gamma, beta, r, y);
+                           parts, part, shifts, gamma, beta, r, y, rec, nrec);
     else
         hipLaunchKernelGGL((gn_apply<VEC, SILU, false>), grid, dim3(kThreads), 0, s, x, spatial, cpg,
-                           parts, part, shifts, gamma, beta, r, y);
+                           parts, part, shifts, gamma, beta, r, y, rec, nrec);
 }
 
 // ------------------------------------------------------------- upsample x2
@@ -312,18 +331,23 @@ int32_t launch_groupnorm(const float *x, int c, long long spatial, const float *
                          hipStream_t s, const floatx4 *rec, int nrec) {
     const int cpg = c / kGroups;
     int parts = 0;
-    int32_t rc = groupnorm_stats(x, c, spatial, ws, s, rec, nrec, &parts);
-    if (rc != VAE_OK) return rc;
+    // a few records per group: every apply workgroup merges its group's own
+    const bool inline_rec = rec && nrec <= kInlineRecords;
+    if (!inline_rec) {
+        int32_t rc = groupnorm_stats(x, c, spatial, ws, s, rec, nrec, &parts);
+        if (rc != VAE_OK) return rc;
+    }
+    const floatx4 *arec = inline_rec ? rec : nullptr;
     const double *part = reinterpret_cast<const double *>(ws);
     const double *shifts = part + 2 * kGroups * parts;
     const bool vec = spatial % 4 == 0 && aligned16(x) && aligned16(y) && (!res || aligned16(res));
     const dim3 grid((unsigned)((spatial + kApplyElems - 1) / kApplyElems), (unsigned)c);
     if (vec) {
-        if (silu) apply2<true, true>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y);
-        else apply2<true, false>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y);
+        if (silu) apply2<true, true>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y, arec, nrec);
+        else apply2<true, false>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y, arec, nrec);
     } else {
-        if (silu) apply2<false, true>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y);
-        else apply2<false, false>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y);
+        if (silu) apply2<false, true>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y, arec, nrec);
+        else apply2<false, false>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y, arec, nrec);
     }
     return check_launch("gn_apply");
 }

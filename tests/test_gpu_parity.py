@@ -194,6 +194,7 @@ CONV_GN_CASES = [
     (64, 128, 24, 20, False, False, True),    # K-split: records from the reduction (vector path)
     (64, 128, 23, 19, False, True, True),     # K-split, odd plane (scalar path), residual
     (16, 64, 21, 30, False, False, True),     # 2 channels per group: separate statistics pass
+    (16, 128, 200, 330, False, False, True),  # 550 tiles: more records than the apply pass merges itself
 ]
 
 
