@@ -19,13 +19,18 @@
 // a chunk is ordered (channel, tap) and lane half h takes the channels
 // [2h, 2h + 2), so both LDS operand reads are one row of 32 consecutive
 // floats per half-wave, and the strides are padded so the two halves fall in
-// different LDS banks.  The halo and weight tiles are double-buffered (47 KB),
+// different LDS banks.  The halo and weight tiles are double-buffered (48 KB),
 // so three workgroups (three waves per SIMD) share a CU and hide each other's
 // staging.  The halo is gathered with raw buffer loads: padding and channels
 // past cin read as 0 from out-of-range offsets, with no branch.
 //
 // Shapes that yield fewer workgroups than the GPU holds are split along K;
 // each split writes partial sums that splitk_reduce adds in a fixed order.
+//
+// When the output is normalised next (a GroupNorm of the following layer),
+// the epilogue (or splitk_reduce) also writes per-group records (count,
+// mean, sum of squared deviations) of the tile, which the normalisation
+// merges instead of making a statistics pass over the output.
 //
 // MODE_GNSILU (optional, off in the decoder by default) applies GroupNorm +
 // SiLU of the input while staging it, from per-channel coefficients held in
@@ -44,8 +49,8 @@ namespace vae {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCK = kConvCC * 9;         // K per chunk (72)
-constexpr int kSteps = kCK / 2;          // MFMA k-steps per chunk (36)
+constexpr int kCK = kConvCC * 9;         // K per chunk (36)
+constexpr int kSteps = kCK / 2;          // MFMA k-steps per chunk (18)
 constexpr int kHalfC = kConvCC / 2;      // channels per lane half
 
 // Smallest stride >= base, a multiple of `align`, with (mult * stride) % 64 == 32:
@@ -56,7 +61,7 @@ constexpr int bank_split_stride(int base, int mult, int align) {
     return -1;
 }
 
-constexpr int kLdaW = bank_split_stride(kConvBM, kHalfC * 9, 4);   // weight row stride (136)
+constexpr int kLdaW = bank_split_stride(kConvBM, kHalfC * 9, 4);   // weight row stride (144)
 static_assert(kLdaW > 0, "no bank-split stride for the weight tile");
 
 template <int TC>

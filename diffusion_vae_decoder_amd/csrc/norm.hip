@@ -3,14 +3,19 @@
 // the statistics: group mean and biased variance) and nearest x2 upsample
 // (VaeUpRef).
 //
-// GroupNorm runs as two HBM-streaming kernels.  gn_stats: a grid of
-// (parts, 32 groups) workgroups each reduces one contiguous slice of a group
-// to (sum d, sum d^2) with d = x - x_first (the group's first value, a shift
-// that keeps the variance free of cancellation); float32 per float4, float64
-// across float4s and threads.  gn_apply: a grid of (spatial chunks,
-// channels); each workgroup merges its group's partials in a fixed order
-// (deterministic), then streams y = silu((x - mean) * rstd * gamma + beta)
-// [+ residual] with float4 loads and stores.
+// GroupNorm needs the group statistics before it can write anything.  In the
+// decoder they come from the producing conv, which writes per-group records
+// (count, mean, sum of squared deviations) of every tile it stores; gn_merge
+// sums the records in float64 in a fixed order (or, for a short list, each
+// gn_apply workgroup does).  Without records (standalone calls, the input of
+// the attention) gn_stats makes the statistics pass: a grid of (parts, 32
+// groups) workgroups each reduces one contiguous slice of a group to (sum d,
+// sum d^2) with d = x - x_first (the group's first value, a shift that keeps
+// the variance free of cancellation); float32 per float4, float64 across
+// float4s and threads.  gn_apply: a grid of (spatial chunks, channels); each
+// workgroup merges its group's statistics in a fixed order (deterministic),
+// then streams y = silu((x - mean) * rstd * gamma + beta) [+ residual] with
+// float4 loads and stores.
 
 #include "vae_internal.h"
 
