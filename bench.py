@@ -55,6 +55,7 @@ def parse():
                     help="skip the second decode size (keeps profiler summaries to one workload)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the single-layer sweep")
     ap.add_argument("--no-3d", action="store_true", help="skip the causal 3-D stack and decode")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timings")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the decodes, run one plain device copy of this many MiB "
@@ -276,7 +277,8 @@ def secondary(dec, args, h2: int) -> dict:
     c2 = [r for r in recs2 if r["kernel"].startswith("conv3x3_mfma")]
     c2_tf = sum(r["flops"] for r in c2) / (sum(r["ms"] for r in c2) / 1e3) / 1e12
     return {"workload": f"decode latent [16,{h2},{h2}] -> RGB [3,{8 * h2},{8 * h2}]",
-            "ms_per_step": ms2, "ms_per_step_graph_replay": graph_replay_ms(dec, z2, args.steps, args.warmup),
+            "ms_per_step": ms2,
+            "ms_per_step_graph_replay": None if args.no_graph else graph_replay_ms(dec, z2, args.steps, args.warmup),
             "tflops": sum(r["flops"] for r in recs2) / args.steps / (ms2 / 1e3) / 1e12,
             "conv3x3_tflops": c2_tf, "conv3x3_frac_fp32_mfma_peak": c2_tf / PEAK_FP32_MFMA_TFLOPS}
 
@@ -366,7 +368,8 @@ def main():
         "roofline": roof,
         "kernels": breakdown,
     }
-    out["ms_per_step_graph_replay"] = graph_replay_ms(dec, z, args.steps, args.warmup)
+    if not args.no_graph:
+        out["ms_per_step_graph_replay"] = graph_replay_ms(dec, z, args.steps, args.warmup)
     # secondary: the other decode size the metric names (after the timed region)
     if not args.no_secondary:
         out["secondary"] = secondary(dec, args, 32 if h != 32 else 128)
