@@ -63,19 +63,40 @@ def parse():
     return ap.parse_args()
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "conv3x3_mfma_decode1024_hbm_counters.md")
-CONV_SRC = os.path.join(ROOT, "diffusion_vae_decoder_amd", "csrc", "conv.hip")
+CSRC = os.path.join(ROOT, "diffusion_vae_decoder_amd", "csrc")
+
+
+def conv_family(kernel: str) -> str:
+    """'conv3x3_wino' or 'conv3x3_mfma' for the two 3x3 conv kernels, else ''."""
+    for f in ("conv3x3_wino", "conv3x3_mfma"):
+        if kernel.startswith(f):
+            return f
+    return ""
+
+
+def is_conv3x3(kernel: str) -> bool:
+    return conv_family(kernel) != ""
+
+
+def mfma_fraction(kernel: str) -> float:
+    """MFMA multiplies the kernel executes per direct-conv multiply: the
+    Winograd F(2x2,3x3) form does 16 of 36 (9 of 36 on an upsampled input)."""
+    if conv_family(kernel) == "conv3x3_wino":
+        return 9.0 / 36.0 if "up2x" in kernel else 16.0 / 36.0
+    return 1.0
 
 
 def counter_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary, or None when that summary was taken on another kernel,
-    another workload, or a conv source that has changed since."""
-    if workload != "decode1024":
+    another workload, or a kernel source that has changed since."""
+    fam = conv_family(kernel)
+    if workload != "decode1024" or not fam:
         return None
+    src_file = "conv_wino.hip" if fam == "conv3x3_wino" else "conv.hip"
     try:
-        text = open(COUNTERS).read()
-        src = open(CONV_SRC, "rb").read()
+        text = open(os.path.join(ROOT, "profiles", f"{fam}_decode1024_hbm_counters.md")).read()
+        src = open(os.path.join(CSRC, src_file), "rb").read()
     except OSError:
         return None
     vals = {}
@@ -234,7 +255,7 @@ def decode3d(args, t: int = 17, h: int = 32) -> dict:
     recs = dec.profile()
     dec.set_profiling(False)
     dec.close()
-    conv = [r for r in recs if r["kernel"].startswith("conv3x3_mfma")]
+    conv = [r for r in recs if is_conv3x3(r["kernel"])]
     conv_tf = sum(r["flops"] for r in conv) / (sum(r["ms"] for r in conv) / 1e3) / 1e12
     return {"workload": f"causal 3-D decode, latent [16,{t},{h},{h}] -> RGB [3,{t},{8 * h},{8 * h}]",
             "ms_per_step": ms, "tflops": sum(r["flops"] for r in recs) / args.steps / (ms / 1e3) / 1e12,
@@ -274,7 +295,7 @@ def secondary(dec, args, h2: int) -> dict:
     ms2 = (time.perf_counter() - t0) * 1e3 / args.steps
     recs2 = dec.profile()
     dec.set_profiling(False)
-    c2 = [r for r in recs2 if r["kernel"].startswith("conv3x3_mfma")]
+    c2 = [r for r in recs2 if is_conv3x3(r["kernel"])]
     c2_tf = sum(r["flops"] for r in c2) / (sum(r["ms"] for r in c2) / 1e3) / 1e12
     return {"workload": f"decode latent [16,{h2},{h2}] -> RGB [3,{8 * h2},{8 * h2}]",
             "ms_per_step": ms2,
@@ -326,7 +347,7 @@ def main():
         k["bytes"] += r["bytes"]
         k["n"] += 1
     dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
-    conv_recs = [r for r in recs if r["kernel"].startswith("conv3x3_mfma")]
+    conv_recs = [r for r in recs if is_conv3x3(r["kernel"])]
     conv_ms = sum(r["ms"] for r in conv_recs)
     conv_fl = sum(r["flops"] for r in conv_recs)
     if dom["flops"] > 0:
@@ -336,6 +357,12 @@ def main():
                 "kernel": dom_name, "launches_per_step": dom["n"] // args.steps,
                 "avg_launch_ms": dom["ms"] / dom["n"], "flops_per_launch": dom["flops"] / dom["n"],
                 "algorithmic_bytes_per_launch": dom["bytes"] / dom["n"]}
+        f = mfma_fraction(dom_name)
+        if f != 1.0:
+            # achieved counts direct-conv FLOPs; the MFMA pipes execute the fraction f of them
+            roof["mfma_flops_per_launch"] = f * dom["flops"] / dom["n"]
+            roof["mfma_executed_tflops"] = f * achieved
+            roof["mfma_executed_frac"] = f * achieved / PEAK_FP32_MFMA_TFLOPS
     else:
         achieved = dom["bytes"] / (dom["ms"] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -77,21 +77,21 @@ int32_t check_plane(const char *who, long long c, long long h, long long w) {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Workspace of a 3x3 conv producing [cout, T, H, W]: the repacked weights, then
-// the split-K partial sums (if the shape is split).
+// Workspace of a 3x3 conv producing [cout, T, H, W]: the repacked weights (room
+// for any layout), then the split-K partial sums (if the shape is split).
 size_t conv_ws(const vae_conv *c, int kt, int T, int H, int W) {
     if (c->kernel == 1) return gemm_partial_floats(c->out_channels, H * W, c->in_channels, false) * sizeof(float);
     if (kt == 1 && c->out_channels <= 4)   // direct kernel (or, with upsample / residual, the implicit GEMM)
         return std::max(conv3x3_direct_partial_floats(c->out_channels, c->in_channels, 1, H, W, 1) * sizeof(float),
-                        align256(conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float)) +
+                        align256(conv3x3_pack_floats_max(c->out_channels, c->in_channels, kt) * sizeof(float)) +
                             conv3x3_partial_floats(c->out_channels, c->in_channels, kt, H, W, T) * sizeof(float));
-    return align256(conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float)) +
+    return align256(conv3x3_pack_floats_max(c->out_channels, c->in_channels, kt) * sizeof(float)) +
            conv3x3_partial_floats(c->out_channels, c->in_channels, kt, H, W, T) * sizeof(float);
 }
 
 float *conv_ws_part(const vae_conv *c, int kt, void *ws) {
     return reinterpret_cast<float *>(static_cast<char *>(ws) +
-                                     align256(conv3x3_packed_floats(c->out_channels, c->in_channels, kt) * sizeof(float)));
+                                     align256(conv3x3_pack_floats_max(c->out_channels, c->in_channels, kt) * sizeof(float)));
 }
 
 }  // namespace
@@ -149,8 +149,10 @@ int32_t vae_conv2d(const float *x, int32_t cin, int32_t h, int32_t w, const vae_
     }
     if (!ws || ws_bytes < need)
         return set_error("vae_conv2d: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
-    if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 1, static_cast<float *>(ws), s))) return rc;
     ConvLaunch a{};
+    a.wino = conv3x3_layout(0, upsample2x);
+    if ((rc = pack_conv3x3_layout(a.wino, conv->weight, conv->out_channels, cin, 1, static_cast<float *>(ws), s)))
+        return rc;
     a.x = x; a.wpk = static_cast<const float *>(ws); a.bias = conv->bias; a.res = residual; a.y = y;
     a.part = conv_ws_part(conv, 1, ws);
     a.cin = cin; a.cout = conv->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
@@ -257,8 +259,10 @@ int32_t vae_conv2d_groupnorm_silu(const float *x, int32_t cin, int32_t h, int32_
         return set_error("vae_conv2d_groupnorm_silu: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *base = static_cast<char *>(ws);
-    if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 1, reinterpret_cast<float *>(base), s))) return rc;
     ConvLaunch a{};
+    a.wino = conv3x3_layout(0, upsample2x);
+    if ((rc = pack_conv3x3_layout(a.wino, conv->weight, conv->out_channels, cin, 1, reinterpret_cast<float *>(base), s)))
+        return rc;
     a.x = x; a.wpk = reinterpret_cast<const float *>(base); a.bias = conv->bias; a.res = residual; a.y = y;
     a.part = conv_ws_part(conv, 1, ws);
     a.cin = cin; a.cout = conv->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
@@ -351,8 +355,10 @@ int32_t vae_conv3d_causal(const float *x, int32_t cin, int32_t t, int32_t h, int
     if (!ws || ws_bytes < need)
         return set_error("vae_conv3d_causal: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((rc = pack_conv3x3(conv->weight, conv->out_channels, cin, 3, static_cast<float *>(ws), s))) return rc;
     ConvLaunch a{};
+    a.wino = conv3x3_layout(0, 0);
+    if ((rc = pack_conv3x3_layout(a.wino, conv->weight, conv->out_channels, cin, 3, static_cast<float *>(ws), s)))
+        return rc;
     a.x = x; a.wpk = static_cast<const float *>(ws); a.bias = conv->bias; a.y = y;
     a.part = conv_ws_part(conv, 3, ws);
     a.cin = cin; a.cout = conv->out_channels; a.H = h; a.W = w; a.T = t; a.kt = 3;

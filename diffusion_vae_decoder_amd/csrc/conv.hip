@@ -588,6 +588,25 @@ int32_t pack_conv3x3(const float *w, int cout, int cin, int kt, float *dst, hipS
     return check_launch("pack_conv3x3");
 }
 
+int conv3x3_layout(int denorm, int upsample) { return denorm ? 0 : (upsample ? 2 : 1); }
+
+size_t conv3x3_pack_floats(int layout, int cout, int cin, int kt) {
+    return layout == 0 ? conv3x3_packed_floats(cout, cin, kt) : conv3x3_wino_packed_floats(cout, cin, kt, layout == 2);
+}
+
+size_t conv3x3_pack_floats_max(int cout, int cin, int kt) {
+    size_t n = conv3x3_packed_floats(cout, cin, kt);
+    for (int up = 0; up < 2; ++up) {
+        const size_t m = conv3x3_wino_packed_floats(cout, cin, kt, up);
+        if (m > n) n = m;
+    }
+    return n;
+}
+
+int32_t pack_conv3x3_layout(int layout, const float *w, int cout, int cin, int kt, float *dst, hipStream_t s) {
+    return layout == 0 ? pack_conv3x3(w, cout, cin, kt, dst, s) : pack_conv3x3_wino(w, cout, cin, kt, layout == 2, dst, s);
+}
+
 namespace {
 int conv_tc(int W) { return W > 16 ? 32 : (W > 8 ? 16 : 8); }
 constexpr int kSlots = 256 * 3;   // CUs x resident conv workgroups per CU
@@ -622,26 +641,30 @@ int conv3x3_gn_records(const ConvLaunch &a) {
 }
 
 const char *conv3x3_kernel_name(const ConvLaunch &a) {
+    static const char *algos[2] = {"mfma", "wino"};
     static const char *tcs[3] = {"32", "16", "8"};
     static const char *modes[4] = {"plain", "up2x", "denorm", "gnsilu"};
     static const char *tails[3] = {"", ",res", ",splitk"};
-    static char names[3][4][3][48];
+    static char names[2][3][4][3][48];
     static bool init = false;
     if (!init) {
-        for (int t = 0; t < 3; ++t)
-            for (int m = 0; m < 4; ++m)
-                for (int k = 0; k < 3; ++k)
-                    snprintf(names[t][m][k], sizeof names[t][m][k], "conv3x3_mfma<%s,%s%s>", tcs[t], modes[m], tails[k]);
+        for (int g = 0; g < 2; ++g)
+            for (int t = 0; t < 3; ++t)
+                for (int m = 0; m < 4; ++m)
+                    for (int k = 0; k < 3; ++k)
+                        snprintf(names[g][t][m][k], sizeof names[g][t][m][k], "conv3x3_%s<%s,%s%s>", algos[g], tcs[t],
+                                 modes[m], tails[k]);
         init = true;
     }
     const int tc = conv_tc(a.W);
     const int ti = tc == 32 ? 0 : (tc == 16 ? 1 : 2);
     const int mi = a.upsample ? 1 : (a.denorm ? 2 : (a.gn_coef ? 3 : 0));
     const int si = conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T) > 1 ? 2 : (a.res ? 1 : 0);
-    return names[ti][mi][si];
+    return names[a.wino ? 1 : 0][ti][mi][si];
 }
 
 int32_t launch_conv3x3_main(const ConvLaunch &a, hipStream_t s) {
+    if (a.wino) return launch_conv3x3_wino_main(a, s);
     Params p;
     p.x = a.x;
     p.wpk = a.wpk;

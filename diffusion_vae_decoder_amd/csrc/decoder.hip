@@ -33,9 +33,10 @@ namespace {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct DConv {
-    const float *w = nullptr;   // packed (3x3) or raw [cout, cin] (1x1)
+    const float *w = nullptr;   // packed (3x3, in ConvLaunch::wino layout `layout`) or raw [cout, cin] (1x1)
     const float *b = nullptr;
     int cout = 0, cin = 0, k = 0;
+    int layout = 0;
     bool present = false;
 };
 struct DNorm {
@@ -84,8 +85,9 @@ struct Packer {
         return d;
     }
     // raw3: keep a 3x3 weight in its own [cout, cin, 3, 3] layout (the
-    // direct conv_out kernel reads that); otherwise 3x3 weights are repacked.
-    DConv conv(const vae_conv &c, bool raw3 = false) {
+    // direct conv_out kernel reads that); otherwise 3x3 weights are repacked
+    // for the conv's input: de-normalised on load (conv_in), upsampled or plain.
+    DConv conv(const vae_conv &c, bool raw3 = false, bool denorm = false, bool upsample = false) {
         DConv d;
         d.present = true;
         d.cout = c.out_channels;
@@ -94,8 +96,10 @@ struct Packer {
         if (c.kernel == 3 && raw3) {
             d.w = copy(c.weight, (size_t)c.out_channels * c.in_channels * 9 * kt);
         } else if (c.kernel == 3) {
-            const float *p = take(conv3x3_packed_floats(c.out_channels, c.in_channels, kt));
-            if (dst && rc == VAE_OK) rc = pack_conv3x3(c.weight, c.out_channels, c.in_channels, kt, const_cast<float *>(p), s);
+            d.layout = conv3x3_layout(denorm, upsample);
+            const float *p = take(conv3x3_pack_floats(d.layout, c.out_channels, c.in_channels, kt));
+            if (dst && rc == VAE_OK)
+                rc = pack_conv3x3_layout(d.layout, c.weight, c.out_channels, c.in_channels, kt, const_cast<float *>(p), s);
             d.w = p;
         } else {
             d.w = copy(c.weight, (size_t)c.out_channels * c.in_channels);
@@ -395,6 +399,7 @@ struct Runner {
         a.dn_shift = d->shift;
         a.part = part;
         a.gn_coef = gn ? coef : nullptr;
+        a.wino = c.layout;
         const int nrec = stats && c.cout % 32 == 0 ? conv3x3_gn_records(a) : 0;
         a.gn_rec = nrec > 0 ? rec : nullptr;
         const double in_elems = (double)c.cin * T * H * W / (up ? 4.0 : 1.0);
@@ -503,13 +508,13 @@ int32_t pack_bytes_kt(const vae_weights *w, int kt, size_t *bytes, const char *w
     if (!bytes) return fail(VAE_ERR_INVALID_ARG, "%s: bytes is NULL", who);
     Packer p{nullptr, 0, nullptr};
     p.kt = kt;
-    p.conv(w->conv_in);
+    p.conv(w->conv_in, false, /*denorm=*/true);
     p.resnet(w->mid_res0, "");
     p.attn(w->mid_attn);
     p.resnet(w->mid_res1, "");
     for (int i = 0; i < w->n_up; ++i) {
         for (int j = 0; j < w->ups[i].n_resnets; ++j) p.resnet(w->ups[i].resnets[j], "");
-        if (w->ups[i].upsample.weight) p.conv(w->ups[i].upsample);
+        if (w->ups[i].upsample.weight) p.conv(w->ups[i].upsample, false, false, /*upsample=*/true);
     }
     p.norm(w->norm_out);
     p.conv(w->conv_out, w->conv_out.out_channels <= 4);
@@ -532,7 +537,7 @@ int32_t create_kt(vae_decoder **out, const vae_weights *w, int kt, void *pack, s
     d->direct_out = w->conv_out.out_channels <= 4;
     Packer p{static_cast<char *>(pack), 0, static_cast<hipStream_t>(stream)};
     p.kt = kt;
-    d->conv_in = p.conv(w->conv_in);
+    d->conv_in = p.conv(w->conv_in, false, /*denorm=*/true);
     d->mid0 = p.resnet(w->mid_res0, "mid_block.resnets.0");
     d->attn = p.attn(w->mid_attn);
     d->mid1 = p.resnet(w->mid_res1, "mid_block.resnets.1");
@@ -540,7 +545,7 @@ int32_t create_kt(vae_decoder **out, const vae_weights *w, int kt, void *pack, s
         DUp u;
         for (int j = 0; j < w->ups[i].n_resnets; ++j)
             u.res.push_back(p.resnet(w->ups[i].resnets[j], "up_blocks." + std::to_string(i) + ".resnets." + std::to_string(j)));
-        if (w->ups[i].upsample.weight) u.up = p.conv(w->ups[i].upsample);
+        if (w->ups[i].upsample.weight) u.up = p.conv(w->ups[i].upsample, false, false, /*upsample=*/true);
         d->ups.push_back(u);
     }
     d->norm_out = p.norm(w->norm_out);

@@ -29,7 +29,7 @@ constexpr int kConvCC = 4;   // input channels per K chunk (K chunk = 4 x 9 taps
 
 struct ConvLaunch {
     const float *x;        // input activations
-    const float *wpk;      // weights repacked by pack_conv3x3
+    const float *wpk;      // packed weights, in the layout `wino` names
     const float *bias;     // [cout]
     const float *res;      // residual [cout, (T,) H, W] or nullptr
     float *y;              // output  [cout, (T,) H, W]
@@ -46,6 +46,8 @@ struct ConvLaunch {
     floatx4 *gn_rec;       // if set: GroupNorm(32) records of y for the normalisation that follows,
                            // [32][conv3x3_gn_records()] of (count, mean, M2, 0); M2 is the sum of
                            // squared deviations from the record's own mean
+    int wino;              // wpk layout: 0 pack_conv3x3 (implicit GEMM), 1 pack_conv3x3_wino,
+                           // 2 pack_conv3x3_wino for an upsampled input (Winograd conv)
 };
 
 // Bytes of the packed weights for a conv with `cout` x `cin` x (kt x 3 x 3).
@@ -67,6 +69,22 @@ size_t conv3x3_partial_floats(int cout, int cin, int kt, int H, int W, int T);
 int conv3x3_gn_records(const ConvLaunch &a);
 // Name of the kernel instantiation launch_conv3x3 picks for `a`.
 const char *conv3x3_kernel_name(const ConvLaunch &a);
+
+// Winograd F(2x2, 3x3) form of the same conv (conv_wino.hip): weights packed
+// by pack_conv3x3_wino (`up`: for a nearest-x2 upsampled input, which only
+// this packing may then be used with).  Same split-K factor, partial-sum
+// workspace, reduction and GroupNorm records as the implicit GEMM; no
+// de-normalisation, and GroupNorm on load only of a plain input.
+size_t conv3x3_wino_packed_floats(int cout, int cin, int kt, int up);
+int32_t pack_conv3x3_wino(const float *w, int cout, int cin, int kt, int up, float *dst, hipStream_t s);
+int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s);
+// The ConvLaunch::wino layout a conv uses (the Winograd form unless its input
+// is de-normalised on load), its packed floats (`upsample`: input upsampled)
+// and the packing.  conv3x3_pack_floats_max bounds both layouts.
+int conv3x3_layout(int denorm, int upsample);
+size_t conv3x3_pack_floats(int layout, int cout, int cin, int kt);
+size_t conv3x3_pack_floats_max(int cout, int cin, int kt);
+int32_t pack_conv3x3_layout(int layout, const float *w, int cout, int cin, int kt, float *dst, hipStream_t s);
 
 // y[o, :] = bias[o] + sum_s part[s * part_stride + o * plane + :] over `splits`
 // partial-sum slices, in slice order, for `rows` rows of `plane` elements.

@@ -47,17 +47,28 @@ def err(lib):
     return lib.vae_last_error().decode()
 
 
+def packed_bytes(cout, cin, kt=1):
+    """Room the per-layer 3x3 entry points reserve for packed weights: the
+    larger of the implicit GEMM's layout (128-channel output blocks x chunks of
+    4 input channels x 36 x 128 floats) and the Winograd form's (32-channel
+    output blocks x input-channel pairs x 64 lanes x 16 transform points)."""
+    ob = (cout + 127) // 128
+    direct = ob * kt * ((cin + 3) // 4) * 36 * 128 * 4
+    wino = ob * 4 * kt * ((cin + 1) // 2) * 64 * 16 * 4
+    return max(direct, wino)
+
+
 def test_conv2d_validation(lib):
     c = conv(64, 32, 3)
     ws = c_size_t()
     assert lib.vae_conv2d_workspace_bytes(byref(c), 8, 8, 0, byref(ws)) == VAE_OK
-    assert ws.value == 1 * 8 * 36 * 128 * 4           # 1 output block x 8 chunks of 4 channels x 36 x 128 floats
+    assert ws.value == packed_bytes(64, 32) == 4 * 16 * 64 * 16 * 4
     # a small shape: the 32x32 conv with 512 channels is K-split, so partial sums are added
     big = conv(512, 512, 3)
     w1, w2 = c_size_t(), c_size_t()
     assert lib.vae_conv2d_workspace_bytes(byref(big), 32, 32, 0, byref(w1)) == VAE_OK
     assert lib.vae_conv2d_workspace_bytes(byref(big), 256, 256, 0, byref(w2)) == VAE_OK
-    packed = 4 * 128 * 36 * 128 * 4
+    packed = packed_bytes(512, 512)
     assert w2.value == packed and w1.value == packed + 16 * 512 * 32 * 32 * 4
     assert lib.vae_conv2d_workspace_bytes(byref(big), 0, 32, 0, byref(w1)) == VAE_ERR_INVALID_ARG
     args = lambda **k: dict(dict(x=FAKE, cin=32, h=8, w=8, conv=byref(c), up=0, res=NULL, y=FAKE + 4096,
@@ -90,7 +101,7 @@ def test_conv_in_and_3d_validation(lib):
     assert lib.vae_conv_in(FAKE, 16, 8, 8, byref(conv(512, 16, 1)), 0.36, 0.1, FAKE + 64, FAKE, 0, NULL) == VAE_ERR_UNSUPPORTED
     c3 = conv(128, 128, 3)
     assert lib.vae_conv3d_causal_workspace_bytes(byref(c3), 3, 8, 8, byref(nb)) == VAE_OK
-    packed = 3 * 32 * 36 * 128 * 4
+    packed = packed_bytes(128, 128, 3)
     assert nb.value >= packed and (nb.value - packed) % (128 * 3 * 64 * 4) == 0
     full = c_size_t()
     assert lib.vae_conv3d_causal_workspace_bytes(byref(c3), 17, 256, 256, byref(full)) == VAE_OK
@@ -104,12 +115,12 @@ def test_conv_groupnorm_validation(lib):
     c = conv(128, 16, 3)
     nb = c_size_t()
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(c), 37, 45, 0, byref(nb)) == VAE_OK
-    # packed weights (4 chunks of 36 x 128), 20 tiles x 32 groups of 16-byte records, GroupNorm partials
-    assert nb.value == 4 * 36 * 128 * 4 + 20 * 32 * 16 + 32 * 16 + 32 * 8
+    # packed weights, 20 tiles x 32 groups of 16-byte records, GroupNorm partials
+    assert nb.value == packed_bytes(128, 16) + 20 * 32 * 16 + 32 * 16 + 32 * 8
     c64 = conv(64, 16, 3)                        # 2 channels per group: no records, a statistics pass
     n64 = c_size_t()
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(c64), 37, 45, 0, byref(n64)) == VAE_OK
-    assert n64.value == 256 * ((4 * 36 * 128 * 4 + 255) // 256) + 32 * 16 + 32 * 8
+    assert n64.value == 256 * ((packed_bytes(64, 16) + 255) // 256) + 32 * 16 + 32 * 8
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(conv(100, 16, 3)), 8, 8, 0, byref(nb)) == VAE_ERR_UNSUPPORTED
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(conv(128, 16, 1)), 8, 8, 0, byref(nb)) == VAE_ERR_UNSUPPORTED
     n = VaeNorm(FAKE, FAKE, 128)
@@ -189,8 +200,10 @@ def test_decoder_pack_and_validation(lib):
     w, keep = fake_weights()
     nb = c_size_t()
     assert lib.vae_decoder_pack_bytes(byref(w), byref(nb)) == VAE_OK, err(lib)
-    # about 50M parameters, 3x3 weights padded to 8-channel chunks
-    assert 49_000_000 * 4 < nb.value < 52_000_000 * 4
+    # about 50M parameters, of which 48.3M in 3x3 convs; their Winograd packing
+    # holds 16 floats per (output, input channel) pair instead of 9 (12 for the
+    # three upsample convs, 5.3M parameters): about 84.6M floats in all
+    assert 84_000_000 * 4 < nb.value < 85_500_000 * 4
     h = c_void_p()
     assert lib.vae_decoder_create(byref(h), byref(w), FAKE, nb.value - 1, NULL) == VAE_ERR_WORKSPACE
     assert lib.vae_decoder_create(byref(h), byref(w), FAKE + 4, nb.value, NULL) == VAE_ERR_INVALID_ARG
