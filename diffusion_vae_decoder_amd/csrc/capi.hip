@@ -79,14 +79,24 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Workspace of a 3x3 conv producing [cout, T, H, W]: the repacked weights (room
 // for any layout), then the split-K partial sums (if the shape is split).
+// Split-K partial sums of the conv in the weight layout it runs with; the
+// workspace sizes below take the larger of the two layouts, so one size
+// serves vae_conv2d and vae_conv_in alike.
+size_t conv_partial_floats(const vae_conv *c, int kt, int T, int H, int W, int layout) {
+    ConvLaunch a{};
+    a.cin = c->in_channels; a.cout = c->out_channels; a.H = H; a.W = W; a.T = T; a.kt = kt; a.wino = layout;
+    return conv3x3_partial_floats(a);
+}
+
 size_t conv_ws(const vae_conv *c, int kt, int T, int H, int W) {
     if (c->kernel == 1) return gemm_partial_floats(c->out_channels, H * W, c->in_channels, false) * sizeof(float);
-    if (kt == 1 && c->out_channels <= 4)   // direct kernel (or, with upsample / residual, the implicit GEMM)
+    const size_t part = std::max(conv_partial_floats(c, kt, T, H, W, 0), conv_partial_floats(c, kt, T, H, W, 1));
+    const size_t packed = align256(conv3x3_pack_floats_max(c->out_channels, c->in_channels, kt) * sizeof(float)) +
+                          part * sizeof(float);
+    if (kt == 1 && c->out_channels <= 4)   // direct kernel (or, with upsample / residual, the packed path)
         return std::max(conv3x3_direct_partial_floats(c->out_channels, c->in_channels, 1, H, W, 1) * sizeof(float),
-                        align256(conv3x3_pack_floats_max(c->out_channels, c->in_channels, kt) * sizeof(float)) +
-                            conv3x3_partial_floats(c->out_channels, c->in_channels, kt, H, W, T) * sizeof(float));
-    return align256(conv3x3_pack_floats_max(c->out_channels, c->in_channels, kt) * sizeof(float)) +
-           conv3x3_partial_floats(c->out_channels, c->in_channels, kt, H, W, T) * sizeof(float);
+                        packed);
+    return packed;
 }
 
 float *conv_ws_part(const vae_conv *c, int kt, void *ws) {
@@ -210,13 +220,14 @@ int32_t vae_groupnorm_silu(const float *x, int32_t c, int64_t spatial, const vae
 namespace {
 // Workspace of vae_conv2d_groupnorm_silu: the conv's workspace, then the
 // GroupNorm records of its output, then the GroupNorm partial sums.
-size_t conv_gn_records_bytes(const vae_conv *c, int cin, int H, int W) {
+size_t conv_gn_records_bytes(const vae_conv *c, int cin, int H, int W, int upsample) {
     ConvLaunch a{};
     a.cin = cin; a.cout = c->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
+    a.upsample = upsample; a.wino = conv3x3_layout(0, upsample);
     return (size_t)32 * conv3x3_gn_records(a) * sizeof(floatx4);
 }
-size_t conv_gn_ws(const vae_conv *c, int H, int W) {
-    return align256(conv_ws(c, 1, 1, H, W)) + align256(conv_gn_records_bytes(c, c->in_channels, H, W)) +
+size_t conv_gn_ws(const vae_conv *c, int H, int W, int upsample) {
+    return align256(conv_ws(c, 1, 1, H, W)) + align256(conv_gn_records_bytes(c, c->in_channels, H, W, upsample)) +
            groupnorm_ws_bytes(c->out_channels, (long long)H * W);
 }
 }  // namespace
@@ -231,7 +242,7 @@ int32_t vae_conv2d_groupnorm_workspace_bytes(const vae_conv *conv, int32_t h, in
     if (conv->out_channels % 32)
         return unsupported("vae_conv2d_groupnorm_workspace_bytes: out_channels %d not divisible by 32",
                            conv->out_channels);
-    *bytes = conv_gn_ws(conv, (int)H, (int)W);
+    *bytes = conv_gn_ws(conv, (int)H, (int)W, upsample2x ? 1 : 0);
     return VAE_OK;
 }
 
@@ -254,7 +265,7 @@ int32_t vae_conv2d_groupnorm_silu(const float *x, int32_t cin, int32_t h, int32_
     if (conv->out_channels % 32)
         return unsupported("vae_conv2d_groupnorm_silu: out_channels %d not divisible by 32", conv->out_channels);
     if (x == y) return bad("vae_conv2d_groupnorm_silu: y may not alias x");
-    const size_t need = conv_gn_ws(conv, H, W);
+    const size_t need = conv_gn_ws(conv, H, W, upsample2x ? 1 : 0);
     if (!ws || ws_bytes < need)
         return set_error("vae_conv2d_groupnorm_silu: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -268,7 +279,7 @@ int32_t vae_conv2d_groupnorm_silu(const float *x, int32_t cin, int32_t h, int32_
     a.cin = cin; a.cout = conv->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
     a.upsample = upsample2x ? 1 : 0;
     char *recs = base + align256(conv_ws(conv, 1, 1, H, W));
-    void *gws = recs + align256(conv_gn_records_bytes(conv, cin, H, W));
+    void *gws = recs + align256(conv_gn_records_bytes(conv, cin, H, W, upsample2x ? 1 : 0));
     const int nrec = conv3x3_gn_records(a);
     a.gn_rec = nrec > 0 ? reinterpret_cast<floatx4 *>(recs) : nullptr;
     if ((rc = launch_conv3x3(a, s))) return rc;

@@ -612,7 +612,8 @@ int conv_tc(int W) { return W > 16 ? 32 : (W > 8 ? 16 : 8); }
 constexpr int kSlots = 256 * 3;   // CUs x resident conv workgroups per CU
 }  // namespace
 
-int conv3x3_ksplit(int cout, int cin, int kt, int H, int W, int T) {
+namespace {
+int mfma_ksplit(int cout, int cin, int kt, int H, int W, int T) {
     const int TC = conv_tc(W), TR = kConvBN / TC;
     const long long base = (long long)((W + TC - 1) / TC) * ((H + TR - 1) / TR) *
                            ((cout + kConvBM - 1) / kConvBM) * T;
@@ -625,16 +626,23 @@ int conv3x3_ksplit(int cout, int cin, int kt, int H, int W, int T) {
     return s < 1 ? 1 : (int)s;
 }
 
-size_t conv3x3_partial_floats(int cout, int cin, int kt, int H, int W, int T) {
-    const int ks = conv3x3_ksplit(cout, cin, kt, H, W, T);
-    return ks > 1 ? (size_t)ks * cout * T * (size_t)H * W : 0;
+}  // namespace
+
+int conv3x3_ksplit(const ConvLaunch &a) {
+    return a.wino ? conv3x3_wino_ksplit(a) : mfma_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T);
+}
+
+size_t conv3x3_partial_floats(const ConvLaunch &a) {
+    const int ks = conv3x3_ksplit(a);
+    return ks > 1 ? (size_t)ks * a.cout * a.T * (size_t)a.H * a.W : 0;
 }
 
 int conv3x3_gn_records(const ConvLaunch &a) {
     if (a.cout % 32 != 0) return 0;
     const long long plane = (long long)a.T * a.H * a.W;
-    if (conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T) > 1)
+    if (conv3x3_ksplit(a) > 1)
         return (int)((a.cout / 32) * ((plane + kRedElems - 1) / kRedElems));
+    if (a.wino) return conv3x3_wino_gn_records(a);
     if (a.cout % kConvBM != 0 || (a.cout / 32) % 4 != 0) return 0;
     const int TC = conv_tc(a.W), TR = kConvBN / TC;
     return ((a.W + TC - 1) / TC) * ((a.H + TR - 1) / TR) * a.T;
@@ -642,24 +650,25 @@ int conv3x3_gn_records(const ConvLaunch &a) {
 
 const char *conv3x3_kernel_name(const ConvLaunch &a) {
     static const char *algos[2] = {"mfma", "wino"};
-    static const char *tcs[3] = {"32", "16", "8"};
+    static const char *tcs[4] = {"32", "16", "8", "4"};
     static const char *modes[4] = {"plain", "up2x", "denorm", "gnsilu"};
     static const char *tails[3] = {"", ",res", ",splitk"};
-    static char names[2][3][4][3][48];
+    static char names[2][4][4][3][48];
     static bool init = false;
     if (!init) {
         for (int g = 0; g < 2; ++g)
-            for (int t = 0; t < 3; ++t)
+            for (int t = 0; t < 4; ++t)
                 for (int m = 0; m < 4; ++m)
                     for (int k = 0; k < 3; ++k)
                         snprintf(names[g][t][m][k], sizeof names[g][t][m][k], "conv3x3_%s<%s,%s%s>", algos[g], tcs[t],
                                  modes[m], tails[k]);
         init = true;
     }
-    const int tc = conv_tc(a.W);
-    const int ti = tc == 32 ? 0 : (tc == 16 ? 1 : 2);
+    // column tile width: the implicit GEMM's output columns, the Winograd form's tiles per row
+    const int tc = a.wino ? conv3x3_wino_tcw(a) : conv_tc(a.W);
+    const int ti = tc == 32 ? 0 : (tc == 16 ? 1 : (tc == 8 ? 2 : 3));
     const int mi = a.upsample ? 1 : (a.denorm ? 2 : (a.gn_coef ? 3 : 0));
-    const int si = conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T) > 1 ? 2 : (a.res ? 1 : 0);
+    const int si = conv3x3_ksplit(a) > 1 ? 2 : (a.res ? 1 : 0);
     return names[a.wino ? 1 : 0][ti][mi][si];
 }
 
@@ -689,7 +698,7 @@ int32_t launch_conv3x3_main(const ConvLaunch &a, hipStream_t s) {
     const int TR = kConvBN / TC;
     p.tiles_x = (a.W + TC - 1) / TC;
     const int tiles_y = (a.H + TR - 1) / TR;
-    p.ksplit = conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T);
+    p.ksplit = mfma_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T);
     p.part = a.part;
     p.part_stride = p.out_cstride * a.cout;
     if (p.ksplit > 1 && !a.part) {
@@ -730,7 +739,7 @@ int32_t launch_conv3x3_main(const ConvLaunch &a, hipStream_t s) {
 }
 
 int32_t launch_conv3x3_reduce(const ConvLaunch &a, hipStream_t s) {
-    const int ksplit = conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T);
+    const int ksplit = conv3x3_ksplit(a);
     if (ksplit == 1) return VAE_OK;
     const long long plane = (long long)a.T * a.H * a.W;
     const long long part_stride = plane * a.cout;

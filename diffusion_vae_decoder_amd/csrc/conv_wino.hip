@@ -10,7 +10,7 @@
 //     A^T = [1 1 1 0; 0 1 -1 -1]
 // the sum over input channels c becomes 16 independent GEMMs, one per point
 // xi of the 4 x 4 transform: M_xi[o, tile] = sum_c U_xi[o, c] V_xi[c, tile],
-// with 16 multiplies per 2 x 2 outputs and channel pair instead of 36.
+// with 16 multiplies per 2 x 2 outputs and input channel instead of 36.
 // U = G g G^T is formed once, in double precision, when the weights are
 // packed.  The result equals the direct conv up to rounding (about 1e-6 of
 // the output's magnitude in float32 at the decoder's shapes).
@@ -21,19 +21,21 @@
 // column) 2 of B^T d B vanishes and 9 of the 16 points remain; rows 1 of
 // B^T d B double.  The kernel reads the 3 x 3 source patch directly and the
 // factors 2 are folded into U (exact).  That is 9 multiplies per 2 x 2
-// outputs and channel pair instead of 36.
+// outputs and input channel instead of 36.
 //
-// Workgroup: 4 waves; wave w owns output channels [32w, 32w + 32) of the
-// workgroup's 128 and all 32 tiles (2 x 2 output blocks) of the workgroup's
-// 4 x 32, 8 x 16 or 16 x 8 output block.  Each lane transforms one
-// (channel, tile) patch per step in registers: lane l takes tile l % 32 and
-// channel l / 32 of the step's channel pair, which is exactly the B operand
-// of v_mfma_f32_32x32x2_f32 for every point xi, so the input needs no LDS and
-// the kernel no barrier in its main loop.  The transformed weights U are
-// packed per (32-channel block, step, lane) and read straight into
-// registers.  All 16 (or 9) accumulators of a lane hold the same (output
-// channel, tile) entries, so the output transform is lane-local.  The 256
-// accumulator registers allow one wave per SIMD; loads run two steps ahead.
+// Workgroup: 4 waves, one block of 32 output channels and 64 tiles (2 x 2
+// output blocks; 256 outputs); wave w owns tiles [16w, 16w + 16).  A step is
+// four input channels: every lane transforms one (channel, tile) patch in
+// registers (lane l: tile l % 16, channel l / 16), which is exactly the B
+// operand of v_mfma_f32_16x16x4_f32 for every point xi; each point takes two
+// MFMAs (output channels 0-15 and 16-31 of the block, A operand from U).
+// All accumulators of a lane hold the same (output channels, tile) entries,
+// so the output transform is lane-local.  The 128 accumulator registers let
+// two waves share a SIMD (two workgroups per CU), so one wave's transform,
+// LDS and memory work overlaps the other's MFMAs.  The input tile with its
+// halo and the block's U are staged through LDS, kWStage steps at a time and
+// double-buffered: step j of a stage also loads step j of the next stage
+// and stores step j - 1 of it, with one barrier per stage.
 
 #include <cstdio>
 
@@ -44,16 +46,42 @@ namespace vae {
 namespace {
 
 constexpr int kWThreads = 256;
-constexpr int kWavesOut = 32;               // output channels per wave
-constexpr int kWOOB = 0x7FFFFFF0;           // buffer offset past every range: reads 0
-constexpr int kWPrefetch = 2;               // steps loaded ahead
+constexpr int kWOut = 32;        // output channels per workgroup (two MFMA row blocks of 16)
+constexpr int kWTiles = 64;      // tiles per workgroup (16 per wave)
+constexpr int kWCh = 4;          // input channels per step (the MFMA's K)
+constexpr int kWStage = 2;       // steps per LDS stage
+constexpr int kWOOB = 0x7FFFFFF0;   // buffer offset past every range: reads 0
 
 template <bool UP>
 struct WinoShape {
-    static constexpr int NX = UP ? 9 : 16;      // transform points
-    static constexpr int NXP = UP ? 12 : 16;    // packed floats per lane and step
-    static constexpr int NP = UP ? 3 : 4;       // input rows (and columns) of a tile's patch
-    static constexpr int NQ = NXP / 4;          // float4 loads of U per step
+    static constexpr int NX = UP ? 9 : 16;                 // transform points
+    static constexpr int NQ = (2 * NX + 3) / 4;            // float4s of U per lane and step (2 row blocks per point)
+    static constexpr int NP = UP ? 3 : 4;                  // input rows (and columns) of a tile's patch
+};
+
+// Channel-plane stride of a staged step.  Plain input: 8-byte patch reads,
+// 32 lanes (two channels x 16 tiles) per LDS cycle; upsampled: 4-byte reads,
+// all four channels in one cycle.  The stride puts those channels in
+// distinct bank ranges.
+constexpr int wino_plane(int n, bool up) {
+    for (int p = n; p < n + 64; ++p)
+        if (p % 64 == (up ? 16 : 32)) return p;
+    return -1;
+}
+
+template <int TCW, bool UP>
+struct WGeom {
+    static constexpr int TRW = kWTiles / TCW;          // tile rows of the block
+    static constexpr int OR = 2 * TRW, OC = 2 * TCW;   // output rows, columns of the block
+    static constexpr int HR = UP ? TRW + 2 : OR + 2;   // staged rows (source rows when upsampled)
+    static constexpr int HC = UP ? TCW + 2 : OC + 2;   // staged columns
+    static constexpr int HCP = UP ? HC : HC + (HC & 1);   // row stride (even: 8-byte reads)
+    static constexpr int PLANE = wino_plane(HR * HCP, UP);
+    static constexpr int EPT = (HR * HC + kWThreads - 1) / kWThreads;   // staged elements per thread and plane
+    static constexpr int XSTEP = kWCh * PLANE;                           // floats of input per step
+    static constexpr int USTEP = WinoShape<UP>::NQ * 64;                 // float4s of U per step
+    static constexpr int UPT = (USTEP + kWThreads - 1) / kWThreads;      // U float4s per thread and step
+    static_assert(PLANE > 0, "no LDS layout");
 };
 
 struct WParams {
@@ -63,8 +91,8 @@ struct WParams {
     const float *gn_coef;   // GroupNorm + SiLU on load: (mean, scale, beta, -) per input channel
     float *y;
     float *part;            // split-K partial sums [ksplit][cout][T][H][W]
-    floatx4 *gn_rec;        // GroupNorm records of y, as for the implicit-GEMM conv
-    int cin, cout, H, W, Hin, Win, kt, npairs, tiles_x, ksplit, gn_cpg, gn_nrec;
+    floatx4 *gn_rec;        // GroupNorm records of y, [32 groups][gn_nrec]
+    int cin, cout, H, W, Hin, Win, kt, nquads, tiles_x, ksplit, gn_cpg, gn_nrec;
     long long in_cstride, in_fstride, out_cstride, out_fstride, part_stride;
 };
 
@@ -72,82 +100,128 @@ __device__ __attribute__((always_inline)) inline __amdgpu_buffer_rsrc_t wino_rsr
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Next step to load: time tap dt, channel pair, the pair's first channel in
-// the tap's frame and the lane's packed U.  Advanced by additions only.
-struct WCursor {
-    int pair, dt;
-    const float *x;
-    const floatx4 *u;
-};
-
 __device__ __attribute__((always_inline)) inline const float *wino_frame(const WParams &p, int frame, int dt) {
     int fr = frame + dt - (p.kt - 1);
     fr = fr < 0 ? 0 : fr;
     return p.x + (long long)fr * p.in_fstride;
 }
 
-// One step's operands in registers: the lane's input patch, its packed U
-// and, for GroupNorm on load, the coefficients of the lane's channel.
-template <bool UP, bool GN>
-struct WSlot {
-    float d[WinoShape<UP>::NP * WinoShape<UP>::NP];
-    floatx4 u[WinoShape<UP>::NQ];
-    floatx4 cf;
-    bool cok;   // the lane's channel is below cin
+// The next step to stage: time tap dt and channel quad, and the quad's first
+// channel in the tap's frame.  Advanced by additions only.
+struct WCursor {
+    int quad, dt;
+    const float *x;
 };
 
-template <bool UP, bool GN>
-__device__ __attribute__((always_inline)) inline void wino_load(const WParams &p, const WCursor &c, int h,
-                                                               const int (&boff)[WinoShape<UP>::NP * WinoShape<UP>::NP],
-                                                               WSlot<UP, GN> &sl) {
-    using S = WinoShape<UP>;
-    const int rem = p.cin - 2 * c.pair;
-    const int nc = rem < 2 ? rem : 2;
-    const __amdgpu_buffer_rsrc_t xr = wino_rsrc(c.x, (unsigned)(nc * p.in_cstride * 4));
-#pragma unroll
-    for (int i = 0; i < S::NP * S::NP; ++i)
-        sl.d[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xr, boff[i], 0, 0));
-#pragma unroll
-    for (int i = 0; i < S::NQ; ++i) sl.u[i] = c.u[i];
-    if (GN) {
-        const int ch = 2 * c.pair + h;
-        sl.cok = ch < p.cin;
-        sl.cf = *reinterpret_cast<const floatx4 *>(p.gn_coef + 4 * (ch < p.cin ? ch : p.cin - 1));
-    }
-}
-
-__device__ __attribute__((always_inline)) inline void wino_next(const WParams &p, int frame, int ustep, WCursor &c) {
-    c.u += ustep;
-    if (++c.pair == p.npairs) {
-        c.pair = 0;
+__device__ __attribute__((always_inline)) inline void wino_next(const WParams &p, int frame, WCursor &c) {
+    if (++c.quad == p.nquads) {
+        c.quad = 0;
         ++c.dt;
         c.x = wino_frame(p, frame, c.dt);
     } else {
-        c.x += 2 * p.in_cstride;
+        c.x += kWCh * p.in_cstride;
     }
 }
 
-// Input transform of the lane's patch and the step's MFMAs.
-// GN: the patch is first normalised, silu((x - mean) * scale + beta), with
-// padding positions (bit clear in vmask) and channels past cin kept at 0.
-template <bool UP, bool GN>
-__device__ __attribute__((always_inline)) inline void wino_step(const WSlot<UP, GN> &sl, unsigned vmask,
-                                                               floatx16 (&acc)[WinoShape<UP>::NX]) {
-    constexpr int NPP = WinoShape<UP>::NP * WinoShape<UP>::NP;
-    float d[NPP];
+// One step's staging in registers on its way to LDS: this thread's elements
+// of the step's four channel planes, its float4s of U and, for GroupNorm on
+// load, the channels' coefficients.
+template <int TCW, bool UP, bool GN>
+struct WStep {
+    float x[kWCh][WGeom<TCW, UP>::EPT];
+    floatx4 u[WGeom<TCW, UP>::UPT];
+    floatx4 cf[kWCh];
+    bool cok[kWCh];
+};
+
+// Global -> registers for the step at the cursor, with no branch (a branch
+// around a load makes the compiler wait for every load in flight).  Channels
+// past cin, the zero padding and dead steps (live false) read 0 from the
+// buffer range check; `ustep` is a live step's U (the caller clamps it), and
+// indices past the step's float4s read its last one (not stored).
+template <int TCW, bool UP, bool GN>
+__device__ __attribute__((always_inline)) inline void wino_step_load(const WParams &p, int frame, bool live,
+                                                                    WCursor &cur, const floatx4 *ustep,
+                                                                    const int (&soff)[WGeom<TCW, UP>::EPT],
+                                                                    WStep<TCW, UP, GN> &st) {
+    using G = WGeom<TCW, UP>;
 #pragma unroll
-    for (int i = 0; i < NPP; ++i) {
+    for (int c = 0; c < kWCh; ++c) {
+        const int ch = kWCh * cur.quad + c;
+        const bool ok = live && ch < p.cin;
+        const __amdgpu_buffer_rsrc_t xr = wino_rsrc(cur.x + c * p.in_cstride, ok ? (unsigned)(p.in_cstride * 4) : 0u);
+#pragma unroll
+        for (int i = 0; i < G::EPT; ++i)
+            st.x[c][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xr, soff[i], 0, 0));
         if (GN) {
-            float t = (sl.d[i] - sl.cf[0]) * sl.cf[1] + sl.cf[2];
-            t = t * __builtin_amdgcn_rcpf(1.f + __expf(-t));
-            d[i] = (((vmask >> i) & 1u) && sl.cok) ? t : 0.f;
-        } else {
-            d[i] = sl.d[i];
+            st.cok[c] = ok;
+            st.cf[c] = *reinterpret_cast<const floatx4 *>(p.gn_coef + 4 * (ch < p.cin ? ch : p.cin - 1));
         }
     }
-    const floatx4 (&u)[WinoShape<UP>::NQ] = sl.u;
-    float v[WinoShape<UP>::NX];
+    wino_next(p, frame, cur);
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < G::UPT; ++i) {
+        const int e = t + i * kWThreads;
+        st.u[i] = ustep[e < G::USTEP ? e : G::USTEP - 1];
+    }
+}
+
+// Registers -> LDS slot j of a stage buffer (GroupNorm + SiLU applied here;
+// padding and channels past cin stay 0).  A dead step is stored as zeros
+// (input and U), so every stage runs all its kWStage steps and those add
+// exactly 0.  Elements a thread does not own go to its word of `dummy`.
+template <int TCW, bool UP, bool GN>
+__device__ __attribute__((always_inline)) inline void wino_step_store(float *lx, floatx4 *lu, float *dummy,
+                                                                     floatx4 *udummy, int j, bool live,
+                                                                     const int (&soff)[WGeom<TCW, UP>::EPT],
+                                                                     const int (&loff)[WGeom<TCW, UP>::EPT],
+                                                                     const WStep<TCW, UP, GN> &st) {
+    using G = WGeom<TCW, UP>;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < kWCh; ++c)
+#pragma unroll
+        for (int i = 0; i < G::EPT; ++i) {
+            float v = st.x[c][i];
+            if (GN) {
+                const floatx4 cf = st.cf[c];
+                float tt = (v - cf[0]) * cf[1] + cf[2];
+                tt = tt * __builtin_amdgcn_rcpf(1.f + __expf(-tt));
+                v = (st.cok[c] && soff[i] != kWOOB) ? tt : 0.f;
+            }
+            float *dst = loff[i] >= 0 ? lx + j * G::XSTEP + c * G::PLANE + loff[i] : dummy + t;
+            *dst = live ? v : 0.f;
+        }
+#pragma unroll
+    for (int i = 0; i < G::UPT; ++i) {
+        const int e = t + i * kWThreads;
+        floatx4 *ud = e < G::USTEP ? lu + j * G::USTEP + e : udummy + (t & 63);
+        *ud = live ? st.u[i] : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// One step from LDS: the lane's patch of its channel, its input transform and
+// the step's 2 NX MFMAs (A operand: U of point k and row block b is float4
+// (2k + b) / 4, component (2k + b) % 4).
+template <int TCW, bool UP>
+__device__ __attribute__((always_inline)) inline void wino_step(const float *lx, const floatx4 *lu, int j, int pbase,
+                                                               int lane, floatx4 (&acc)[WinoShape<UP>::NX][2]) {
+    using G = WGeom<TCW, UP>;
+    using S = WinoShape<UP>;
+    const float *pl = lx + j * G::XSTEP + pbase;
+    float v[S::NX];
     if (!UP) {
+        float d[16];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const floatx2 a = *reinterpret_cast<const floatx2 *>(pl + r * G::HCP);
+            const floatx2 b = *reinterpret_cast<const floatx2 *>(pl + r * G::HCP + 2);
+            d[4 * r + 0] = a[0];
+            d[4 * r + 1] = a[1];
+            d[4 * r + 2] = b[0];
+            d[4 * r + 3] = b[1];
+        }
         float t[4][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -164,8 +238,13 @@ __device__ __attribute__((always_inline)) inline void wino_step(const WSlot<UP, 
             v[4 * r + 3] = t[r][1] - t[r][3];
         }
     } else {
-        // source patch e (3 x 3): transform points (0, 1, 3) of each axis, the
+        // source patch (3 x 3): transform points (0, 1, 3) of each axis, the
         // factor 2 of point 1 being in U
+        float d[9];
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) d[3 * r + q] = pl[r * G::HCP + q];
         float t[3][3];
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
@@ -180,21 +259,30 @@ __device__ __attribute__((always_inline)) inline void wino_step(const WSlot<UP, 
             v[3 * r + 2] = t[r][1] - t[r][2];
         }
     }
+    const floatx4 *ul = lu + j * G::USTEP + lane;
 #pragma unroll
-    for (int k = 0; k < WinoShape<UP>::NX; ++k)
-        acc[k] = __builtin_amdgcn_mfma_f32_32x32x2f32(u[k >> 2][k & 3], v[k], acc[k], 0, 0, 0);
+    for (int q = 0; q < S::NQ; ++q) {
+        const floatx4 u = ul[q * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kb = 4 * q + e;
+            if (kb < 2 * S::NX)
+                acc[kb >> 1][kb & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(u[e], v[kb >> 1], acc[kb >> 1][kb & 1], 0, 0, 0);
+        }
+    }
 }
 
-// Output transform of register r of every accumulator: the lane's 2 x 2 outputs.
+// Output transform of register i of row block b of every accumulator: the
+// lane's 2 x 2 outputs.
 template <bool UP>
-__device__ __attribute__((always_inline)) inline void wino_out(const floatx16 (&acc)[WinoShape<UP>::NX], int r,
+__device__ __attribute__((always_inline)) inline void wino_out(const floatx4 (&acc)[WinoShape<UP>::NX][2], int b, int i,
                                                               float (&y)[2][2]) {
     if (!UP) {
         float s[2][4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            s[0][c] = (acc[c][r] + acc[4 + c][r]) + acc[8 + c][r];
-            s[1][c] = (acc[4 + c][r] - acc[8 + c][r]) - acc[12 + c][r];
+            s[0][c] = (acc[c][b][i] + acc[4 + c][b][i]) + acc[8 + c][b][i];
+            s[1][c] = (acc[4 + c][b][i] - acc[8 + c][b][i]) - acc[12 + c][b][i];
         }
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
@@ -205,8 +293,8 @@ __device__ __attribute__((always_inline)) inline void wino_out(const floatx16 (&
         float s[2][3];
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
-            s[0][c] = acc[c][r] + acc[3 + c][r];
-            s[1][c] = acc[3 + c][r] - acc[6 + c][r];
+            s[0][c] = acc[c][b][i] + acc[3 + c][b][i];
+            s[1][c] = acc[3 + c][b][i] - acc[6 + c][b][i];
         }
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
@@ -227,102 +315,108 @@ __device__ __attribute__((always_inline)) inline void wino_chan_merge(float (&a)
     a[0] = nt;
 }
 
-template <int TC, bool UP, bool GN, bool RES, bool SPLIT>
-__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv3x3_wino(WParams p) {
+template <int TCW, bool UP, bool GN, bool RES, bool SPLIT>
+__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv3x3_wino(WParams p) {
+    using G = WGeom<TCW, UP>;
     using S = WinoShape<UP>;
-    constexpr int TCT = TC / 2;            // tiles per row
-    constexpr int TRT = 32 / TCT;          // rows of tiles
-    constexpr int TR = 2 * TRT;            // output rows of the block
+    __shared__ __attribute__((aligned(16))) float lds_x[2][kWStage * G::XSTEP];
+    __shared__ floatx4 lds_u[2][kWStage * G::USTEP];
+    __shared__ float lds_dummy[kWThreads];   // stores of staged elements a thread does not own
+    __shared__ floatx4 lds_udummy[64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int h = lane >> 5, n = lane & 31;
+    const int g4 = lane >> 4;   // the lane's channel of a step, and its 4-row group of an MFMA output
 
-    // XCD-aware renumbering, as in the implicit-GEMM conv.
+    // XCD-aware renumbering, as in the implicit-GEMM conv: each XCD walks one
+    // contiguous band of tile blocks.
     int tile = blockIdx.x;
     if ((gridDim.x & 7) == 0) tile = (tile & 7) * (gridDim.x >> 3) + (tile >> 3);
     const int ty = tile / p.tiles_x;
     const int tx = tile - ty * p.tiles_x;
-    const int y0 = ty * TR, x0 = tx * TC;
-    const int ob = blockIdx.y;
+    const int y0 = ty * G::OR, x0 = tx * G::OC;
+    const int cb = blockIdx.y;   // block of 32 output channels
     const int frame = SPLIT ? blockIdx.z / p.ksplit : blockIdx.z;
     const int split = SPLIT ? blockIdx.z - frame * p.ksplit : 0;
 
-    const int tr = n / TCT, tc = n - (n / TCT) * TCT;
-    const int Y0 = y0 + 2 * tr, X0 = x0 + 2 * tc;   // the lane's tile (top-left output)
+    // The lane's tile and the offset of its patch in a staged step.
+    const int n = wave * 16 + (lane & 15);
+    const int tr = n / TCW, tc = n - (n / TCW) * TCW;
+    const int Y0 = y0 + 2 * tr, X0 = x0 + 2 * tc;   // top-left output of the tile
+    const int pbase = g4 * G::PLANE + (UP ? tr * G::HCP + tc : 2 * tr * G::HCP + 2 * tc);
 
-    // Byte offsets of the lane's patch from its channel pair's first channel
-    // (kWOOB for zero padding); the same for every step.
-    int boff[S::NP * S::NP];
-    unsigned vmask = 0;   // bit i: patch element i lies in the image
+    // This thread's staged elements of a plane: byte offset in the channel
+    // (kWOOB for zero padding) and LDS offset in the plane (-1: none).
+    int soff[G::EPT], loff[G::EPT];
     {
-        const int ry = UP ? (Y0 >> 1) - 1 : Y0 - 1;
-        const int rx = UP ? (X0 >> 1) - 1 : X0 - 1;
+        const int ry = UP ? (y0 >> 1) - 1 : y0 - 1;
+        const int rx = UP ? (x0 >> 1) - 1 : x0 - 1;
         const int Hs = UP ? p.Hin : p.H, Ws = UP ? p.Win : p.W;
 #pragma unroll
-        for (int r = 0; r < S::NP; ++r)
-#pragma unroll
-            for (int q = 0; q < S::NP; ++q) {
+        for (int i = 0; i < G::EPT; ++i) {
+            const int e = tid + i * kWThreads;
+            soff[i] = kWOOB;
+            loff[i] = -1;
+            if (e < G::HR * G::HC) {
+                const int r = e / G::HC, q = e - (e / G::HC) * G::HC;
                 const int yy = ry + r, xx = rx + q;
-                const bool ok = yy >= 0 && yy < Hs && xx >= 0 && xx < Ws;
-                boff[r * S::NP + q] = ok ? (int)((h * p.in_cstride + (long long)yy * Ws + xx) * 4) : kWOOB;
-                vmask |= (ok ? 1u : 0u) << (r * S::NP + q);
+                loff[i] = r * G::HCP + q;
+                if (yy >= 0 && yy < Hs && xx >= 0 && xx < Ws) soff[i] = (yy * Ws + xx) * 4;
             }
+        }
     }
 
-    const int nsteps = p.kt * p.npairs;
+    const int nsteps = p.kt * p.nquads;
     const int s0 = SPLIT ? (int)((long long)split * nsteps / p.ksplit) : 0;
     const int s1 = SPLIT ? (int)((long long)(split + 1) * nsteps / p.ksplit) : nsteps;
-    constexpr int USTEP = 64 * S::NQ;    // float4s of U per step (all lanes)
-    const int cb32 = ob * (kConvBM / kWavesOut) + wave;
+    const floatx4 *ublock = reinterpret_cast<const floatx4 *>(p.u) + (size_t)cb * nsteps * G::USTEP;
+    auto ustep = [&](int s) { return ublock + (size_t)(s < s1 ? s : s1 - 1) * G::USTEP; };
 
     WCursor cur;
-    cur.dt = s0 / p.npairs;
-    cur.pair = s0 - cur.dt * p.npairs;
-    cur.x = wino_frame(p, frame, cur.dt) + 2LL * cur.pair * p.in_cstride;
-    cur.u = reinterpret_cast<const floatx4 *>(p.u) + ((size_t)cb32 * nsteps + s0) * USTEP + lane * S::NQ;
+    cur.dt = s0 / p.nquads;
+    cur.quad = s0 - cur.dt * p.nquads;
+    cur.x = wino_frame(p, frame, cur.dt) + (long long)kWCh * cur.quad * p.in_cstride;
 
-    floatx16 acc[S::NX];
+    floatx4 acc[S::NX][2];
 #pragma unroll
     for (int k = 0; k < S::NX; ++k)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[k][r] = 0.f;
+        for (int b = 0; b < 2; ++b) acc[k][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int NB = kWPrefetch + 1;
-    WSlot<UP, GN> sl[NB];
+    const int nst = (s1 - s0 + kWStage - 1) / kWStage;
+    WStep<TCW, UP, GN> rs[kWStage];
+    // stage 0: all its loads in flight, then the stores
 #pragma unroll
-    for (int j = 0; j < kWPrefetch; ++j)
-        if (s0 + j < s1) {
-            wino_load<UP, GN>(p, cur, h, boff, sl[j]);
-            wino_next(p, frame, USTEP, cur);
-        }
-    // Steady state: groups of NB steps whose prefetches all lie in range, with
-    // no branch around a load (step s uses register slot (s - s0) % NB).
-    int s = s0;
-    for (; s + NB + kWPrefetch <= s1; s += NB) {
+    for (int j = 0; j < kWStage; ++j)
+        wino_step_load<TCW, UP, GN>(p, frame, s0 + j < s1, cur, ustep(s0 + j), soff, rs[j]);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            wino_load<UP, GN>(p, cur, h, boff, sl[(j + kWPrefetch) % NB]);
-            wino_next(p, frame, USTEP, cur);
-            wino_step<UP, GN>(sl[j], vmask, acc);
+    for (int j = 0; j < kWStage; ++j)
+        wino_step_store<TCW, UP, GN>(lds_x[0], lds_u[0], lds_dummy, lds_udummy, j, s0 + j < s1, soff, loff, rs[j]);
+    __syncthreads();
+    // Stages but the last: step j also loads step j of the next stage and
+    // stores step j - 1 of it.
+    int k = 0;
+    for (; k + 1 < nst; ++k) {
+        const int buf = k & 1;
+        const int nb = s0 + (k + 1) * kWStage;
+#pragma unroll
+        for (int j = 0; j < kWStage; ++j) {
+            wino_step_load<TCW, UP, GN>(p, frame, nb + j < s1, cur, ustep(nb + j), soff, rs[j]);
+            wino_step<TCW, UP>(lds_x[buf], lds_u[buf], j, pbase, lane, acc);
+            if (j >= 1)
+                wino_step_store<TCW, UP, GN>(lds_x[buf ^ 1], lds_u[buf ^ 1], lds_dummy, lds_udummy, j - 1,
+                                             nb + j - 1 < s1, soff, loff, rs[j - 1]);
         }
+        wino_step_store<TCW, UP, GN>(lds_x[buf ^ 1], lds_u[buf ^ 1], lds_dummy, lds_udummy, kWStage - 1,
+                                     nb + kWStage - 1 < s1, soff, loff, rs[kWStage - 1]);
+        __syncthreads();
     }
-    // The last (fewer than NB + kWPrefetch) steps.
 #pragma unroll
-    for (int j = 0; j < NB + kWPrefetch - 1; ++j) {
-        if (s + j < s1) {
-            if (s + j + kWPrefetch < s1) {
-                wino_load<UP, GN>(p, cur, h, boff, sl[(j + kWPrefetch) % NB]);
-                wino_next(p, frame, USTEP, cur);
-            }
-            wino_step<UP, GN>(sl[j % NB], vmask, acc);
-        }
-    }
+    for (int j = 0; j < kWStage; ++j) wino_step<TCW, UP>(lds_x[k & 1], lds_u[k & 1], j, pbase, lane, acc);
 
-    // Epilogue: register r of a 32x32 MFMA tile is output channel
-    // 8 (r / 4) + 4 h + r % 4 of the wave's block, for the lane's tile n.
+    // Epilogue: register i of row block b of a 16x16 MFMA tile is output
+    // channel 16 b + 4 g4 + i of the block, for the lane's tile.
     const long long fo = (long long)frame * p.out_fstride;
-    const int obase = ob * kConvBM + wave * kWavesOut + 4 * h;
     bool pv[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -337,34 +431,35 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
             sp[a][b] = fo + (long long)min(Y0 + a, p.H - 1) * p.W + min(X0 + b, p.W - 1);
     const float nval = (float)((pv[0][0] + pv[0][1] + pv[1][0] + pv[1][1]) * 4);
 
-    // Per 4-channel quad rq of the lane: its 16 outputs, and, for GroupNorm
-    // records, their count, mean and sum of squared deviations (st).
-    float st[4][3];
+    // Per row block b (the lane's quad of 4 output channels): its 16 outputs,
+    // and, for GroupNorm records, their count, mean and sum of squared
+    // deviations (gs).
+    float gs[2][3];
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
+    for (int b = 0; b < 2; ++b) {
+        const int obase = cb * kWOut + 16 * b + 4 * g4;
         float rv[4][4];
         if (RES && !SPLIT) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int o = min(obase + 8 * rq + k, p.cout - 1);
+            for (int i = 0; i < 4; ++i) {
+                const int o = min(obase + i, p.cout - 1);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rv[k][e] = p.res[(long long)o * p.out_cstride + sp[e >> 1][e & 1]];
+                for (int e = 0; e < 4; ++e) rv[i][e] = p.res[(long long)o * p.out_cstride + sp[e >> 1][e & 1]];
             }
         }
         float val[4][4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int r = 4 * rq + k;
-            const int o = obase + 8 * rq + k;
+        for (int i = 0; i < 4; ++i) {
+            const int o = obase + i;
             float yv[2][2];
-            wino_out<UP>(acc, r, yv);
+            wino_out<UP>(acc, b, i, yv);
             const long long base = (long long)min(o, p.cout - 1) * p.out_cstride;
             const float bo = SPLIT ? 0.f : p.bias[min(o, p.cout - 1)];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float v = yv[e >> 1][e & 1] + bo;
-                if (RES && !SPLIT) v += rv[k][e];
-                val[k][e] = v;
+                if (RES && !SPLIT) v += rv[i][e];
+                val[i][e] = v;
                 if (o < p.cout && pv[e >> 1][e & 1]) {
                     if (SPLIT) p.part[split * p.part_stride + base + sp[e >> 1][e & 1]] = v;
                     else p.y[base + sp[e >> 1][e & 1]] = v;
@@ -374,146 +469,199 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
         if (!SPLIT && p.gn_rec) {
             float t = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (pv[e >> 1][e & 1]) t += val[k][e];
+                    if (pv[e >> 1][e & 1]) t += val[i][e];
             const float mean = nval > 0.f ? t / nval : 0.f;
             float m2 = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (pv[e >> 1][e & 1]) {
-                        const float dv = val[k][e] - mean;
+                        const float dv = val[i][e] - mean;
                         m2 += dv * dv;
                     }
-            st[rq][0] = nval;
-            st[rq][1] = mean;
-            st[rq][2] = m2;
+            gs[b][0] = nval;
+            gs[b][1] = mean;
+            gs[b][2] = m2;
         }
     }
 
     if (!SPLIT && p.gn_rec) {
-        // GroupNorm records of the workgroup's outputs: per group (count, mean,
-        // sum of squared deviations from that mean), merged pairwise (Chan,
-        // Golub and LeVeque) over the 32 tiles of a lane half, then over the
-        // quads of a group.  The host enables this only for cout % 128 == 0 and
-        // channels per group a multiple of 4: a group is then a whole number of
-        // quads.
-        __shared__ float qst[32][3];   // per quad of the workgroup's 128 channels
+        // GroupNorm records of the block: per group (count, mean, sum of
+        // squared deviations from that mean), merged pairwise (Chan, Golub and
+        // LeVeque) over the 16 tiles of a lane group, then over the four waves
+        // and the quads of a group, in a fixed order.  Quad 4 b + g4 holds
+        // output channels 16 b + 4 g4 + (0..3) of the block.  The host enables
+        // this only when a group is a whole number of quads within 32 channels
+        // (cout % 128 == 0, cout <= 1024).
+        __syncthreads();   // the staging buffers are reused below
+        float *qst = lds_x[0];   // [wave][quad of 8][3]
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1)
+        for (int o = 1; o < 16; o <<= 1)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const float nb = __shfl_xor(st[rq][0], o, 64);
-                const float mb = __shfl_xor(st[rq][1], o, 64);
-                const float qb = __shfl_xor(st[rq][2], o, 64);
-                wino_chan_merge(st[rq], nb, mb, qb);
+            for (int b = 0; b < 2; ++b) {
+                const float nb = __shfl_xor(gs[b][0], o, 64);
+                const float mb = __shfl_xor(gs[b][1], o, 64);
+                const float qb = __shfl_xor(gs[b][2], o, 64);
+                wino_chan_merge(gs[b], nb, mb, qb);
             }
-        if (n == 0)
+        if ((lane & 15) == 0)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int qd = wave * 8 + 2 * rq + h;
-                qst[qd][0] = st[rq][0];
-                qst[qd][1] = st[rq][1];
-                qst[qd][2] = st[rq][2];
+            for (int b = 0; b < 2; ++b) {
+                float *d = qst + (wave * 8 + 4 * b + g4) * 3;
+                d[0] = gs[b][0];
+                d[1] = gs[b][1];
+                d[2] = gs[b][2];
             }
         __syncthreads();
         const int qpg = p.gn_cpg >> 2;
-        const int gpb = kConvBM / p.gn_cpg;
+        const int gpb = kWOut / p.gn_cpg;
         if (tid < gpb) {
-            float g[3] = {qst[tid * qpg][0], qst[tid * qpg][1], qst[tid * qpg][2]};
-            for (int k = 1; k < qpg; ++k) wino_chan_merge(g, qst[tid * qpg + k][0], qst[tid * qpg + k][1], qst[tid * qpg + k][2]);
-            const long long rec = (long long)(ob * gpb + tid) * p.gn_nrec + (long long)frame * gridDim.x + tile;
+            float g[3] = {0.f, 0.f, 0.f};
+            for (int w = 0; w < 4; ++w)
+                for (int q = 0; q < qpg; ++q) {
+                    const float *d = qst + (w * 8 + tid * qpg + q) * 3;
+                    wino_chan_merge(g, d[0], d[1], d[2]);
+                }
+            const long long rec = (long long)(cb * gpb + tid) * p.gn_nrec + (long long)frame * gridDim.x + tile;
             p.gn_rec[rec] = floatx4{g[0], g[1], g[2], 0.f};
         }
     }
 }
 
-
-// Packed U: [cout block of 32][step = (dt, channel pair)][lane][NXP], lane =
-// (channel of the pair) * 32 + (output channel in the block); zero where the
-// output or input channel is out of range.  One thread per (block, step, lane).
+// Packed U: [32-channel output block][step = (dt, channel quad)][q][lane][4]
+// with lane = (channel of the quad) * 16 + (output channel within its row
+// block) and float4 component e of q holding transform point (4q + e) / 2 of
+// row block (4q + e) % 2; zero where the output or input channel is out of
+// range and in the padding.  One thread per (block, step, lane).
 template <bool UP>
 __global__ __launch_bounds__(256) void pack_wino_kernel(const float *__restrict__ w, float *__restrict__ dst, int cout,
-                                                        int cin, int kt, int npairs, long long total) {
+                                                        int cin, int kt, int nquads, long long total) {
     using S = WinoShape<UP>;
     const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
     if (id >= total) return;
     const int lane = (int)(id & 63);
-    const long long bs = id >> 6;
-    const int nsteps = kt * npairs;
-    const int cb32 = (int)(bs / nsteps);
-    const int s = (int)(bs - (long long)cb32 * nsteps);
-    const int dt = s / npairs, pair = s - dt * npairs;
-    const int o = cb32 * kWavesOut + (lane & 31);
-    const int c = 2 * pair + (lane >> 5);
-    double g[3][3];
-#pragma unroll
-    for (int i = 0; i < 9; ++i)
-        g[i / 3][i % 3] = (o < cout && c < cin) ? (double)w[(((long long)o * cin + c) * kt + dt) * 9 + i] : 0.0;
-    // U = G g G^T
+    const long long bs = id >> 6;   // block * nsteps + step
+    const int nsteps = kt * nquads;
+    const int cb = (int)(bs / nsteps);
+    const int s = (int)(bs - (long long)cb * nsteps);
+    const int dt = s / nquads, quad = s - dt * nquads;
+    const int c = kWCh * quad + (lane >> 4);
     const double G[4][3] = {{1.0, 0.0, 0.0}, {0.5, 0.5, 0.5}, {0.5, -0.5, 0.5}, {0.0, 0.0, 1.0}};
-    double t[4][3];
+    float u[2][16];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int b = 0; b < 2; ++b) {
+        const int o = cb * kWOut + 16 * b + (lane & 15);
+        double g[3][3];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) t[x][j] = G[x][0] * g[0][j] + G[x][1] * g[1][j] + G[x][2] * g[2][j];
-    float *out = dst + id * S::NXP;
-    if (!UP) {
+        for (int i = 0; i < 9; ++i)
+            g[i / 3][i % 3] = (o < cout && c < cin) ? (double)w[(((long long)o * cin + c) * kt + dt) * 9 + i] : 0.0;
+        // U = G g G^T
+        double t[4][3];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
-            for (int y = 0; y < 4; ++y) out[4 * x + y] = (float)(t[x][0] * G[y][0] + t[x][1] * G[y][1] + t[x][2] * G[y][2]);
-    } else {
-        const int pts[3] = {0, 1, 3};
+            for (int j = 0; j < 3; ++j) t[x][j] = G[x][0] * g[0][j] + G[x][1] * g[1][j] + G[x][2] * g[2][j];
+        if (!UP) {
 #pragma unroll
-        for (int ix = 0; ix < 3; ++ix)
+            for (int x = 0; x < 4; ++x)
 #pragma unroll
-            for (int iy = 0; iy < 3; ++iy) {
-                const int x = pts[ix], y = pts[iy];
-                const double f = (ix == 1 ? 2.0 : 1.0) * (iy == 1 ? 2.0 : 1.0);
-                out[3 * ix + iy] = (float)(f * (t[x][0] * G[y][0] + t[x][1] * G[y][1] + t[x][2] * G[y][2]));
-            }
+                for (int y = 0; y < 4; ++y)
+                    u[b][4 * x + y] = (float)(t[x][0] * G[y][0] + t[x][1] * G[y][1] + t[x][2] * G[y][2]);
+        } else {
+            const int pts[3] = {0, 1, 3};
 #pragma unroll
-        for (int k = 9; k < S::NXP; ++k) out[k] = 0.f;
+            for (int ix = 0; ix < 3; ++ix)
+#pragma unroll
+                for (int iy = 0; iy < 3; ++iy) {
+                    const int x = pts[ix], y = pts[iy];
+                    const double f = (ix == 1 ? 2.0 : 1.0) * (iy == 1 ? 2.0 : 1.0);
+                    u[b][3 * ix + iy] = (float)(f * (t[x][0] * G[y][0] + t[x][1] * G[y][1] + t[x][2] * G[y][2]));
+                }
+        }
     }
+    float *out = dst + bs * (S::NQ * 64 * 4) + lane * 4;
+#pragma unroll
+    for (int q = 0; q < S::NQ; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kb = 4 * q + e;
+            out[q * 256 + e] = kb < 2 * S::NX ? u[kb & 1][kb >> 1] : 0.f;
+        }
 }
 
-int wino_tc(int W) { return W > 16 ? 32 : (W > 8 ? 16 : 8); }
+int wino_tcw(int W) { return W > 16 ? 16 : (W > 8 ? 8 : 4); }
 
-template <int TC, bool UP, bool GN>
+struct WinoGrid {
+    int tcw, tiles_x, tiles_y, ncb;
+};
+
+WinoGrid wino_grid(int cout, int H, int W) {
+    WinoGrid g;
+    g.tcw = wino_tcw(W);
+    const int oc = 2 * g.tcw, orr = 2 * (kWTiles / g.tcw);
+    g.tiles_x = (W + oc - 1) / oc;
+    g.tiles_y = (H + orr - 1) / orr;
+    g.ncb = (cout + kWOut - 1) / kWOut;
+    return g;
+}
+
+template <int TCW, bool UP, bool GN>
 void wino_launch_t(const WParams &p, bool res, bool split, dim3 grid, hipStream_t s) {
-    if (split) hipLaunchKernelGGL((conv3x3_wino<TC, UP, GN, false, true>), grid, dim3(kWThreads), 0, s, p);
-    else if (res) hipLaunchKernelGGL((conv3x3_wino<TC, UP, GN, true, false>), grid, dim3(kWThreads), 0, s, p);
-    else hipLaunchKernelGGL((conv3x3_wino<TC, UP, GN, false, false>), grid, dim3(kWThreads), 0, s, p);
+    if (split) hipLaunchKernelGGL((conv3x3_wino<TCW, UP, GN, false, true>), grid, dim3(kWThreads), 0, s, p);
+    else if (res) hipLaunchKernelGGL((conv3x3_wino<TCW, UP, GN, true, false>), grid, dim3(kWThreads), 0, s, p);
+    else hipLaunchKernelGGL((conv3x3_wino<TCW, UP, GN, false, false>), grid, dim3(kWThreads), 0, s, p);
 }
 
-template <int TC>
+template <int TCW>
 void wino_launch_tc(const WParams &p, bool up, bool gn, bool res, bool split, dim3 grid, hipStream_t s) {
-    if (up) wino_launch_t<TC, true, false>(p, res, split, grid, s);
-    else if (gn) wino_launch_t<TC, false, true>(p, res, split, grid, s);
-    else wino_launch_t<TC, false, false>(p, res, split, grid, s);
+    if (up) wino_launch_t<TCW, true, false>(p, res, split, grid, s);
+    else if (gn) wino_launch_t<TCW, false, true>(p, res, split, grid, s);
+    else wino_launch_t<TCW, false, false>(p, res, split, grid, s);
 }
+
+constexpr int kWSlots = 512;   // resident workgroups: two per CU
 
 }  // namespace
 
 size_t conv3x3_wino_packed_floats(int cout, int cin, int kt, int up) {
-    const size_t ncb32 = (size_t)((cout + kConvBM - 1) / kConvBM) * (kConvBM / kWavesOut);
-    const size_t nsteps = (size_t)kt * ((cin + 1) / 2);
-    return ncb32 * nsteps * 64 * (up ? WinoShape<true>::NXP : WinoShape<false>::NXP);
+    const size_t ncb = (size_t)(cout + kWOut - 1) / kWOut;
+    const size_t nsteps = (size_t)kt * ((cin + kWCh - 1) / kWCh);
+    return ncb * nsteps * 64 * 4 * (up ? WinoShape<true>::NQ : WinoShape<false>::NQ);
 }
 
 int32_t pack_conv3x3_wino(const float *w, int cout, int cin, int kt, int up, float *dst, hipStream_t s) {
-    const int npairs = (cin + 1) / 2;
-    const long long ncb32 = (long long)((cout + kConvBM - 1) / kConvBM) * (kConvBM / kWavesOut);
-    const long long total = ncb32 * kt * npairs * 64;
+    const int nquads = (cin + kWCh - 1) / kWCh;
+    const long long ncb = (cout + kWOut - 1) / kWOut;
+    const long long total = ncb * kt * nquads * 64;
     const dim3 grid((unsigned)((total + 255) / 256));
-    if (up) hipLaunchKernelGGL(pack_wino_kernel<true>, grid, dim3(256), 0, s, w, dst, cout, cin, kt, npairs, total);
-    else hipLaunchKernelGGL(pack_wino_kernel<false>, grid, dim3(256), 0, s, w, dst, cout, cin, kt, npairs, total);
+    if (up) hipLaunchKernelGGL(pack_wino_kernel<true>, grid, dim3(256), 0, s, w, dst, cout, cin, kt, nquads, total);
+    else hipLaunchKernelGGL(pack_wino_kernel<false>, grid, dim3(256), 0, s, w, dst, cout, cin, kt, nquads, total);
     return check_launch("pack_conv3x3_wino");
 }
+
+int conv3x3_wino_ksplit(const ConvLaunch &a) {
+    const WinoGrid g = wino_grid(a.cout, a.H, a.W);
+    const long long base = (long long)g.tiles_x * g.tiles_y * g.ncb * a.T;
+    if (base >= 2 * kWSlots) return 1;
+    const int nsteps = a.kt * ((a.cin + kWCh - 1) / kWCh);
+    long long s = (2 * kWSlots + base - 1) / base;     // about two rounds of workgroups
+    if (s > nsteps / (2 * kWStage)) s = nsteps / (2 * kWStage);   // each split keeps >= 2 stages
+    if (s > 16) s = 16;
+    if (s * a.T > 65535) s = 65535 / a.T;
+    return s < 1 ? 1 : (int)s;
+}
+
+int conv3x3_wino_gn_records(const ConvLaunch &a) {
+    if (a.cout % 128 != 0 || a.cout > 32 * kWOut) return 0;
+    const WinoGrid g = wino_grid(a.cout, a.H, a.W);
+    return g.tiles_x * g.tiles_y * a.T;
+}
+
+int conv3x3_wino_tcw(const ConvLaunch &a) { return wino_tcw(a.W); }
 
 int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s) {
     if (a.denorm || (a.gn_coef && a.upsample)) {
@@ -526,6 +674,10 @@ int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s) {
     }
     if (a.gn_coef && (reinterpret_cast<uintptr_t>(a.gn_coef) & 15)) {
         set_error("conv3x3_wino: GroupNorm coefficients must be 16-byte aligned");
+        return VAE_ERR_INVALID_ARG;
+    }
+    if (a.upsample && ((a.H | a.W) & 1)) {
+        set_error("conv3x3_wino: an upsampled input has even sizes");
         return VAE_ERR_INVALID_ARG;
     }
     WParams p;
@@ -542,38 +694,32 @@ int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s) {
     p.Hin = a.upsample ? a.H / 2 : a.H;
     p.Win = a.upsample ? a.W / 2 : a.W;
     p.kt = a.kt;
-    p.npairs = (a.cin + 1) / 2;
+    p.nquads = (a.cin + kWCh - 1) / kWCh;
     p.in_fstride = (long long)p.Hin * p.Win;
     p.in_cstride = p.in_fstride * a.T;
     p.out_fstride = (long long)a.H * a.W;
     p.out_cstride = p.out_fstride * a.T;
-    const int TC = wino_tc(a.W);
-    const int TR = 128 / TC;
-    p.tiles_x = (a.W + TC - 1) / TC;
-    const int tiles_y = (a.H + TR - 1) / TR;
-    p.ksplit = conv3x3_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T);
+    const WinoGrid g = wino_grid(a.cout, a.H, a.W);
+    p.tiles_x = g.tiles_x;
+    p.ksplit = conv3x3_wino_ksplit(a);
     p.part = a.part;
     p.part_stride = p.out_cstride * a.cout;
     if (p.ksplit > 1 && !a.part) {
         set_error("conv3x3_wino: split-K needs a partial-sum workspace");
         return VAE_ERR_WORKSPACE;
     }
-    if (p.in_cstride * 2 * 4 >= (1LL << 31)) {
-        set_error("conv3x3_wino: input plane of %lld elements is too large", p.in_cstride);
+    // byte offsets within one channel are 32-bit
+    if (p.in_cstride * 4 >= (1LL << 31)) {
+        set_error("conv3x3_wino: input channel of %lld elements is too large", p.in_cstride);
         return VAE_ERR_UNSUPPORTED;
     }
-    if (a.upsample && ((a.H | a.W) & 1)) {
-        set_error("conv3x3_wino: an upsampled input has even sizes");
-        return VAE_ERR_INVALID_ARG;
-    }
-    const dim3 grid((unsigned)(p.tiles_x * tiles_y), (unsigned)((a.cout + kConvBM - 1) / kConvBM),
-                    (unsigned)(a.T * p.ksplit));
+    const dim3 grid((unsigned)(g.tiles_x * g.tiles_y), (unsigned)g.ncb, (unsigned)(a.T * p.ksplit));
     p.gn_rec = nullptr;
     p.gn_cpg = 0;
     p.gn_nrec = 0;
     if (a.gn_rec && p.ksplit == 1) {
-        if (conv3x3_gn_records(a) == 0) {
-            set_error("conv3x3_wino: GroupNorm records in the epilogue need out_channels %% 128 == 0");
+        if (conv3x3_wino_gn_records(a) == 0) {
+            set_error("conv3x3_wino: GroupNorm records in the epilogue need out_channels %% 128 == 0 (<= 1024)");
             return VAE_ERR_UNSUPPORTED;
         }
         p.gn_rec = a.gn_rec;
@@ -581,9 +727,11 @@ int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s) {
         p.gn_nrec = (int)(grid.x * grid.z);
     }
     const bool up = a.upsample != 0, gn = a.gn_coef != nullptr, res = a.res != nullptr, split = p.ksplit > 1;
-    if (TC == 32) wino_launch_tc<32>(p, up, gn, res, split, grid, s);
-    else if (TC == 16) wino_launch_tc<16>(p, up, gn, res, split, grid, s);
-    else wino_launch_tc<8>(p, up, gn, res, split, grid, s);
+    switch (g.tcw) {
+    case 16: wino_launch_tc<16>(p, up, gn, res, split, grid, s); break;
+    case 8: wino_launch_tc<8>(p, up, gn, res, split, grid, s); break;
+    default: wino_launch_tc<4>(p, up, gn, res, split, grid, s); break;
+    }
     return check_launch("conv3x3_wino");
 }
 

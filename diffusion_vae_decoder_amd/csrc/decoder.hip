@@ -278,6 +278,8 @@ ConvLaunch launch_shape(const DConv &c, long long H, long long W, int T, int kt)
     a.W = (int)W;
     a.T = T;
     a.kt = kt;
+    a.wino = c.layout;
+    a.upsample = c.layout == 2;
     return a;
 }
 
@@ -295,7 +297,7 @@ Plan plan_for(const vae_decoder *d, int T, int h, int w) {
         if ((size_t)c * 16 > p.coef) p.coef = (size_t)c * 16;
     };
     auto part = [&](const DConv &c, long long H, long long W) {
-        const size_t n = conv3x3_partial_floats(c.cout, c.cin, kt, (int)H, (int)W, T);
+        const size_t n = conv3x3_partial_floats(launch_shape(c, H, W, T, kt));
         if (n > p.part) p.part = n;
         const size_t r = (size_t)32 * conv3x3_gn_records(launch_shape(c, H, W, T, kt)) * sizeof(floatx4);
         if (r > p.rec) p.rec = r;
@@ -405,7 +407,7 @@ struct Runner {
         const double in_elems = (double)c.cin * T * H * W / (up ? 4.0 : 1.0);
         const double out_elems = (double)c.cout * T * H * W;
         const double bytes = 4.0 * (in_elems + out_elems * (res ? 2.0 : 1.0));
-        const int ks = conv3x3_ksplit(c.cout, c.cin, d->kt, H, W, T);
+        const int ks = conv3x3_ksplit(a);
         ProfEntry *e = begin(conv3x3_kernel_name(a), layer, conv_flops(c, H, W, d->kt) * T,
                              ks > 1 ? 4.0 * (in_elems + out_elems * ks) : bytes);
         if (rc != VAE_OK) return;

@@ -59,10 +59,11 @@ int32_t pack_conv3x3(const float *w, int cout, int cin, int kt, float *dst, hipS
 int32_t launch_conv3x3(const ConvLaunch &a, hipStream_t s);
 int32_t launch_conv3x3_main(const ConvLaunch &a, hipStream_t s);
 int32_t launch_conv3x3_reduce(const ConvLaunch &a, hipStream_t s);
-// K-split factor launch_conv3x3 uses for a conv of this shape (1 = none), and
-// the partial-sum workspace it then needs (floats, 0 when not split).
-int conv3x3_ksplit(int cout, int cin, int kt, int H, int W, int T);
-size_t conv3x3_partial_floats(int cout, int cin, int kt, int H, int W, int T);
+// K-split factor launch_conv3x3 uses for `a` (its shape and weight layout;
+// 1 = none), and the partial-sum workspace it then needs (floats, 0 when not
+// split).
+int conv3x3_ksplit(const ConvLaunch &a);
+size_t conv3x3_partial_floats(const ConvLaunch &a);
 // GroupNorm records per group that launch_conv3x3 writes for `a` when
 // a.gn_rec is set; 0 if this launch cannot produce them (then normalise with
 // a separate statistics pass).
@@ -78,6 +79,9 @@ const char *conv3x3_kernel_name(const ConvLaunch &a);
 size_t conv3x3_wino_packed_floats(int cout, int cin, int kt, int up);
 int32_t pack_conv3x3_wino(const float *w, int cout, int cin, int kt, int up, float *dst, hipStream_t s);
 int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s);
+int conv3x3_wino_ksplit(const ConvLaunch &a);
+int conv3x3_wino_gn_records(const ConvLaunch &a);
+int conv3x3_wino_tcw(const ConvLaunch &a);   // tiles per row of its workgroup block
 // The ConvLaunch::wino layout a conv uses (the Winograd form unless its input
 // is de-normalised on load), its packed floats (`upsample`: input upsampled)
 // and the packing.  conv3x3_pack_floats_max bounds both layouts.
