@@ -75,8 +75,9 @@ struct WGeom {
     static constexpr int OR = 2 * TRW, OC = 2 * TCW;   // output rows, columns of the block
     static constexpr int HR = UP ? TRW + 2 : OR + 2;   // staged rows (source rows when upsampled)
     static constexpr int HC = UP ? TCW + 2 : OC + 2;   // staged columns
-    static constexpr int HCP = UP ? HC : HC + (HC & 1);   // row stride (even: 8-byte reads)
-    static constexpr int PLANE = wino_plane(HR * HCP, UP);
+    static constexpr int HCP = HC;   // row stride: contiguous rows (HC is even for plain input: 8-byte reads)
+    static constexpr int NCH = (HR * HC + 63) / 64;       // 64-element chunks of a staged plane
+    static constexpr int PLANE = wino_plane(NCH * 64, UP);
     static constexpr int EPT = (HR * HC + kWThreads - 1) / kWThreads;   // staged elements per thread and plane
     static constexpr int XSTEP = kWCh * PLANE;                           // floats of input per step
     static constexpr int USTEP = WinoShape<UP>::NQ * 64;                 // float4s of U per step
@@ -201,6 +202,53 @@ __device__ __attribute__((always_inline)) inline void wino_step_store(float *lx,
     }
 }
 
+// Direct global -> LDS load: lane i's 4 (16) bytes land at lds + i (float or
+// float4); an offset past the buffer's range writes 0.
+__device__ __attribute__((always_inline)) inline void wino_dma4(__amdgpu_buffer_rsrc_t r, float *lds, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voffset, 0, 0, 0);
+}
+__device__ __attribute__((always_inline)) inline void wino_dma16(__amdgpu_buffer_rsrc_t r, floatx4 *lds, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
+}
+
+// Issue the direct loads of one stage (kWStage steps from sb) into (lx, lu):
+// wave w takes chunks w, w + 4, ... of every channel plane and float4 rows
+// w, w + 4, ... of every step's U.  Channels past cin, the zero padding and
+// dead steps (from s1 on: zero-range buffers) land as zeros, so every stage
+// runs all its steps and those add exactly 0.
+template <int TCW, bool UP>
+__device__ __attribute__((always_inline)) inline void wino_stage_dma(const WParams &p, int frame, int sb, int s1,
+                                                                    WCursor &cur, const floatx4 *ublock, float *lx,
+                                                                    floatx4 *lu,
+                                                                    const int (&soffd)[(WGeom<TCW, UP>::NCH + 3) / 4]) {
+    using G = WGeom<TCW, UP>;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < kWStage; ++j) {
+        const bool live = sb + j < s1;
+#pragma unroll
+        for (int c = 0; c < kWCh; ++c) {
+            const int ch = kWCh * cur.quad + c;
+            const bool ok = live && ch < p.cin;
+            const __amdgpu_buffer_rsrc_t xr = wino_rsrc(cur.x + c * p.in_cstride, ok ? (unsigned)(p.in_cstride * 4) : 0u);
+#pragma unroll
+            for (int i = 0; i < (G::NCH + 3) / 4; ++i) {
+                const int ck = w + 4 * i;
+                if (ck < G::NCH) wino_dma4(xr, lx + j * G::XSTEP + c * G::PLANE + 64 * ck, soffd[i]);
+            }
+        }
+        wino_next(p, frame, cur);
+        const int s = live ? sb + j : s1 - 1;
+        const __amdgpu_buffer_rsrc_t ur = wino_rsrc(reinterpret_cast<const float *>(ublock + (size_t)s * G::USTEP),
+                                                    live ? (unsigned)(G::USTEP * 16) : 0u);
+#pragma unroll
+        for (int i = 0; i < (WinoShape<UP>::NQ + 3) / 4; ++i) {
+            const int q = w + 4 * i;
+            if (q < WinoShape<UP>::NQ) wino_dma16(ur, lu + j * G::USTEP + q * 64, (q * 64 + lane) * 16);
+        }
+    }
+}
+
 // One step from LDS: the lane's patch of its channel, its input transform and
 // the step's 2 NX MFMAs (A operand: U of point k and row block b is float4
 // (2k + b) / 4, component (2k + b) % 4).
@@ -319,10 +367,15 @@ template <int TCW, bool UP, bool GN, bool RES, bool SPLIT>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv3x3_wino(WParams p) {
     using G = WGeom<TCW, UP>;
     using S = WinoShape<UP>;
-    __shared__ __attribute__((aligned(16))) float lds_x[2][kWStage * G::XSTEP];
-    __shared__ floatx4 lds_u[2][kWStage * G::USTEP];
-    __shared__ float lds_dummy[kWThreads];   // stores of staged elements a thread does not own
-    __shared__ floatx4 lds_udummy[64];
+    // Two stage buffers, declared apart: the compiler then knows that LDS
+    // reads of one buffer do not wait for direct loads into the other.
+    __shared__ __attribute__((aligned(16))) float lx0[kWStage * G::XSTEP];
+    __shared__ __attribute__((aligned(16))) float lx1[kWStage * G::XSTEP];
+    __shared__ floatx4 lu0[kWStage * G::USTEP];
+    __shared__ floatx4 lu1[kWStage * G::USTEP];
+    // GroupNorm on load: stores of staged elements a thread does not own
+    __shared__ float lds_dummy[GN ? kWThreads : 1];
+    __shared__ floatx4 lds_udummy[GN ? 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -345,10 +398,11 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int Y0 = y0 + 2 * tr, X0 = x0 + 2 * tc;   // top-left output of the tile
     const int pbase = g4 * G::PLANE + (UP ? tr * G::HCP + tc : 2 * tr * G::HCP + 2 * tc);
 
-    // This thread's staged elements of a plane: byte offset in the channel
-    // (kWOOB for zero padding) and LDS offset in the plane (-1: none).
+    // GroupNorm on load: this thread's staged elements of a plane, their byte
+    // offset in the channel (kWOOB for zero padding) and LDS offset in the
+    // plane (-1: none).
     int soff[G::EPT], loff[G::EPT];
-    {
+    if (GN) {
         const int ry = UP ? (y0 >> 1) - 1 : y0 - 1;
         const int rx = UP ? (x0 >> 1) - 1 : x0 - 1;
         const int Hs = UP ? p.Hin : p.H, Ws = UP ? p.Win : p.W;
@@ -384,35 +438,78 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         for (int b = 0; b < 2; ++b) acc[k][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     const int nst = (s1 - s0 + kWStage - 1) / kWStage;
-    WStep<TCW, UP, GN> rs[kWStage];
-    // stage 0: all its loads in flight, then the stores
+    if constexpr (!GN) {
+        // Direct loads: per-lane offsets of this wave's chunks of a staged plane.
+        int soffd[(G::NCH + 3) / 4];
+        {
+            const int ry = UP ? (y0 >> 1) - 1 : y0 - 1;
+            const int rx = UP ? (x0 >> 1) - 1 : x0 - 1;
+            const int Hs = UP ? p.Hin : p.H, Ws = UP ? p.Win : p.W;
 #pragma unroll
-    for (int j = 0; j < kWStage; ++j)
-        wino_step_load<TCW, UP, GN>(p, frame, s0 + j < s1, cur, ustep(s0 + j), soff, rs[j]);
-#pragma unroll
-    for (int j = 0; j < kWStage; ++j)
-        wino_step_store<TCW, UP, GN>(lds_x[0], lds_u[0], lds_dummy, lds_udummy, j, s0 + j < s1, soff, loff, rs[j]);
-    __syncthreads();
-    // Stages but the last: step j also loads step j of the next stage and
-    // stores step j - 1 of it.
-    int k = 0;
-    for (; k + 1 < nst; ++k) {
-        const int buf = k & 1;
-        const int nb = s0 + (k + 1) * kWStage;
-#pragma unroll
-        for (int j = 0; j < kWStage; ++j) {
-            wino_step_load<TCW, UP, GN>(p, frame, nb + j < s1, cur, ustep(nb + j), soff, rs[j]);
-            wino_step<TCW, UP>(lds_x[buf], lds_u[buf], j, pbase, lane, acc);
-            if (j >= 1)
-                wino_step_store<TCW, UP, GN>(lds_x[buf ^ 1], lds_u[buf ^ 1], lds_dummy, lds_udummy, j - 1,
-                                             nb + j - 1 < s1, soff, loff, rs[j - 1]);
+            for (int i = 0; i < (G::NCH + 3) / 4; ++i) {
+                const int e = 64 * (wave + 4 * i) + lane;
+                const int r = e / G::HC, q = e - (e / G::HC) * G::HC;
+                const int yy = ry + r, xx = rx + q;
+                soffd[i] = (e < G::HR * G::HC && yy >= 0 && yy < Hs && xx >= 0 && xx < Ws) ? (yy * Ws + xx) * 4 : kWOOB;
+            }
         }
-        wino_step_store<TCW, UP, GN>(lds_x[buf ^ 1], lds_u[buf ^ 1], lds_dummy, lds_udummy, kWStage - 1,
-                                     nb + kWStage - 1 < s1, soff, loff, rs[kWStage - 1]);
+        // Stage k + 1 is loaded while stage k is computed; the loop is unrolled
+        // by two so each buffer is named statically.
+        wino_stage_dma<TCW, UP>(p, frame, s0, s1, cur, ublock, lx0, lu0, soffd);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-    }
+        int k = 0;
+        for (; k + 2 <= nst; k += 2) {
+            const int sb = s0 + k * kWStage;
+            wino_stage_dma<TCW, UP>(p, frame, sb + kWStage, s1, cur, ublock, lx1, lu1, soffd);
 #pragma unroll
-    for (int j = 0; j < kWStage; ++j) wino_step<TCW, UP>(lds_x[k & 1], lds_u[k & 1], j, pbase, lane, acc);
+            for (int j = 0; j < kWStage; ++j) wino_step<TCW, UP>(lx0, lu0, j, pbase, lane, acc);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (k + 2 < nst) wino_stage_dma<TCW, UP>(p, frame, sb + 2 * kWStage, s1, cur, ublock, lx0, lu0, soffd);
+#pragma unroll
+            for (int j = 0; j < kWStage; ++j) wino_step<TCW, UP>(lx1, lu1, j, pbase, lane, acc);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        if (k < nst) {   // an odd stage count: the last stage is in buffer 0
+#pragma unroll
+            for (int j = 0; j < kWStage; ++j) wino_step<TCW, UP>(lx0, lu0, j, pbase, lane, acc);
+        }
+    } else {
+        // GroupNorm on load: staged through registers, where each element is
+        // normalised.
+        WStep<TCW, UP, GN> rs[kWStage];
+        // stage 0: all its loads in flight, then the stores
+#pragma unroll
+        for (int j = 0; j < kWStage; ++j)
+            wino_step_load<TCW, UP, GN>(p, frame, s0 + j < s1, cur, ustep(s0 + j), soff, rs[j]);
+#pragma unroll
+        for (int j = 0; j < kWStage; ++j)
+            wino_step_store<TCW, UP, GN>(lx0, lu0, lds_dummy, lds_udummy, j, s0 + j < s1, soff, loff, rs[j]);
+        __syncthreads();
+        // Stages but the last: step j also loads step j of the next stage and
+        // stores step j - 1 of it.
+        int k = 0;
+        for (; k + 1 < nst; ++k) {
+            const int buf = k & 1;
+            const int nb = s0 + (k + 1) * kWStage;
+#pragma unroll
+            for (int j = 0; j < kWStage; ++j) {
+                wino_step_load<TCW, UP, GN>(p, frame, nb + j < s1, cur, ustep(nb + j), soff, rs[j]);
+                wino_step<TCW, UP>(buf ? lx1 : lx0, buf ? lu1 : lu0, j, pbase, lane, acc);
+                if (j >= 1)
+                    wino_step_store<TCW, UP, GN>(buf ? lx0 : lx1, buf ? lu0 : lu1, lds_dummy, lds_udummy, j - 1,
+                                                 nb + j - 1 < s1, soff, loff, rs[j - 1]);
+            }
+            wino_step_store<TCW, UP, GN>(buf ? lx0 : lx1, buf ? lu0 : lu1, lds_dummy, lds_udummy, kWStage - 1,
+                                         nb + kWStage - 1 < s1, soff, loff, rs[kWStage - 1]);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < kWStage; ++j)
+            wino_step<TCW, UP>((k & 1) ? lx1 : lx0, (k & 1) ? lu1 : lu0, j, pbase, lane, acc);
+    }
 
     // Epilogue: register i of row block b of a 16x16 MFMA tile is output
     // channel 16 b + 4 g4 + i of the block, for the lane's tile.
@@ -498,7 +595,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         // this only when a group is a whole number of quads within 32 channels
         // (cout % 128 == 0, cout <= 1024).
         __syncthreads();   // the staging buffers are reused below
-        float *qst = lds_x[0];   // [wave][quad of 8][3]
+        float *qst = lx0;   // [wave][quad of 8][3]
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1)
 #pragma unroll
