@@ -16,7 +16,7 @@ VAE_ERR_INVALID_ARG = -1
 VAE_ERR_UNSUPPORTED = -2
 VAE_ERR_WORKSPACE = -3
 VAE_ERR_HIP = -4
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class VaeConv(ctypes.Structure):
@@ -92,6 +92,8 @@ SIGNATURES = {
     "vae_decoder_destroy": (None, [c_void_p]),
     "vae_decoder_set_groupnorm_fusion": (c_int32, [c_void_p, c_int32]),
     "vae_decoder_set_graph": (c_int32, [c_void_p, c_int32]),
+    "vae_set_conv3x3_algorithm": (c_int32, [c_int32]),
+    "vae_get_conv3x3_algorithm": (c_int32, []),
     "vae_decoder_set_profiling": (c_int32, [c_void_p, c_int32]),
     "vae_decoder_profile": (c_int32, [c_void_p, POINTER(VaeProfRecord), c_int32, POINTER(c_int32)]),
 }

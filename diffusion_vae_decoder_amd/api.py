@@ -19,8 +19,24 @@ from ._lib import VaeAttn, VaeConv, VaeError, VaeNorm, VaeProfRecord, VaeResnet,
 
 __all__ = [
     "VaeError", "conv2d", "conv_in", "groupnorm_silu", "upsample_nearest2x", "attention",
-    "conv3d_causal", "Decoder",
+    "conv3d_causal", "Decoder", "CONV3X3_ALGORITHMS", "set_conv3x3_algorithm", "get_conv3x3_algorithm",
 ]
+
+# Forms of the 3x3 convolutions (vae_set_conv3x3_algorithm).
+CONV3X3_ALGORITHMS = {"winograd": 0, "implicit_gemm": 1}
+
+
+def set_conv3x3_algorithm(name: str) -> None:
+    """Process-wide form of the 3x3 convs for decoders created and per-layer
+    calls made afterwards: "winograd" (default) or "implicit_gemm"."""
+    if name not in CONV3X3_ALGORITHMS:
+        raise ValueError(f"unknown conv3x3 algorithm {name!r}; expected one of {sorted(CONV3X3_ALGORITHMS)}")
+    check(_lib_().vae_set_conv3x3_algorithm(CONV3X3_ALGORITHMS[name]))
+
+
+def get_conv3x3_algorithm() -> str:
+    code = _lib_().vae_get_conv3x3_algorithm()
+    return {v: k for k, v in CONV3X3_ALGORITHMS.items()}[code]
 
 
 def _lib_():

@@ -112,6 +112,10 @@ const char *vae_last_error(void) { return g_err; }
 
 int32_t vae_abi_version(void) { return VAE_ABI_VERSION; }
 
+int32_t vae_set_conv3x3_algorithm(int32_t algorithm) { return set_conv3x3_algorithm(algorithm); }
+
+int32_t vae_get_conv3x3_algorithm(void) { return get_conv3x3_algorithm(); }
+
 int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, int32_t h, int32_t w, int32_t upsample2x,
                                    size_t *bytes) {
     int32_t rc = check_conv("vae_conv2d_workspace_bytes", conv, 0);

@@ -37,9 +37,13 @@
 // an LDS table.  It removes the separate normalisation pass but costs about
 // 10% of the conv on MI355X, more than that pass.
 //
-// The decoder's conv_out (3 output channels) runs on conv3x3_direct in
-// conv_direct.hip.
+// By default the 3x3 convs run in the Winograd form (conv_wino.hip); this
+// implicit GEMM serves conv_in, whose gather de-normalises the latent, and
+// every 3x3 conv when the implicit-GEMM form is selected
+// (vae_set_conv3x3_algorithm).  The decoder's conv_out (3 output channels)
+// runs on conv3x3_direct in conv_direct.hip.
 
+#include <atomic>
 #include <cstdio>
 
 #include "vae_internal.h"
@@ -588,7 +592,25 @@ int32_t pack_conv3x3(const float *w, int cout, int cin, int kt, float *dst, hipS
     return check_launch("pack_conv3x3");
 }
 
-int conv3x3_layout(int denorm, int upsample) { return denorm ? 0 : (upsample ? 2 : 1); }
+namespace {
+std::atomic<int32_t> g_conv3x3_algorithm{VAE_CONV3X3_WINOGRAD};
+}  // namespace
+
+int32_t set_conv3x3_algorithm(int32_t algorithm) {
+    if (algorithm != VAE_CONV3X3_WINOGRAD && algorithm != VAE_CONV3X3_IMPLICIT_GEMM) {
+        set_error("vae_set_conv3x3_algorithm: unknown algorithm %d", algorithm);
+        return VAE_ERR_INVALID_ARG;
+    }
+    g_conv3x3_algorithm.store(algorithm);
+    return VAE_OK;
+}
+
+int32_t get_conv3x3_algorithm() { return g_conv3x3_algorithm.load(); }
+
+int conv3x3_layout(int denorm, int upsample) {
+    if (denorm || g_conv3x3_algorithm.load() == VAE_CONV3X3_IMPLICIT_GEMM) return 0;
+    return upsample ? 2 : 1;
+}
 
 size_t conv3x3_pack_floats(int layout, int cout, int cin, int kt) {
     return layout == 0 ? conv3x3_packed_floats(cout, cin, kt) : conv3x3_wino_packed_floats(cout, cin, kt, layout == 2);

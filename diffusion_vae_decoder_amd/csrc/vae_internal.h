@@ -82,10 +82,14 @@ int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s);
 int conv3x3_wino_ksplit(const ConvLaunch &a);
 int conv3x3_wino_gn_records(const ConvLaunch &a);
 int conv3x3_wino_tcw(const ConvLaunch &a);   // tiles per row of its workgroup block
-// The ConvLaunch::wino layout a conv uses (the Winograd form unless its input
-// is de-normalised on load), its packed floats (`upsample`: input upsampled)
-// and the packing.  conv3x3_pack_floats_max bounds both layouts.
+// The ConvLaunch::wino layout a conv's weights are packed in now: the
+// Winograd form (`upsample`: for an upsampled input) unless its input is
+// de-normalised on load or the process-wide setting
+// (set_conv3x3_algorithm) asks for the implicit GEMM; then its packed floats
+// and the packing.  conv3x3_pack_floats_max bounds every layout.
 int conv3x3_layout(int denorm, int upsample);
+int32_t set_conv3x3_algorithm(int32_t algorithm);
+int32_t get_conv3x3_algorithm();
 size_t conv3x3_pack_floats(int layout, int cout, int cin, int kt);
 size_t conv3x3_pack_floats_max(int cout, int cin, int kt);
 int32_t pack_conv3x3_layout(int layout, const float *w, int cout, int cin, int kt, float *dst, hipStream_t s);

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 5
+#define VAE_ABI_VERSION 6
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -109,6 +109,25 @@ typedef struct vae_weights {
 const char *vae_last_error(void);
 int32_t vae_abi_version(void);
 
+/* The form of the 3x3 convolutions (every 3x3 conv but conv_in, which always
+ * runs as an implicit GEMM that de-normalises the latent while loading it):
+ *   VAE_CONV3X3_WINOGRAD       Winograd F(2x2, 3x3) on FP32 MFMA (default):
+ *                              16 of the direct conv's 36 multiplies per 2x2
+ *                              outputs and input channel (9 on a nearest-x2
+ *                              input); results within about 1e-6 of the
+ *                              output's magnitude of the exact conv;
+ *   VAE_CONV3X3_IMPLICIT_GEMM  the direct conv as an implicit GEMM (all 36;
+ *                              about 2e-7).
+ * Both stay within the decoder's per-layer bound of 1e-4 (normwise).  The
+ * setting is process-wide and read when weights are packed: by
+ * vae_decoder_create / vae_decoder3d_create (a decoder keeps the form it was
+ * created with) and by each per-layer call.  VAE_ERR_INVALID_ARG for other
+ * values. */
+#define VAE_CONV3X3_WINOGRAD 0
+#define VAE_CONV3X3_IMPLICIT_GEMM 1
+int32_t vae_set_conv3x3_algorithm(int32_t algorithm);
+int32_t vae_get_conv3x3_algorithm(void);
+
 /* ---------------------------------------------------------------- layers */
 
 /* Workspace (device bytes) needed by vae_conv2d / vae_conv_in for `conv` on an
@@ -128,7 +147,8 @@ int32_t vae_conv2d_workspace_bytes(const vae_conv *conv, int32_t h, int32_t w, i
  *   conv     kernel 1 or 3; conv->in_channels must equal cin
  *   ws       >= vae_conv2d_workspace_bytes(conv, h, w, upsample2x) device bytes (may be NULL if 0)
  * A convolution with out_channels <= 4 (the decoder's conv_out) runs on a
- * direct kernel; other 3x3 convolutions run as implicit GEMM on FP32 MFMA.
+ * direct kernel; other 3x3 convolutions run in the form set by
+ * vae_set_conv3x3_algorithm, on FP32 MFMA.
  * upsample2x requires kernel 3.  y may not alias x; it may alias residual. */
 int32_t vae_conv2d(const float *x, int32_t cin, int32_t h, int32_t w, const vae_conv *conv,
                    int32_t upsample2x, const float *residual, float *y,

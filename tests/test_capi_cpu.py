@@ -58,6 +58,26 @@ def packed_bytes(cout, cin, kt=1):
     return max(direct, wino)
 
 
+def test_conv3x3_algorithm_setting(lib):
+    assert lib.vae_get_conv3x3_algorithm() == 0            # Winograd by default
+    assert lib.vae_set_conv3x3_algorithm(2) == VAE_ERR_INVALID_ARG and "algorithm" in err(lib)
+    assert lib.vae_get_conv3x3_algorithm() == 0
+    try:
+        assert lib.vae_set_conv3x3_algorithm(1) == VAE_OK
+        assert lib.vae_get_conv3x3_algorithm() == 1
+        # the per-layer workspace covers either form, whichever is set
+        ws = c_size_t()
+        assert lib.vae_conv2d_workspace_bytes(byref(conv(64, 32, 3)), 8, 8, 0, byref(ws)) == VAE_OK
+        assert ws.value >= packed_bytes(64, 32)
+        # decoders pack for the form set when they are created
+        w, keep = fake_weights()
+        nb = c_size_t()
+        assert lib.vae_decoder_pack_bytes(byref(w), byref(nb)) == VAE_OK
+        assert 49_000_000 * 4 < nb.value < 52_000_000 * 4   # raw-sized implicit-GEMM packing
+    finally:
+        assert lib.vae_set_conv3x3_algorithm(0) == VAE_OK
+
+
 def test_conv2d_validation(lib):
     c = conv(64, 32, 3)
     ws = c_size_t()

@@ -34,6 +34,14 @@ def api():
     return a
 
 
+@pytest.fixture(params=["winograd", "implicit_gemm"])
+def algo(api, request):
+    """Runs the test with each form of the 3x3 convs, then restores the default."""
+    api.set_conv3x3_algorithm(request.param)
+    yield request.param
+    api.set_conv3x3_algorithm("winograd")
+
+
 def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
@@ -58,7 +66,7 @@ def conv_params(seed, name, cin, cout, k, dims=2):
 
 
 # ---------------------------------------------------------------------------
-# 3x3 convolution (implicit GEMM on MFMA)
+# 3x3 convolution (Winograd form and implicit GEMM, both on MFMA)
 # ---------------------------------------------------------------------------
 
 CONV_CASES = [
@@ -76,7 +84,7 @@ CONV_CASES = [
 
 
 @pytest.mark.parametrize("cin,cout,h,w", CONV_CASES)
-def test_conv3x3(api, cin, cout, h, w):
+def test_conv3x3(api, algo, cin, cout, h, w):
     x = vaegen.activation(1, f"x{cin}_{h}_{w}", (cin, h, w))
     wt, b = conv_params(1, f"c{cin}_{cout}", cin, cout, 3)
     y = api.conv2d(dev(x), dev(wt), dev(b), out=nan_like((cout, h, w)))
@@ -84,7 +92,7 @@ def test_conv3x3(api, cin, cout, h, w):
 
 
 @pytest.mark.parametrize("cin,cout,h,w", [(32, 64, 9, 13), (64, 128, 16, 16), (16, 32, 4, 4), (128, 128, 32, 32)])
-def test_conv3x3_upsample_folded(api, cin, cout, h, w):
+def test_conv3x3_upsample_folded(api, algo, cin, cout, h, w):
     x = vaegen.activation(2, "xu", (cin, h, w))
     wt, b = conv_params(2, "cu", cin, cout, 3)
     y = api.conv2d(dev(x), dev(wt), dev(b), upsample2x=True, out=nan_like((cout, 2 * h, 2 * w)))
@@ -93,7 +101,7 @@ def test_conv3x3_upsample_folded(api, cin, cout, h, w):
 
 
 @pytest.mark.parametrize("cin,cout,h,w", [(64, 64, 23, 17), (128, 128, 32, 32), (99, 96, 9, 11)])
-def test_conv3x3_residual_epilogue(api, cin, cout, h, w):
+def test_conv3x3_residual_epilogue(api, algo, cin, cout, h, w):
     x = vaegen.activation(3, "xr", (cin, h, w))
     r = vaegen.activation(3, "rr", (cout, h, w))
     wt, b = conv_params(3, "cr", cin, cout, 3)
@@ -199,7 +207,7 @@ CONV_GN_CASES = [
 
 
 @pytest.mark.parametrize("cin,cout,h,w,up,res,silu", CONV_GN_CASES)
-def test_conv_groupnorm_silu(api, cin, cout, h, w, up, res, silu):
+def test_conv_groupnorm_silu(api, algo, cin, cout, h, w, up, res, silu):
     H, W = (2 * h, 2 * w) if up else (h, w)
     x = vaegen.activation(21, "xcg", (cin, h, w))
     wt, b = conv_params(21, f"ccg{cin}_{cout}", cin, cout, 3)
@@ -272,7 +280,7 @@ def test_attention_peaked_softmax(api):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("cin,cout,t,h,w", [(16, 32, 5, 6, 10), (128, 128, 4, 16, 16), (24, 130, 3, 9, 35)])
-def test_conv3d_causal(api, cin, cout, t, h, w):
+def test_conv3d_causal(api, algo, cin, cout, t, h, w):
     x = vaegen.activation(11, "x3", (cin, t, h, w))
     wt, b = conv_params(11, "c3", cin, cout, 3, dims=3)
     y = api.conv3d_causal(dev(x), dev(wt), dev(b), out=nan_like((cout, t, h, w)))
@@ -399,6 +407,34 @@ def test_decode_causal3d(decoder3d, params3d, t, h, w):
     rgb = decoder3d.decode(dev(z), out=nan_like((3, t, 8 * h, 8 * w)))
     ref = oracle.decode_causal3d(z, params3d, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
     cos, mx = rgb_metrics(host(rgb), ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
+@pytest.mark.parametrize("dims,fused", [(2, False), (2, True), (3, False), (3, True)])
+def test_decode_implicit_gemm_form(api, params, params3d, dims, fused):
+    # a decoder created under the implicit-GEMM form keeps it (the setting is
+    # restored before decoding), with and without GroupNorm on load
+    api.set_conv3x3_algorithm("implicit_gemm")
+    try:
+        p = params if dims == 2 else params3d
+        d = api.Decoder({k: dev(v) for k, v in p.items()}, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR,
+                        causal3d=dims == 3)
+    finally:
+        api.set_conv3x3_algorithm("winograd")
+    try:
+        d.set_groupnorm_fusion(fused)
+        if dims == 2:
+            z = vaegen.latent(7, 5, 6)
+            rgb = d.decode(dev(z), out=nan_like((3, 40, 48)))
+            ref = oracle.decode(z, p, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+        else:
+            z = vaegen.latent3d(7, 2, 4, 5)
+            rgb = d.decode(dev(z), out=nan_like((3, 2, 32, 40)))
+            ref = oracle.decode_causal3d(z, p, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+        got = host(rgb)
+    finally:
+        d.close()
+    cos, mx = rgb_metrics(got, ref)
     assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
 
 
