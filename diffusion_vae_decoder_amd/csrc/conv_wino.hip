@@ -93,7 +93,7 @@ struct WParams {
     float *y;
     float *part;            // split-K partial sums [ksplit][cout][T][H][W]
     floatx4 *gn_rec;        // GroupNorm records of y, [32 groups][gn_nrec]
-    int cin, cout, H, W, Hin, Win, kt, nquads, tiles_x, ksplit, gn_cpg, gn_nrec;
+    int cin, cout, H, W, Hin, Win, kt, nquads, tiles_x, ncb, ksplit, gn_cpg, gn_nrec;
     long long in_cstride, in_fstride, out_cstride, out_fstride, part_stride;
 };
 
@@ -381,14 +381,18 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int lane = tid & 63, wave = tid >> 6;
     const int g4 = lane >> 4;   // the lane's channel of a step, and its 4-row group of an MFMA output
 
-    // XCD-aware renumbering, as in the implicit-GEMM conv: each XCD walks one
-    // contiguous band of tile blocks.
-    int tile = blockIdx.x;
-    if ((gridDim.x & 7) == 0) tile = (tile & 7) * (gridDim.x >> 3) + (tile >> 3);
+    // blockIdx.x enumerates (tile block, 32-channel output block) with the
+    // channel block fastest.  Workgroups are dealt to the 8 XCDs round-robin by
+    // linear id; when their count is a multiple of 8 they are renumbered so each
+    // XCD walks one contiguous band: all channel blocks of a tile then run
+    // together on one XCD and read the tile's input from HBM once.
+    int lin = blockIdx.x;
+    if ((gridDim.x & 7) == 0) lin = (lin & 7) * (gridDim.x >> 3) + (lin >> 3);
+    const int tile = lin / p.ncb;
+    const int cb = lin - tile * p.ncb;   // block of 32 output channels
     const int ty = tile / p.tiles_x;
     const int tx = tile - ty * p.tiles_x;
     const int y0 = ty * G::OR, x0 = tx * G::OC;
-    const int cb = blockIdx.y;   // block of 32 output channels
     const int frame = SPLIT ? blockIdx.z / p.ksplit : blockIdx.z;
     const int split = SPLIT ? blockIdx.z - frame * p.ksplit : 0;
 
@@ -623,7 +627,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     const float *d = qst + (w * 8 + tid * qpg + q) * 3;
                     wino_chan_merge(g, d[0], d[1], d[2]);
                 }
-            const long long rec = (long long)(cb * gpb + tid) * p.gn_nrec + (long long)frame * gridDim.x + tile;
+            const long long rec = (long long)(cb * gpb + tid) * p.gn_nrec + (long long)frame * (gridDim.x / p.ncb) + tile;
             p.gn_rec[rec] = floatx4{g[0], g[1], g[2], 0.f};
         }
     }
@@ -798,6 +802,7 @@ int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s) {
     p.out_cstride = p.out_fstride * a.T;
     const WinoGrid g = wino_grid(a.cout, a.H, a.W);
     p.tiles_x = g.tiles_x;
+    p.ncb = g.ncb;
     p.ksplit = conv3x3_wino_ksplit(a);
     p.part = a.part;
     p.part_stride = p.out_cstride * a.cout;
@@ -810,7 +815,12 @@ int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s) {
         set_error("conv3x3_wino: input channel of %lld elements is too large", p.in_cstride);
         return VAE_ERR_UNSUPPORTED;
     }
-    const dim3 grid((unsigned)(g.tiles_x * g.tiles_y), (unsigned)g.ncb, (unsigned)(a.T * p.ksplit));
+    const long long nwg = (long long)g.tiles_x * g.tiles_y * g.ncb;
+    if (nwg >= (1LL << 31)) {
+        set_error("conv3x3_wino: %lld workgroups exceed the grid limit", nwg);
+        return VAE_ERR_UNSUPPORTED;
+    }
+    const dim3 grid((unsigned)nwg, 1u, (unsigned)(a.T * p.ksplit));
     p.gn_rec = nullptr;
     p.gn_cpg = 0;
     p.gn_nrec = 0;
@@ -821,7 +831,7 @@ int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s) {
         }
         p.gn_rec = a.gn_rec;
         p.gn_cpg = a.cout / 32;
-        p.gn_nrec = (int)(grid.x * grid.z);
+        p.gn_nrec = g.tiles_x * g.tiles_y * (int)grid.z;
     }
     const bool up = a.upsample != 0, gn = a.gn_coef != nullptr, res = a.res != nullptr, split = p.ksplit > 1;
     switch (g.tcw) {
