@@ -222,7 +222,9 @@ __device__ __attribute__((always_inline)) inline void wino_stage_dma(const WPara
                                                                     floatx4 *lu,
                                                                     const int (&soffd)[(WGeom<TCW, UP>::NCH + 3) / 4]) {
     using G = WGeom<TCW, UP>;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is uniform: held in a scalar register, the chunk tests
+    // are scalar branches and the LDS destinations scalar sums
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
     for (int j = 0; j < kWStage; ++j) {
         const bool live = sb + j < s1;
