@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-3d", action="store_true", help="skip the causal 3-D stack and decode")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timings")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--conv3x3", default=None,
+                    help="form of the 3x3 convs (winograd_2x2, implicit_gemm, winograd_4x4); default: the library's")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the decodes, run one plain device copy of this many MiB "
                          "(reference dispatch for calibrating HBM byte counters)")
@@ -66,10 +68,13 @@ def parse():
 CSRC = os.path.join(ROOT, "diffusion_vae_decoder_amd", "csrc")
 
 
+CONV_SOURCES = {"conv3x3_wino4": "conv_wino4.hip", "conv3x3_wino": "conv_wino.hip", "conv3x3_mfma": "conv.hip"}
+
+
 def conv_family(kernel: str) -> str:
-    """'conv3x3_wino' or 'conv3x3_mfma' for the two 3x3 conv kernels, else ''."""
-    for f in ("conv3x3_wino", "conv3x3_mfma"):
-        if kernel.startswith(f):
+    """'conv3x3_wino4', 'conv3x3_wino' or 'conv3x3_mfma' for the 3x3 conv kernels, else ''."""
+    for f in CONV_SOURCES:
+        if kernel.startswith(f + "<"):
             return f
     return ""
 
@@ -80,9 +85,13 @@ def is_conv3x3(kernel: str) -> bool:
 
 def mfma_fraction(kernel: str) -> float:
     """MFMA multiplies the kernel executes per direct-conv multiply: the
-    Winograd F(2x2,3x3) form does 16 of 36 (9 of 36 on an upsampled input)."""
-    if conv_family(kernel) == "conv3x3_wino":
+    Winograd F(2x2,3x3) form does 16 of 36 (9 of 36 on an upsampled input),
+    F(4x4,3x3) 36 of 144 (25 of 144)."""
+    fam = conv_family(kernel)
+    if fam == "conv3x3_wino":
         return 9.0 / 36.0 if "up2x" in kernel else 16.0 / 36.0
+    if fam == "conv3x3_wino4":
+        return 25.0 / 144.0 if "up2x" in kernel else 36.0 / 144.0
     return 1.0
 
 
@@ -93,7 +102,7 @@ def counter_traffic(kernel: str, workload: str):
     fam = conv_family(kernel)
     if workload != "decode1024" or not fam:
         return None
-    src_file = "conv_wino.hip" if fam == "conv3x3_wino" else "conv.hip"
+    src_file = CONV_SOURCES[fam]
     try:
         text = open(os.path.join(ROOT, "profiles", f"{fam}_decode1024_hbm_counters.md")).read()
         src = open(os.path.join(CSRC, src_file), "rb").read()
@@ -315,6 +324,8 @@ def main():
 
     h = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.conv3x3:
+        api.set_conv3x3_algorithm(args.conv3x3)
     params = vaegen.decoder_params(args.seed)
     dec = api.Decoder({k: torch.from_numpy(v).cuda() for k, v in params.items()}, vaegen.SCALING_FACTOR,
                       vaegen.SHIFT_FACTOR)
@@ -389,7 +400,7 @@ def main():
         "data": "synthetic (seeded SplitMix64 latent N(0,1) and weights at the stated init; no trained weights)",
         "config": {"workload": f"FLUX-class AutoencoderKL decode, latent [16,{h},{h}] -> RGB [3,{ho},{wo}], "
                                "batch 1, f32 NCHW", "latent": [16, h, h], "rgb": [co, ho, wo],
-                   "flops_per_decode": flops_per_step},
+                   "flops_per_decode": flops_per_step, "conv3x3_form": api.get_conv3x3_algorithm()},
         "conv3x3": {"ms_per_step": conv_ms / args.steps, "tflops": conv_fl / (conv_ms / 1e3) / 1e12,
                     "frac_fp32_mfma_peak": conv_fl / (conv_ms / 1e3) / 1e12 / PEAK_FP32_MFMA_TFLOPS},
         "roofline": roof,

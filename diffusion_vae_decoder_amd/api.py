@@ -22,13 +22,14 @@ __all__ = [
     "conv3d_causal", "Decoder", "CONV3X3_ALGORITHMS", "set_conv3x3_algorithm", "get_conv3x3_algorithm",
 ]
 
-# Forms of the 3x3 convolutions (vae_set_conv3x3_algorithm).
-CONV3X3_ALGORITHMS = {"winograd": 0, "implicit_gemm": 1}
+# Forms of the 3x3 convolutions (vae_set_conv3x3_algorithm): Winograd
+# F(2x2, 3x3), the implicit GEMM of the direct conv, Winograd F(4x4, 3x3).
+CONV3X3_ALGORITHMS = {"winograd_2x2": 0, "implicit_gemm": 1, "winograd_4x4": 2}
 
 
 def set_conv3x3_algorithm(name: str) -> None:
     """Process-wide form of the 3x3 convs for decoders created and per-layer
-    calls made afterwards: "winograd" (default) or "implicit_gemm"."""
+    calls made afterwards: one of CONV3X3_ALGORITHMS."""
     if name not in CONV3X3_ALGORITHMS:
         raise ValueError(f"unknown conv3x3 algorithm {name!r}; expected one of {sorted(CONV3X3_ALGORITHMS)}")
     check(_lib_().vae_set_conv3x3_algorithm(CONV3X3_ALGORITHMS[name]))

@@ -90,7 +90,8 @@ size_t conv_partial_floats(const vae_conv *c, int kt, int T, int H, int W, int l
 
 size_t conv_ws(const vae_conv *c, int kt, int T, int H, int W) {
     if (c->kernel == 1) return gemm_partial_floats(c->out_channels, H * W, c->in_channels, false) * sizeof(float);
-    const size_t part = std::max(conv_partial_floats(c, kt, T, H, W, 0), conv_partial_floats(c, kt, T, H, W, 1));
+    const size_t part = std::max({conv_partial_floats(c, kt, T, H, W, 0), conv_partial_floats(c, kt, T, H, W, 1),
+                                  conv_partial_floats(c, kt, T, H, W, 3)});
     const size_t packed = align256(conv3x3_pack_floats_max(c->out_channels, c->in_channels, kt) * sizeof(float)) +
                           part * sizeof(float);
     if (kt == 1 && c->out_channels <= 4)   // direct kernel (or, with upsample / residual, the packed path)
@@ -227,8 +228,14 @@ namespace {
 size_t conv_gn_records_bytes(const vae_conv *c, int cin, int H, int W, int upsample) {
     ConvLaunch a{};
     a.cin = cin; a.cout = c->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
-    a.upsample = upsample; a.wino = conv3x3_layout(0, upsample);
-    return (size_t)32 * conv3x3_gn_records(a) * sizeof(floatx4);
+    a.upsample = upsample;
+    int n = 0;   // the most records any form writes, so the size holds whatever the setting
+    for (int layout : {0, upsample ? 2 : 1, 3}) {
+        if (layout == 3 && upsample) continue;   // F(4x4) runs on plain inputs only
+        a.wino = layout;
+        n = std::max(n, conv3x3_gn_records(a));
+    }
+    return (size_t)32 * n * sizeof(floatx4);
 }
 size_t conv_gn_ws(const vae_conv *c, int H, int W, int upsample) {
     return align256(conv_ws(c, 1, 1, H, W)) + align256(conv_gn_records_bytes(c, c->in_channels, H, W, upsample)) +

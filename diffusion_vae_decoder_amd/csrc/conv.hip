@@ -593,11 +593,12 @@ int32_t pack_conv3x3(const float *w, int cout, int cin, int kt, float *dst, hipS
 }
 
 namespace {
-std::atomic<int32_t> g_conv3x3_algorithm{VAE_CONV3X3_WINOGRAD};
+std::atomic<int32_t> g_conv3x3_algorithm{VAE_CONV3X3_WINOGRAD_4X4};
 }  // namespace
 
 int32_t set_conv3x3_algorithm(int32_t algorithm) {
-    if (algorithm != VAE_CONV3X3_WINOGRAD && algorithm != VAE_CONV3X3_IMPLICIT_GEMM) {
+    if (algorithm != VAE_CONV3X3_WINOGRAD_2X2 && algorithm != VAE_CONV3X3_IMPLICIT_GEMM &&
+        algorithm != VAE_CONV3X3_WINOGRAD_4X4) {
         set_error("vae_set_conv3x3_algorithm: unknown algorithm %d", algorithm);
         return VAE_ERR_INVALID_ARG;
     }
@@ -608,25 +609,35 @@ int32_t set_conv3x3_algorithm(int32_t algorithm) {
 int32_t get_conv3x3_algorithm() { return g_conv3x3_algorithm.load(); }
 
 int conv3x3_layout(int denorm, int upsample) {
-    if (denorm || g_conv3x3_algorithm.load() == VAE_CONV3X3_IMPLICIT_GEMM) return 0;
+    const int32_t alg = g_conv3x3_algorithm.load();
+    if (denorm || alg == VAE_CONV3X3_IMPLICIT_GEMM) return 0;
+    // an upsampled input keeps F(2x2, 3x3) under the F(4x4) setting: it runs
+    // faster there than the F(4x4) kernel's 25 products per 4 x 4 block
+    if (alg == VAE_CONV3X3_WINOGRAD_4X4) return upsample ? 2 : 3;
     return upsample ? 2 : 1;
 }
 
+bool conv3x3_layout_gn_on_load(int layout) { return layout <= 1; }
+
 size_t conv3x3_pack_floats(int layout, int cout, int cin, int kt) {
-    return layout == 0 ? conv3x3_packed_floats(cout, cin, kt) : conv3x3_wino_packed_floats(cout, cin, kt, layout == 2);
+    if (layout == 0) return conv3x3_packed_floats(cout, cin, kt);
+    if (layout <= 2) return conv3x3_wino_packed_floats(cout, cin, kt, layout == 2);
+    return conv3x3_wino4_packed_floats(cout, cin, kt);
 }
 
 size_t conv3x3_pack_floats_max(int cout, int cin, int kt) {
-    size_t n = conv3x3_packed_floats(cout, cin, kt);
-    for (int up = 0; up < 2; ++up) {
-        const size_t m = conv3x3_wino_packed_floats(cout, cin, kt, up);
+    size_t n = 0;
+    for (int layout = 0; layout <= 3; ++layout) {
+        const size_t m = conv3x3_pack_floats(layout, cout, cin, kt);
         if (m > n) n = m;
     }
     return n;
 }
 
 int32_t pack_conv3x3_layout(int layout, const float *w, int cout, int cin, int kt, float *dst, hipStream_t s) {
-    return layout == 0 ? pack_conv3x3(w, cout, cin, kt, dst, s) : pack_conv3x3_wino(w, cout, cin, kt, layout == 2, dst, s);
+    if (layout == 0) return pack_conv3x3(w, cout, cin, kt, dst, s);
+    if (layout <= 2) return pack_conv3x3_wino(w, cout, cin, kt, layout == 2, dst, s);
+    return pack_conv3x3_wino4(w, cout, cin, kt, dst, s);
 }
 
 namespace {
@@ -651,6 +662,7 @@ int mfma_ksplit(int cout, int cin, int kt, int H, int W, int T) {
 }  // namespace
 
 int conv3x3_ksplit(const ConvLaunch &a) {
+    if (a.wino >= 3) return conv3x3_wino4_ksplit(a);
     return a.wino ? conv3x3_wino_ksplit(a) : mfma_ksplit(a.cout, a.cin, a.kt, a.H, a.W, a.T);
 }
 
@@ -664,6 +676,7 @@ int conv3x3_gn_records(const ConvLaunch &a) {
     const long long plane = (long long)a.T * a.H * a.W;
     if (conv3x3_ksplit(a) > 1)
         return (int)((a.cout / 32) * ((plane + kRedElems - 1) / kRedElems));
+    if (a.wino >= 3) return conv3x3_wino4_gn_records(a);
     if (a.wino) return conv3x3_wino_gn_records(a);
     if (a.cout % kConvBM != 0 || (a.cout / 32) % 4 != 0) return 0;
     const int TC = conv_tc(a.W), TR = kConvBN / TC;
@@ -671,14 +684,14 @@ int conv3x3_gn_records(const ConvLaunch &a) {
 }
 
 const char *conv3x3_kernel_name(const ConvLaunch &a) {
-    static const char *algos[2] = {"mfma", "wino"};
+    static const char *algos[3] = {"mfma", "wino", "wino4"};
     static const char *tcs[4] = {"32", "16", "8", "4"};
     static const char *modes[4] = {"plain", "up2x", "denorm", "gnsilu"};
     static const char *tails[3] = {"", ",res", ",splitk"};
-    static char names[2][4][4][3][48];
+    static char names[3][4][4][3][48];
     static bool init = false;
     if (!init) {
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < 3; ++g)
             for (int t = 0; t < 4; ++t)
                 for (int m = 0; m < 4; ++m)
                     for (int k = 0; k < 3; ++k)
@@ -687,14 +700,15 @@ const char *conv3x3_kernel_name(const ConvLaunch &a) {
         init = true;
     }
     // column tile width: the implicit GEMM's output columns, the Winograd form's tiles per row
-    const int tc = a.wino ? conv3x3_wino_tcw(a) : conv_tc(a.W);
+    const int tc = a.wino >= 3 ? conv3x3_wino4_tcw(a) : (a.wino ? conv3x3_wino_tcw(a) : conv_tc(a.W));
     const int ti = tc == 32 ? 0 : (tc == 16 ? 1 : (tc == 8 ? 2 : 3));
     const int mi = a.upsample ? 1 : (a.denorm ? 2 : (a.gn_coef ? 3 : 0));
     const int si = conv3x3_ksplit(a) > 1 ? 2 : (a.res ? 1 : 0);
-    return names[a.wino ? 1 : 0][ti][mi][si];
+    return names[a.wino >= 3 ? 2 : (a.wino ? 1 : 0)][ti][mi][si];
 }
 
 int32_t launch_conv3x3_main(const ConvLaunch &a, hipStream_t s) {
+    if (a.wino >= 3) return launch_conv3x3_wino4_main(a, s);
     if (a.wino) return launch_conv3x3_wino_main(a, s);
     Params p;
     p.x = a.x;

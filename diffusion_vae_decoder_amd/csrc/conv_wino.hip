@@ -39,18 +39,18 @@
 
 #include <cstdio>
 
-#include "vae_internal.h"
+#include "wino_common.h"
 
 namespace vae {
 
 namespace {
 
+using namespace wino;
+
 constexpr int kWThreads = 256;
 constexpr int kWOut = 32;        // output channels per workgroup (two MFMA row blocks of 16)
 constexpr int kWTiles = 64;      // tiles per workgroup (16 per wave)
-constexpr int kWCh = 4;          // input channels per step (the MFMA's K)
 constexpr int kWStage = 2;       // steps per LDS stage
-constexpr int kWOOB = 0x7FFFFFF0;   // buffer offset past every range: reads 0
 
 template <bool UP>
 struct WinoShape {
@@ -85,44 +85,10 @@ struct WGeom {
     static_assert(PLANE > 0, "no LDS layout");
 };
 
-struct WParams {
-    const float *x;         // input [cin, T, Hin, Win]
-    const float *u;         // packed U
-    const float *bias, *res;
-    const float *gn_coef;   // GroupNorm + SiLU on load: (mean, scale, beta, -) per input channel
-    float *y;
-    float *part;            // split-K partial sums [ksplit][cout][T][H][W]
-    floatx4 *gn_rec;        // GroupNorm records of y, [32 groups][gn_nrec]
-    int cin, cout, H, W, Hin, Win, kt, nquads, tiles_x, ncb, ksplit, gn_cpg, gn_nrec;
-    long long in_cstride, in_fstride, out_cstride, out_fstride, part_stride;
-};
 
-__device__ __attribute__((always_inline)) inline __amdgpu_buffer_rsrc_t wino_rsrc(const float *base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, (int)bytes, 0x00020000);
-}
 
-__device__ __attribute__((always_inline)) inline const float *wino_frame(const WParams &p, int frame, int dt) {
-    int fr = frame + dt - (p.kt - 1);
-    fr = fr < 0 ? 0 : fr;
-    return p.x + (long long)fr * p.in_fstride;
-}
 
-// The next step to stage: time tap dt and channel quad, and the quad's first
-// channel in the tap's frame.  Advanced by additions only.
-struct WCursor {
-    int quad, dt;
-    const float *x;
-};
 
-__device__ __attribute__((always_inline)) inline void wino_next(const WParams &p, int frame, WCursor &c) {
-    if (++c.quad == p.nquads) {
-        c.quad = 0;
-        ++c.dt;
-        c.x = wino_frame(p, frame, c.dt);
-    } else {
-        c.x += kWCh * p.in_cstride;
-    }
-}
 
 // One step's staging in registers on its way to LDS: this thread's elements
 // of the step's four channel planes, its float4s of U and, for GroupNorm on
@@ -202,14 +168,6 @@ __device__ __attribute__((always_inline)) inline void wino_step_store(float *lx,
     }
 }
 
-// Direct global -> LDS load: lane i's 4 (16) bytes land at lds + i (float or
-// float4); an offset past the buffer's range writes 0.
-__device__ __attribute__((always_inline)) inline void wino_dma4(__amdgpu_buffer_rsrc_t r, float *lds, int voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voffset, 0, 0, 0);
-}
-__device__ __attribute__((always_inline)) inline void wino_dma16(__amdgpu_buffer_rsrc_t r, floatx4 *lds, int voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
-}
 
 // Issue the direct loads of one stage (kWStage steps from sb) into (lx, lu):
 // wave w takes chunks w, w + 4, ... of every channel plane and float4 rows
@@ -354,16 +312,6 @@ __device__ __attribute__((always_inline)) inline void wino_out(const floatx4 (&a
     }
 }
 
-// (n, mean, M2) of a set merged with (nb, mb, qb) of another (pairwise update
-// of Chan, Golub and LeVeque); empty sets (n = 0) merge as the identity.
-__device__ __attribute__((always_inline)) inline void wino_chan_merge(float (&a)[3], float nb, float mb, float qb) {
-    const float nt = a[0] + nb;
-    const float delta = mb - a[1];
-    const float fb = nt > 0.f ? nb / nt : 0.f;
-    a[2] = (a[2] + qb) + delta * delta * a[0] * fb;
-    a[1] = a[1] + delta * fb;
-    a[0] = nt;
-}
 
 template <int TCW, bool UP, bool GN, bool RES, bool SPLIT>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv3x3_wino(WParams p) {
@@ -432,10 +380,7 @@ __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const floatx4 *ublock = reinterpret_cast<const floatx4 *>(p.u) + (size_t)cb * nsteps * G::USTEP;
     auto ustep = [&](int s) { return ublock + (size_t)(s < s1 ? s : s1 - 1) * G::USTEP; };
 
-    WCursor cur;
-    cur.dt = s0 / p.nquads;
-    cur.quad = s0 - cur.dt * p.nquads;
-    cur.x = wino_frame(p, frame, cur.dt) + (long long)kWCh * cur.quad * p.in_cstride;
+    WCursor cur = wino_cursor(p, frame, s0);
 
     floatx4 acc[S::NX][2];
 #pragma unroll

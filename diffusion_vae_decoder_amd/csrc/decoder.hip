@@ -792,14 +792,22 @@ void vae_decoder_destroy(vae_decoder *d) {
 int32_t vae_decoder_set_groupnorm_fusion(vae_decoder *d, int32_t on) {
     if (!d) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_set_groupnorm_fusion: NULL decoder");
     if (on) {
-        // the conv's coefficient table holds 512 input channels
-        auto ok = [](const DConv &c) { return c.cin <= 512; };
-        bool all = ok(d->conv_out);
-        for (const DRes *r : {&d->mid0, &d->mid1}) all = all && ok(r->c1) && ok(r->c2);
+        // the conv's coefficient table holds 512 input channels, and its
+        // kernel must normalise while loading (not the F(4x4) Winograd form)
+        bool wide = false, form = false;
+        auto check = [&](const DConv &c) {
+            wide = wide || c.cin > 512;
+            form = form || !conv3x3_layout_gn_on_load(c.layout);
+        };
+        check(d->conv_out);
+        for (const DRes *r : {&d->mid0, &d->mid1}) check(r->c1), check(r->c2);
         for (const DUp &u : d->ups)
-            for (const DRes &r : u.res) all = all && ok(r.c1) && ok(r.c2);
-        if (!all)
-            return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_set_groupnorm_fusion: a conv has more than 512 inputs");
+            for (const DRes &r : u.res) check(r.c1), check(r.c2);
+        if (wide) return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_set_groupnorm_fusion: a conv has more than 512 inputs");
+        if (form)
+            return fail(VAE_ERR_UNSUPPORTED,
+                        "vae_decoder_set_groupnorm_fusion: the decoder's 3x3 convs use the F(4x4) Winograd form, "
+                        "which does not apply GroupNorm on load (create it with the F(2x2) form or the implicit GEMM)");
     }
     d->gn_fused = on != 0;
     return VAE_OK;

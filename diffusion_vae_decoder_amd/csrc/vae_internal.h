@@ -46,8 +46,9 @@ struct ConvLaunch {
     floatx4 *gn_rec;       // if set: GroupNorm(32) records of y for the normalisation that follows,
                            // [32][conv3x3_gn_records()] of (count, mean, M2, 0); M2 is the sum of
                            // squared deviations from the record's own mean
-    int wino;              // wpk layout: 0 pack_conv3x3 (implicit GEMM), 1 pack_conv3x3_wino,
-                           // 2 pack_conv3x3_wino for an upsampled input (Winograd conv)
+    int wino;              // wpk layout: 0 pack_conv3x3 (implicit GEMM); 1, 2 pack_conv3x3_wino
+                           // (Winograd F(2x2,3x3)) for a plain, an upsampled input; 3
+                           // pack_conv3x3_wino4 (Winograd F(4x4,3x3), a plain input only)
 };
 
 // Bytes of the packed weights for a conv with `cout` x `cin` x (kt x 3 x 3).
@@ -82,12 +83,25 @@ int32_t launch_conv3x3_wino_main(const ConvLaunch &a, hipStream_t s);
 int conv3x3_wino_ksplit(const ConvLaunch &a);
 int conv3x3_wino_gn_records(const ConvLaunch &a);
 int conv3x3_wino_tcw(const ConvLaunch &a);   // tiles per row of its workgroup block
-// The ConvLaunch::wino layout a conv's weights are packed in now: the
-// Winograd form (`upsample`: for an upsampled input) unless its input is
-// de-normalised on load or the process-wide setting
-// (set_conv3x3_algorithm) asks for the implicit GEMM; then its packed floats
-// and the packing.  conv3x3_pack_floats_max bounds every layout.
+
+// Winograd F(4x4, 3x3) form (conv_wino4.hip) for a plain input: weights
+// packed by pack_conv3x3_wino4; same split-K workspace, reduction and
+// GroupNorm records as the forms above; no upsampling, de-normalisation or
+// GroupNorm on load.
+size_t conv3x3_wino4_packed_floats(int cout, int cin, int kt);
+int32_t pack_conv3x3_wino4(const float *w, int cout, int cin, int kt, float *dst, hipStream_t s);
+int32_t launch_conv3x3_wino4_main(const ConvLaunch &a, hipStream_t s);
+int conv3x3_wino4_ksplit(const ConvLaunch &a);
+int conv3x3_wino4_gn_records(const ConvLaunch &a);
+int conv3x3_wino4_tcw(const ConvLaunch &a);
+// The ConvLaunch::wino layout a conv's weights are packed in now: the form
+// the process-wide setting (set_conv3x3_algorithm) selects, for a plain or
+// an upsampled input; the implicit GEMM for an input de-normalised on load.
+// Then its packed floats and the packing; conv3x3_pack_floats_max bounds
+// every layout.  conv3x3_layout_gn_on_load: whether a layout's kernel can
+// apply GroupNorm + SiLU while loading its input.
 int conv3x3_layout(int denorm, int upsample);
+bool conv3x3_layout_gn_on_load(int layout);
 int32_t set_conv3x3_algorithm(int32_t algorithm);
 int32_t get_conv3x3_algorithm();
 size_t conv3x3_pack_floats(int layout, int cout, int cin, int kt);

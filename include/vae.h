@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 6
+#define VAE_ABI_VERSION 7
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -111,20 +111,27 @@ int32_t vae_abi_version(void);
 
 /* The form of the 3x3 convolutions (every 3x3 conv but conv_in, which always
  * runs as an implicit GEMM that de-normalises the latent while loading it):
- *   VAE_CONV3X3_WINOGRAD       Winograd F(2x2, 3x3) on FP32 MFMA (default):
- *                              16 of the direct conv's 36 multiplies per 2x2
- *                              outputs and input channel (9 on a nearest-x2
- *                              input); results within about 1e-6 of the
- *                              output's magnitude of the exact conv;
+ *   VAE_CONV3X3_WINOGRAD_4X4   (default) Winograd F(4x4, 3x3) on FP32 MFMA for
+ *                              convs on a plain input: 36 of the direct conv's
+ *                              144 multiplies per 4x4 outputs and input
+ *                              channel, results within about 1e-5 of the
+ *                              output's magnitude of the exact conv; convs on
+ *                              a nearest-x2 input use F(2x2, 3x3);
+ *   VAE_CONV3X3_WINOGRAD_2X2   Winograd F(2x2, 3x3) on FP32 MFMA for every
+ *                              conv: 16 of 36 multiplies per 2x2 outputs and
+ *                              input channel (9 on a nearest-x2 input); about
+ *                              1e-6;
  *   VAE_CONV3X3_IMPLICIT_GEMM  the direct conv as an implicit GEMM (all 36;
  *                              about 2e-7).
- * Both stay within the decoder's per-layer bound of 1e-4 (normwise).  The
+ * All stay within the decoder's per-layer bound of 1e-4 (normwise).  The
  * setting is process-wide and read when weights are packed: by
  * vae_decoder_create / vae_decoder3d_create (a decoder keeps the form it was
- * created with) and by each per-layer call.  VAE_ERR_INVALID_ARG for other
- * values. */
-#define VAE_CONV3X3_WINOGRAD 0
+ * created with) and by each per-layer call.  GroupNorm applied on load
+ * (vae_decoder_set_groupnorm_fusion) needs a decoder created with the F(2x2)
+ * form or the implicit GEMM.  VAE_ERR_INVALID_ARG for other values. */
+#define VAE_CONV3X3_WINOGRAD_2X2 0
 #define VAE_CONV3X3_IMPLICIT_GEMM 1
+#define VAE_CONV3X3_WINOGRAD_4X4 2
 int32_t vae_set_conv3x3_algorithm(int32_t algorithm);
 int32_t vae_get_conv3x3_algorithm(void);
 
@@ -278,7 +285,8 @@ void vae_decoder_destroy(vae_decoder *d);
  * of a separate normalisation pass that writes the normalised tensor (the
  * default).  Same results up to rounding.  On MI355X the separate pass is
  * faster, so the default is off.  VAE_ERR_UNSUPPORTED if a normalised conv
- * has more than 512 input channels. */
+ * has more than 512 input channels, or if the decoder's 3x3 convs were
+ * packed in the F(4x4) Winograd form (VAE_CONV3X3_WINOGRAD_4X4). */
 int32_t vae_decoder_set_groupnorm_fusion(vae_decoder *d, int32_t on);
 
 /* on != 0: vae_decode / vae_decode3d capture their launch sequence into a HIP

@@ -49,20 +49,31 @@ def err(lib):
 
 def packed_bytes(cout, cin, kt=1):
     """Room the per-layer 3x3 entry points reserve for packed weights: the
-    larger of the implicit GEMM's layout (128-channel output blocks x chunks of
-    4 input channels x 36 x 128 floats) and the Winograd form's (32-channel
-    output blocks x chunks of 4 input channels x 64 lanes x 32 floats: 16
-    transform points per output and input channel)."""
+    largest of the implicit GEMM's layout (128-channel output blocks x chunks
+    of 4 input channels x 36 x 128 floats), the F(2x2) Winograd form's
+    (32-channel output blocks x chunks of 4 input channels x 64 lanes x 32
+    floats: 16 transform points per output and input channel) and the F(4x4)
+    form's (32-channel output blocks x chunks of 4 input channels x 2 row
+    blocks x 10 float4s x 64 lanes: 36 transform points, padded to 40, per
+    output and input channel)."""
     direct = ((cout + 127) // 128) * kt * ((cin + 3) // 4) * 36 * 128 * 4
     wino = ((cout + 31) // 32) * kt * ((cin + 3) // 4) * 64 * 32 * 4
-    return max(direct, wino)
+    wino4 = ((cout + 31) // 32) * kt * ((cin + 3) // 4) * 2 * 10 * 64 * 16
+    return max(direct, wino, wino4)
 
 
 def test_conv3x3_algorithm_setting(lib):
-    assert lib.vae_get_conv3x3_algorithm() == 0            # Winograd by default
-    assert lib.vae_set_conv3x3_algorithm(2) == VAE_ERR_INVALID_ARG and "algorithm" in err(lib)
-    assert lib.vae_get_conv3x3_algorithm() == 0
+    assert lib.vae_get_conv3x3_algorithm() == 2            # Winograd F(4x4) by default
+    assert lib.vae_set_conv3x3_algorithm(3) == VAE_ERR_INVALID_ARG and "algorithm" in err(lib)
+    assert lib.vae_set_conv3x3_algorithm(-1) == VAE_ERR_INVALID_ARG
+    assert lib.vae_get_conv3x3_algorithm() == 2
     try:
+        assert lib.vae_set_conv3x3_algorithm(0) == VAE_OK   # Winograd F(2x2)
+        assert lib.vae_get_conv3x3_algorithm() == 0
+        w, keep = fake_weights()
+        nb = c_size_t()
+        assert lib.vae_decoder_pack_bytes(byref(w), byref(nb)) == VAE_OK
+        assert 83_000_000 * 4 < nb.value < 84_000_000 * 4   # 16 transform points per weight (32 per 2 on x2 input)
         assert lib.vae_set_conv3x3_algorithm(1) == VAE_OK
         assert lib.vae_get_conv3x3_algorithm() == 1
         # the per-layer workspace covers either form, whichever is set
@@ -75,7 +86,7 @@ def test_conv3x3_algorithm_setting(lib):
         assert lib.vae_decoder_pack_bytes(byref(w), byref(nb)) == VAE_OK
         assert 49_000_000 * 4 < nb.value < 52_000_000 * 4   # raw-sized implicit-GEMM packing
     finally:
-        assert lib.vae_set_conv3x3_algorithm(0) == VAE_OK
+        assert lib.vae_set_conv3x3_algorithm(2) == VAE_OK
 
 
 def test_conv2d_validation(lib):
@@ -83,7 +94,7 @@ def test_conv2d_validation(lib):
     ws = c_size_t()
     assert lib.vae_conv2d_workspace_bytes(byref(c), 8, 8, 0, byref(ws)) == VAE_OK
     # the packed weights, then split-K partial sums (whole [64, 8, 8] slices)
-    assert ws.value >= packed_bytes(64, 32) == 8 * 36 * 128 * 4
+    assert ws.value >= packed_bytes(64, 32) == 2 * 8 * 2 * 10 * 64 * 16    # the F(4x4) packing is the largest
     assert (ws.value - packed_bytes(64, 32)) % (64 * 8 * 8 * 4) == 0
     # a small shape: the 32x32 conv with 512 channels is K-split, so partial sums are added
     big = conv(512, 512, 3)
@@ -137,9 +148,10 @@ def test_conv_groupnorm_validation(lib):
     c = conv(128, 16, 3)
     nb = c_size_t()
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(c), 37, 45, 0, byref(nb)) == VAE_OK
-    # packed weights, 32 groups x 16-byte records of the Winograd conv's 2 x 5 blocks of
-    # 8 x 32 outputs, GroupNorm partials
-    assert nb.value == packed_bytes(128, 16) + 10 * 32 * 16 + 32 * 16 + 32 * 8
+    # packed weights, 32 groups x 16-byte records for the form writing the most
+    # (the implicit GEMM's 2 x 10 blocks of 4 x 32 outputs; F(2x2): 2 x 5, F(4x4):
+    # 1 x 3), GroupNorm partials
+    assert nb.value == packed_bytes(128, 16) + 20 * 32 * 16 + 32 * 16 + 32 * 8
     c64 = conv(64, 16, 3)                        # 2 channels per group: no records, a statistics pass
     n64 = c_size_t()
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(c64), 37, 45, 0, byref(n64)) == VAE_OK
@@ -223,10 +235,12 @@ def test_decoder_pack_and_validation(lib):
     w, keep = fake_weights()
     nb = c_size_t()
     assert lib.vae_decoder_pack_bytes(byref(w), byref(nb)) == VAE_OK, err(lib)
-    # about 50M parameters, of which 48.3M in 3x3 convs; their Winograd packing
-    # holds 16 floats per (output, input channel) pair instead of 9 (10 for the
-    # three upsample convs, 5.3M parameters): about 83.5M floats in all
-    assert 83_000_000 * 4 < nb.value < 84_000_000 * 4
+    # about 50M parameters, of which 48.3M in 3x3 convs; the F(4x4) Winograd
+    # packing of the convs on a plain input (43M parameters) holds 40 floats
+    # per (output, input channel) pair instead of 9 (36 transform points, padded
+    # to whole float4s per half), the F(2x2) packing of the three upsample
+    # convs (5.3M parameters) 10: about 198M floats in all
+    assert 197_000_000 * 4 < nb.value < 199_000_000 * 4
     h = c_void_p()
     assert lib.vae_decoder_create(byref(h), byref(w), FAKE, nb.value - 1, NULL) == VAE_ERR_WORKSPACE
     assert lib.vae_decoder_create(byref(h), byref(w), FAKE + 4, nb.value, NULL) == VAE_ERR_INVALID_ARG

@@ -34,12 +34,27 @@ def api():
     return a
 
 
-@pytest.fixture(params=["winograd", "implicit_gemm"])
+FORMS = ["winograd_2x2", "implicit_gemm", "winograd_4x4"]
+
+
+@pytest.fixture(params=FORMS)
 def algo(api, request):
-    """Runs the test with each form of the 3x3 convs, then restores the default."""
+    """Runs the test with each form of the 3x3 convs, then restores the setting."""
+    before = api.get_conv3x3_algorithm()
     api.set_conv3x3_algorithm(request.param)
     yield request.param
-    api.set_conv3x3_algorithm("winograd")
+    api.set_conv3x3_algorithm(before)
+
+
+def make_decoder(api, p, form, dims=2):
+    """A decoder packed under `form` (the process-wide setting is restored)."""
+    before = api.get_conv3x3_algorithm()
+    api.set_conv3x3_algorithm(form)
+    try:
+        return api.Decoder({k: dev(v) for k, v in p.items()}, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR,
+                           causal3d=dims == 3)
+    finally:
+        api.set_conv3x3_algorithm(before)
 
 
 def dev(a):
@@ -361,16 +376,24 @@ def test_decode_full_size_against_stored_oracle(decoder, name, h):
     assert abs(math.sqrt((rgb * rgb).sum()) / float(g["l2"]) - 1.0) < 1e-4
 
 
+@pytest.fixture(scope="module")
+def decoder_2x2(api, params):
+    """GroupNorm on load needs a form whose kernels normalise while loading."""
+    d = make_decoder(api, params, "winograd_2x2")
+    yield d
+    d.close()
+
+
 @pytest.mark.parametrize("h,w", [(8, 8), (5, 3), (32, 32)])
-def test_decode_with_groupnorm_on_load(decoder, params, h, w):
+def test_decode_with_groupnorm_on_load(decoder_2x2, params, h, w):
     # the optional fused path: GroupNorm + SiLU applied while each conv loads
     z = vaegen.latent(6, h, w)
-    decoder.set_groupnorm_fusion(True)
+    decoder_2x2.set_groupnorm_fusion(True)
     try:
-        rgb = decoder.decode(dev(z), out=nan_like((3, 8 * h, 8 * w)))
+        rgb = decoder_2x2.decode(dev(z), out=nan_like((3, 8 * h, 8 * w)))
         got = host(rgb)
     finally:
-        decoder.set_groupnorm_fusion(False)
+        decoder_2x2.set_groupnorm_fusion(False)
     ref = oracle.decode(z, params, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
     cos, mx = rgb_metrics(got, ref)
     assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
@@ -410,17 +433,13 @@ def test_decode_causal3d(decoder3d, params3d, t, h, w):
     assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
 
 
-@pytest.mark.parametrize("dims,fused", [(2, False), (2, True), (3, False), (3, True)])
-def test_decode_implicit_gemm_form(api, params, params3d, dims, fused):
-    # a decoder created under the implicit-GEMM form keeps it (the setting is
-    # restored before decoding), with and without GroupNorm on load
-    api.set_conv3x3_algorithm("implicit_gemm")
-    try:
-        p = params if dims == 2 else params3d
-        d = api.Decoder({k: dev(v) for k, v in p.items()}, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR,
-                        causal3d=dims == 3)
-    finally:
-        api.set_conv3x3_algorithm("winograd")
+@pytest.mark.parametrize("form,dims,fused", [(f, d, g) for f in FORMS for d in (2, 3) for g in (False, True)
+                                             if not (g and f == "winograd_4x4")])
+def test_decode_form(api, params, params3d, form, dims, fused):
+    # a decoder keeps the form it was created under (the setting is restored
+    # before decoding), with and without GroupNorm on load
+    p = params if dims == 2 else params3d
+    d = make_decoder(api, p, form, dims)
     try:
         d.set_groupnorm_fusion(fused)
         if dims == 2:
@@ -438,13 +457,35 @@ def test_decode_implicit_gemm_form(api, params, params3d, dims, fused):
     assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
 
 
-def test_decode_causal3d_with_groupnorm_on_load(decoder3d, params3d):
-    z = vaegen.latent3d(3, 2, 4, 4)
-    decoder3d.set_groupnorm_fusion(True)
+def test_groupnorm_on_load_needs_a_loading_form(api, params):
+    # the F(4x4) Winograd kernel does not normalise on load: the switch is refused
+    d = make_decoder(api, params, "winograd_4x4")
     try:
-        got = host(decoder3d.decode(dev(z), out=nan_like((3, 2, 32, 32))))
+        with pytest.raises(api.VaeError, match="F\\(4x4\\)"):
+            d.set_groupnorm_fusion(True)
+        z = vaegen.latent(8, 4, 4)           # and the decoder still works
+        got = host(d.decode(dev(z), out=nan_like((3, 32, 32))))
     finally:
-        decoder3d.set_groupnorm_fusion(False)
+        d.close()
+    ref = oracle.decode(z, params, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    cos, mx = rgb_metrics(got, ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
+@pytest.fixture(scope="module")
+def decoder3d_2x2(api, params3d):
+    d = make_decoder(api, params3d, "winograd_2x2", dims=3)
+    yield d
+    d.close()
+
+
+def test_decode_causal3d_with_groupnorm_on_load(decoder3d_2x2, params3d):
+    z = vaegen.latent3d(3, 2, 4, 4)
+    decoder3d_2x2.set_groupnorm_fusion(True)
+    try:
+        got = host(decoder3d_2x2.decode(dev(z), out=nan_like((3, 2, 32, 32))))
+    finally:
+        decoder3d_2x2.set_groupnorm_fusion(False)
     ref = oracle.decode_causal3d(z, params3d, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
     cos, mx = rgb_metrics(got, ref)
     assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
