@@ -230,8 +230,7 @@ size_t conv_gn_records_bytes(const vae_conv *c, int cin, int H, int W, int upsam
     a.cin = cin; a.cout = c->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
     a.upsample = upsample;
     int n = 0;   // the most records any form writes, so the size holds whatever the setting
-    for (int layout : {0, upsample ? 2 : 1, 3}) {
-        if (layout == 3 && upsample) continue;   // F(4x4) runs on plain inputs only
+    for (int layout : {0, upsample ? 2 : 1, upsample ? 4 : 3}) {
         a.wino = layout;
         n = std::max(n, conv3x3_gn_records(a));
     }

@@ -611,9 +611,7 @@ int32_t get_conv3x3_algorithm() { return g_conv3x3_algorithm.load(); }
 int conv3x3_layout(int denorm, int upsample) {
     const int32_t alg = g_conv3x3_algorithm.load();
     if (denorm || alg == VAE_CONV3X3_IMPLICIT_GEMM) return 0;
-    // an upsampled input keeps F(2x2, 3x3) under the F(4x4) setting: it runs
-    // faster there than the F(4x4) kernel's 25 products per 4 x 4 block
-    if (alg == VAE_CONV3X3_WINOGRAD_4X4) return upsample ? 2 : 3;
+    if (alg == VAE_CONV3X3_WINOGRAD_4X4) return upsample ? 4 : 3;
     return upsample ? 2 : 1;
 }
 
@@ -622,12 +620,12 @@ bool conv3x3_layout_gn_on_load(int layout) { return layout <= 1; }
 size_t conv3x3_pack_floats(int layout, int cout, int cin, int kt) {
     if (layout == 0) return conv3x3_packed_floats(cout, cin, kt);
     if (layout <= 2) return conv3x3_wino_packed_floats(cout, cin, kt, layout == 2);
-    return conv3x3_wino4_packed_floats(cout, cin, kt);
+    return conv3x3_wino4_packed_floats(cout, cin, kt, layout == 4);
 }
 
 size_t conv3x3_pack_floats_max(int cout, int cin, int kt) {
     size_t n = 0;
-    for (int layout = 0; layout <= 3; ++layout) {
+    for (int layout = 0; layout <= 4; ++layout) {
         const size_t m = conv3x3_pack_floats(layout, cout, cin, kt);
         if (m > n) n = m;
     }
@@ -637,7 +635,7 @@ size_t conv3x3_pack_floats_max(int cout, int cin, int kt) {
 int32_t pack_conv3x3_layout(int layout, const float *w, int cout, int cin, int kt, float *dst, hipStream_t s) {
     if (layout == 0) return pack_conv3x3(w, cout, cin, kt, dst, s);
     if (layout <= 2) return pack_conv3x3_wino(w, cout, cin, kt, layout == 2, dst, s);
-    return pack_conv3x3_wino4(w, cout, cin, kt, dst, s);
+    return pack_conv3x3_wino4(w, cout, cin, kt, layout == 4, dst, s);
 }
 
 namespace {

@@ -1,5 +1,4 @@
-// Winograd F(4x4, 3x3) form of the decoder's 3x3 convolutions on a plain
-// (not upsampled) input, on FP32 MFMA.
+// Winograd F(4x4, 3x3) form of the decoder's 3x3 convolutions on FP32 MFMA.
 //
 // The conv (cortiq-engine 0.7.7 `vae`, VaeConvRef: stride 1, zero padding
 // 1, cross-correlation) computes each 4 x 4 block of outputs from the 6 x 6
@@ -20,15 +19,25 @@
 // decoder's shapes (the larger transform coefficients cost about one decimal
 // digit against F(2x2, 3x3)).
 //
+// Nearest-x2 upsampled input (VaeUpRef): the 6 x 6 patch of a 4 x 4 output
+// block at multiples of 4 reads upsampled rows 4i-1 .. 4i+4, i.e. source rows
+// 2i-1, 2i, 2i, 2i+1, 2i+1, 2i+2.  On that repetition B^T collapses to four
+// rows over the 4 source rows s: (4 -5 1 0), (0 -8 2 0), (0 1 -1 0) and
+// (0 4 -5 1); point 2 vanishes and point 3 is -3 times point 4.  The 4 x 4
+// source patch transforms to 16 values, and the 25 products of points
+// {0, 1, 3, 4, 5}^2 use them with the factors -3 folded into U (exact in
+// double precision before rounding): 25 multiplies per 4 x 4 outputs and
+// channel instead of 144 (F(2x2, 3x3): 36).
+//
 // On MI355X a SIMD does not overlap FP32 vector instructions with FP32 MFMA
 // execution, so the input transform's VALU work adds to the MFMA time; the
 // layout below spends as little of it per MFMA as the registers allow.
 // Workgroup: 4 waves, 32 output channels (two MFMA row blocks) and 32 tiles
 // (4 x 4 output blocks) in two groups of 16.  The two waves of a tile group
 // split the transform's points: wave half h takes columns 3h .. 3h + 2 of
-// B^T d B (18 points) for both row blocks, so each transformed value feeds
-// two MFMAs and the first transform pass computes only the half's three
-// outputs per patch row.  A step is four input channels: every lane
+// B^T d B (18 points; on an upsampled input 13 and 12 of the 25 products)
+// for both row blocks, so each transformed value feeds two MFMAs and the
+// first transform pass computes only the outputs the half uses.  A step is four input channels: every lane
 // transforms one (channel, tile) patch (lane l: tile l % 16, channel l / 16),
 // which is the B operand of v_mfma_f32_16x16x4_f32; the A operand is U of the
 // point.  Accumulators: 2 row blocks x 18 points x 4 = 144 registers, so two
@@ -52,9 +61,16 @@ constexpr int kW4RB = 2;                 // row blocks of a wave and of a workgr
 constexpr int kW4TG = 2;                 // tile groups (of 16 tiles) of a workgroup
 constexpr int kW4Waves = 2 * kW4TG;      // a wave pair (point halves) per tile group
 constexpr int kW4Threads = 64 * kW4Waves;
-constexpr int kW4NX = 18;                // products of a half: 3 transform columns x 6 rows
-constexpr int kW4NQ = 5;                 // float4s of U per (row block, half) and step
-constexpr int kW4UQ = 2 * kW4NQ;         // float4 rows of U per row block and step
+
+// Products of a point half, and float4 rows of U per row block and step (a
+// plain input: 18 per half in 5 float4s each; an upsampled one: 13 and 12 in
+// 4 and 3 float4s).
+template <bool UP>
+struct W4Shape {
+    static constexpr int NX = UP ? 13 : 18;      // accumulators per row block (the larger half)
+    static constexpr int Q1 = UP ? 4 : 5;        // first float4 row of half 1
+    static constexpr int UQ = UP ? 7 : 10;       // float4 rows per row block
+};
 constexpr int kW4Slots = 512;            // resident workgroups: two per CU
 
 // Staged columns: column x of a row sits at position w4_pos(x).  Layout 1
@@ -68,14 +84,16 @@ constexpr int w4_col(int q, int lay, int hc) {
 }
 
 // LDS bank check of the patch reads: pair h (columns 2h, 2h + 1 of a patch
-// row) of every lane, `nl` lanes served together from `nb` four-byte banks.
-constexpr bool w4_reads_ok(int tcw, int hcp, int lay, int plane, int nb, int nl) {
-    for (int h = 0; h < 3; ++h)
+// row) of every lane, `nl` lanes served together from `nb` four-byte banks
+// (a patch starts every 4 staged columns, every 2 on an upsampled input).
+constexpr bool w4_reads_ok(int tcw, bool up, int hcp, int lay, int plane, int nb, int nl) {
+    const int stride = up ? 2 : 4;
+    for (int h = 0; h < (up ? 2 : 3); ++h)
         for (int g0 = 0; g0 < 64; g0 += nl) {
             bool used[64] = {};
             for (int l = g0; l < g0 + nl; ++l) {
                 const int ch = l / 16, t = l % 16;
-                const int addr = ch * plane + 4 * (t / tcw) * hcp + w4_pos(4 * (t % tcw) + 2 * h, lay);
+                const int addr = ch * plane + stride * (t / tcw) * hcp + w4_pos(stride * (t % tcw) + 2 * h, lay);
                 for (int k = 0; k < 2; ++k) {
                     const int b = (addr + k) % nb;
                     if (used[b]) return false;
@@ -95,7 +113,7 @@ struct W4Layout {
 // are free of bank conflicts both with 32 banks serving 16 lanes and with 64
 // banks serving 32; failing that (fewer than 16 tiles per row, whose tile
 // rows a 4-row stride cannot separate in 32 banks), free of them with 64.
-constexpr W4Layout w4_layout(int tcw, int hr, int hc) {
+constexpr W4Layout w4_layout(int tcw, bool up, int hr, int hc) {
     for (int strict = 1; strict >= 0; --strict)
         for (int lay = 0; lay < (hc <= 66 ? 2 : 1); ++lay) {
             int width = 0;
@@ -103,26 +121,28 @@ constexpr W4Layout w4_layout(int tcw, int hr, int hc) {
             for (int hcp = width + (width & 1); hcp < width + 64; hcp += 2) {
                 const int base = (hr * hcp + 63) / 64 * 64;
                 for (int plane = base; plane < base + 64; plane += 2)
-                    if ((!strict || w4_reads_ok(tcw, hcp, lay, plane, 32, 16)) && w4_reads_ok(tcw, hcp, lay, plane, 64, 32))
+                    if ((!strict || w4_reads_ok(tcw, up, hcp, lay, plane, 32, 16)) &&
+                        w4_reads_ok(tcw, up, hcp, lay, plane, 64, 32))
                         return W4Layout{lay, hcp, plane};
             }
         }
     return W4Layout{-1, -1, -1};
 }
 
-template <int TCW>
+template <int TCW, bool UP>
 struct W4Geom {
     static constexpr int TILES = 16 * kW4TG;            // tiles of the block
     static constexpr int TRW = TILES / TCW;             // tile rows of the block
     static constexpr int OR = 4 * TRW, OC = 4 * TCW;    // output rows, columns of the block
-    static constexpr int HR = OR + 2, HC = OC + 2;      // staged rows, columns
-    static constexpr W4Layout L = w4_layout(TCW, HR, HC);
+    static constexpr int HR = UP ? 2 * TRW + 2 : OR + 2;   // staged rows (source rows when upsampled)
+    static constexpr int HC = UP ? 2 * TCW + 2 : OC + 2;   // staged columns
+    static constexpr W4Layout L = w4_layout(TCW, UP, HR, HC);
     static constexpr int LAY = L.lay;                   // column layout (w4_pos)
     static constexpr int HCP = L.hcp;                   // row stride
     static constexpr int PLANE = L.plane;               // channel-plane stride
     static constexpr int NCH = (HR * HCP + 63) / 64;    // 64-element chunks of a staged plane
     static constexpr int XSTEP = kWCh * PLANE;          // floats of input per step
-    static constexpr int UROWS = kW4RB * kW4UQ;         // 64-lane float4 rows of U per step
+    static constexpr int UROWS = kW4RB * W4Shape<UP>::UQ;   // 64-lane float4 rows of U per step
     static constexpr int USTEP = UROWS * 64;            // float4s of U per step
     // wave w loads chunks w, w + 4, ... of every channel plane and U rows
     // w, w + 4, ...
@@ -144,6 +164,15 @@ __device__ __attribute__((always_inline)) inline void w4_bt(float d0, float d1, 
     v[3] = fmaf(2.f, d31, d42);
     v[4] = fmaf(-2.f, d31, d42);
     v[5] = fmaf(4.f, d1, fmaf(-5.f, d3, d5));
+}
+
+// One axis of B^T on the repeated source line s0 s1 s1 s2 s2 s3: points 0, 1,
+// 4 and 5 (point 3 is -3 times point 4, point 2 is zero).
+__device__ __attribute__((always_inline)) inline void w4_btu(float s0, float s1, float s2, float s3, float (&w)[4]) {
+    w[0] = fmaf(4.f, s0, fmaf(-5.f, s1, s2));
+    w[1] = fmaf(-8.f, s1, 2.f * s2);
+    w[2] = s1 - s2;
+    w[3] = fmaf(4.f, s1, fmaf(-5.f, s2, s3));
 }
 
 // Points 3H .. 3H + 2 of B^T on a 6-point line.
@@ -176,11 +205,11 @@ __device__ __attribute__((always_inline)) inline void w4_at(float m0, float m1, 
 // those add exactly 0.  `soffd` holds the lane's byte offsets of the wave's
 // input chunks; `ublk` is the workgroup's packed U (a step's rows are
 // contiguous).
-template <int TCW>
+template <int TCW, bool UP>
 __device__ __attribute__((always_inline)) inline void w4_stage(const WParams &p, int frame, int sb, int s1,
                                                               const float *ublk, WCursor &cur, float *lx, floatx4 *lu,
-                                                              const int (&soffd)[W4Geom<TCW>::CPW]) {
-    using G = W4Geom<TCW>;
+                                                              const int (&soffd)[W4Geom<TCW, UP>::CPW]) {
+    using G = W4Geom<TCW, UP>;
     // the wave index is uniform: in a scalar register the load tests are
     // scalar branches and the LDS destinations scalar sums
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -208,16 +237,17 @@ __device__ __attribute__((always_inline)) inline void w4_stage(const WParams &p,
     }
 }
 
-// One step from LDS for point half H: the lane's patch of its channel, the
-// half's transform and its 2 x 18 MFMAs.  The patch rows pass through B^T
-// for the half's three columns as they are read, then each column is
-// finished and multiplied at once.  Product k = 6 c + r of the half is point
-// (r, 3H + c); its A operand for row block b is component k % 4 of float4
-// b * 10 + 5 H + k / 4.
+// One step from LDS for point half H of a plain input: the lane's patch of
+// its channel, the half's transform and its 2 x 18 MFMAs.  The patch rows
+// pass through B^T for the half's three columns as they are read, then each
+// column is finished and multiplied at once.  Product k = 6 c + r of the half
+// is point (r, 3H + c); its A operand for row block b is component k % 4 of
+// float4 b * 10 + 5 H + k / 4.
 template <int TCW, int H>
 __device__ __attribute__((always_inline)) inline void w4_step(const float *lx, const floatx4 *lu, const int (&pb)[3],
-                                                             int lane, floatx4 (&acc)[kW4RB][kW4NX]) {
-    using G = W4Geom<TCW>;
+                                                             int lane, floatx4 (&acc)[kW4RB][W4Shape<false>::NX]) {
+    using G = W4Geom<TCW, false>;
+    using S = W4Shape<false>;
     float t[6][3];   // d B, the half's columns
 #pragma unroll
     for (int r = 0; r < 6; ++r) {
@@ -230,8 +260,8 @@ __device__ __attribute__((always_inline)) inline void w4_step(const float *lx, c
         }
         w4_bt_half<H>(d, t[r][0], t[r][1], t[r][2]);
     }
-    const floatx4 *ul = lu + H * kW4NQ * 64 + lane;
-    floatx4 u[kW4RB][kW4NQ];
+    const floatx4 *ul = lu + H * S::Q1 * 64 + lane;
+    floatx4 u[kW4RB][S::Q1];
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
         float v[6];
@@ -241,17 +271,72 @@ __device__ __attribute__((always_inline)) inline void w4_step(const float *lx, c
             const int k = 6 * c + r;
 #pragma unroll
             for (int b = 0; b < kW4RB; ++b) {
-                if (k % 4 == 0) u[b][k / 4] = ul[(b * kW4UQ + k / 4) * 64];
+                if (k % 4 == 0) u[b][k / 4] = ul[(b * S::UQ + k / 4) * 64];
                 acc[b][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(u[b][k / 4][k % 4], v[r], acc[b][k], 0, 0, 0);
             }
         }
     }
 }
 
+// The 25 products of an upsampled input, over rows a and columns c indexing
+// the points P = {0, 1, 3, 4, 5}: half 0 takes columns 0 and 1 and rows 0..2
+// of column 2 (13 products), half 1 rows 3 and 4 of column 2 and columns 3 and
+// 4 (12).  Product k of half H is (w4u_row(H, k), w4u_col(H, k)); a point
+// index reads value w4u_src(a) of a source line's transform.
+constexpr int w4u_col(int h, int k) { return h == 0 ? (k < 10 ? k / 5 : 2) : (k < 2 ? 2 : 3 + (k - 2) / 5); }
+constexpr int w4u_row(int h, int k) { return h == 0 ? (k < 10 ? k % 5 : k - 10) : (k < 2 ? 3 + k : (k - 2) % 5); }
+constexpr int w4u_count(int h) { return h == 0 ? 13 : 12; }
+constexpr int w4u_src(int a) { return a <= 1 ? a : (a <= 3 ? 2 : 3); }
+
+// One step from LDS for point half H of an upsampled input: the lane's 4 x 4
+// source patch, the half's share of its transform (first pass: the half's
+// distinct columns of each source row; then each distinct column, whose four
+// values serve every product of it) and its 2 x 13 (12) MFMAs.  The A operand
+// of product k for row block b is component k % 4 of float4 b * 7 + 4 H + k / 4.
+template <int TCW, int H>
+__device__ __attribute__((always_inline)) inline void w4_step_up(const float *lx, const floatx4 *lu, const int (&pb)[2],
+                                                                int lane, floatx4 (&acc)[kW4RB][W4Shape<true>::NX]) {
+    using G = W4Geom<TCW, true>;
+    using S = W4Shape<true>;
+    constexpr int C0 = H == 0 ? 0 : 2, NC = H == 0 ? 3 : 2;   // the half's distinct columns C0 .. C0 + NC - 1
+    float t[4][NC];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const floatx2 a = *reinterpret_cast<const floatx2 *>(lx + pb[0] + r * G::HCP);
+        const floatx2 b = *reinterpret_cast<const floatx2 *>(lx + pb[1] + r * G::HCP);
+        if (H == 0) {
+            t[r][0] = fmaf(4.f, a[0], fmaf(-5.f, a[1], b[0]));
+            t[r][1] = fmaf(-8.f, a[1], 2.f * b[0]);
+            t[r][2] = a[1] - b[0];
+        } else {
+            t[r][0] = a[1] - b[0];
+            t[r][1] = fmaf(4.f, a[1], fmaf(-5.f, b[0], b[1]));
+        }
+    }
+    const floatx4 *ul = lu + H * S::Q1 * 64 + lane;
+    floatx4 u[kW4RB][4];
+#pragma unroll
+    for (int dc = 0; dc < NC; ++dc) {
+        float w[4];
+        w4_btu(t[0][dc], t[1][dc], t[2][dc], t[3][dc], w);
+#pragma unroll
+        for (int k = 0; k < w4u_count(H); ++k) {
+            if (w4u_src(w4u_col(H, k)) != C0 + dc) continue;
+#pragma unroll
+            for (int b = 0; b < kW4RB; ++b) {
+                if (k % 4 == 0) u[b][k / 4] = ul[(b * S::UQ + k / 4) * 64];   // products come in increasing k
+                acc[b][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(u[b][k / 4][k % 4], w[w4u_src(w4u_row(H, k))], acc[b][k],
+                                                                0, 0, 0);
+            }
+        }
+    }
+}
+
 // The half's share of the output transform of register i of a row block:
-// y[a][x] = sum over the half's columns c of (A^T M)[a][c] A^T[x][c].
+// y[a][x] = sum over the half's products (r, c) of A^T[a][r] M[r][c] A^T[x][c].
 template <int H>
-__device__ __attribute__((always_inline)) inline void w4_out_half(const floatx4 (&acc)[kW4NX], int i, float (&y)[4][4]) {
+__device__ __attribute__((always_inline)) inline void w4_out_half(const floatx4 (&acc)[W4Shape<false>::NX], int i,
+                                                                 float (&y)[4][4]) {
     float s[4][3];
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
@@ -279,13 +364,47 @@ __device__ __attribute__((always_inline)) inline void w4_out_half(const floatx4 
     }
 }
 
+// The same for an upsampled input's half (point 2 of M is zero; columns of
+// A^T for the points {0, 1, 3, 4, 5}: (1 0 0 0), (1 1 1 1), (1 2 4 8),
+// (1 -2 4 -8), (0 0 0 1)).
+template <int H>
+__device__ __attribute__((always_inline)) inline void w4_out_half_up(const floatx4 (&acc)[W4Shape<true>::NX], int i,
+                                                                    float (&y)[4][4]) {
+    constexpr float AC[5][4] = {{1.f, 0.f, 0.f, 0.f}, {1.f, 1.f, 1.f, 1.f}, {1.f, 2.f, 4.f, 8.f},
+                                {1.f, -2.f, 4.f, -8.f}, {0.f, 0.f, 0.f, 1.f}};
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) y[a][x] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+        float m[5] = {0.f, 0.f, 0.f, 0.f, 0.f};   // the half's products in column c
+        bool any = false;
+#pragma unroll
+        for (int k = 0; k < w4u_count(H); ++k)
+            if (w4u_col(H, k) == c) {
+                m[w4u_row(H, k)] = acc[k][i];
+                any = true;
+            }
+        if (!any) continue;
+        float o[4];
+        w4_at(m[0], m[1], 0.f, m[2], m[3], m[4], o);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                if (AC[c][x] != 0.f) y[a][x] = fmaf(AC[c][x], o[a], y[a][x]);
+    }
+}
+
 // The workgroup's work for the waves of point half H (H is the wave's index
 // mod 2, so the two instantiations run side by side through the same
 // barriers).
-template <int TCW, int H, bool RES, bool SPLIT>
+template <int TCW, bool UP, int H, bool RES, bool SPLIT>
 __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, float *lx0, float *lx1, floatx4 *lu0,
-                                                             floatx4 *lu1) {
-    using G = W4Geom<TCW>;
+                                                             floatx4 *lu1, float *lxb) {
+    using G = W4Geom<TCW, UP>;
+    using S = W4Shape<UP>;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -310,20 +429,21 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
     const int n = wtg * 16 + (lane & 15);
     const int tr = n / TCW, tc = n - (n / TCW) * TCW;
     const int Y0 = y0 + 4 * tr, X0 = x0 + 4 * tc;   // top-left output of the tile
-    int pb[3];
+    constexpr int NPAIR = UP ? 2 : 3, STRIDE = UP ? 2 : 4;   // column pairs of a patch row; tile spacing when staged
+    int pb[NPAIR];
 #pragma unroll
-    for (int h = 0; h < 3; ++h) pb[h] = g4 * G::PLANE + 4 * tr * G::HCP + w4_pos(4 * tc + 2 * h, G::LAY);
+    for (int h = 0; h < NPAIR; ++h) pb[h] = g4 * G::PLANE + STRIDE * tr * G::HCP + w4_pos(STRIDE * tc + 2 * h, G::LAY);
 
     const int nsteps = p.kt * p.nquads;
     const int s0 = SPLIT ? (int)((long long)split * nsteps / p.ksplit) : 0;
     const int s1 = SPLIT ? (int)((long long)(split + 1) * nsteps / p.ksplit) : nsteps;
     WCursor cur = wino_cursor(p, frame, s0);
 
-    floatx4 acc[kW4RB][kW4NX];
+    floatx4 acc[kW4RB][S::NX];
 #pragma unroll
     for (int b = 0; b < kW4RB; ++b)
 #pragma unroll
-        for (int k = 0; k < kW4NX; ++k) acc[b][k] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < S::NX; ++k) acc[b][k] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // Per-lane byte offsets of this wave's chunks of a staged plane (the same
     // for every plane).
@@ -333,8 +453,9 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
         const int e = 64 * (wave + kW4Waves * i) + lane;
         const int r = e / G::HCP, q = e - (e / G::HCP) * G::HCP;
         const int x = w4_col(q, G::LAY, G::HC);   // staged column at position q (-1: none)
-        const int yy = y0 - 1 + r, xx = x0 - 1 + x;
-        soffd[i] = (r < G::HR && x >= 0 && yy >= 0 && yy < p.H && xx >= 0 && xx < p.W) ? (yy * p.W + xx) * 4 : kWOOB;
+        const int yy = (UP ? y0 >> 1 : y0) - 1 + r, xx = (UP ? x0 >> 1 : x0) - 1 + x;
+        soffd[i] = (r < G::HR && x >= 0 && yy >= 0 && yy < p.Hin && xx >= 0 && xx < p.Win) ? (yy * p.Win + xx) * 4
+                                                                                          : kWOOB;
     }
 
     // Step k + 1 is loaded while step k is computed.  The loop is unrolled by
@@ -352,14 +473,18 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
-    w4_stage<TCW>(p, frame, s0, s1, ublk, cur, lx0, lu0, soffd);
+    auto step = [&](const float *lx, const floatx4 *lu) {
+        if constexpr (UP) w4_step_up<TCW, H>(lx, lu, pb, lane, acc);
+        else w4_step<TCW, H>(lx, lu, pb, lane, acc);
+    };
+    w4_stage<TCW, UP>(p, frame, s0, s1, ublk, cur, lx0, lu0, soffd);
     next();
     for (int k = 0; k < nst; k += 2) {
-        w4_stage<TCW>(p, frame, s0 + k + 1, s1, ublk, cur, lx1, lu1, soffd);
-        w4_step<TCW, H>(lx0, lu0, pb, lane, acc);
+        w4_stage<TCW, UP>(p, frame, s0 + k + 1, s1, ublk, cur, lx1, lu1, soffd);
+        step(lx0, lu0);
         next();
-        w4_stage<TCW>(p, frame, s0 + k + 2, s1, ublk, cur, lx0, lu0, soffd);
-        w4_step<TCW, H>(lx1, lu1, pb, lane, acc);
+        w4_stage<TCW, UP>(p, frame, s0 + k + 2, s1, ublk, cur, lx0, lu0, soffd);
+        step(lx1, lu1);
         next();
     }
 
@@ -370,13 +495,17 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
     // rows 2 and 3) and adds the partner's share to its own rows.
     const long long fo = (long long)frame * p.out_fstride;
     const bool rowvec = (p.W & 3) == 0 && X0 < p.W;   // 4 outputs of a row in range, 16-byte aligned
-    float *xb = reinterpret_cast<float *>(wtg == 0 ? lu0 : lu1);   // [receiving half][i][row][col][lane]
+    // [receiving half][i][row][col][lane]: a U buffer, or the upsampled kernel's own exchange area
+    float *xb = UP ? lxb + wtg * (2 * 4 * 8 * 64) : reinterpret_cast<float *>(wtg == 0 ? lu0 : lu1);
     float gs[kW4RB][3];   // per row block: (count, mean, sum of squared deviations) of the lane's outputs
 #pragma unroll
     for (int b = 0; b < kW4RB; ++b) {
         float y[4][4][4];   // [i][row][col]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w4_out_half<H>(acc[b], i, y[i]);
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (UP) w4_out_half_up<H>(acc[b], i, y[i]);
+            else w4_out_half<H>(acc[b], i, y[i]);
+        }
         // the partner's rows to LDS
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -501,31 +630,38 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
     }
 }
 
-template <int TCW, bool RES, bool SPLIT>
+template <int TCW, bool UP, bool RES, bool SPLIT>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(2, 2))) void conv3x3_wino4(WParams p) {
-    using G = W4Geom<TCW>;
+    using G = W4Geom<TCW, UP>;
     // Two stage buffers, declared apart: the compiler then knows that LDS
     // reads of one buffer do not wait for direct loads into the other.
     __shared__ __attribute__((aligned(16))) float lx0[G::XSTEP];
     __shared__ __attribute__((aligned(16))) float lx1[G::XSTEP];
     __shared__ floatx4 lu0[G::USTEP];
     __shared__ floatx4 lu1[G::USTEP];
-    static_assert(G::USTEP * 4 >= 2 * 4 * 8 * 64, "the epilogue exchange of a wave pair fits a U buffer");
+    // the epilogue exchange of a wave pair: a U buffer, or (upsampled input,
+    // whose U buffers are smaller) an area of its own
+    __shared__ float lxb[UP ? kW4TG * 2 * 4 * 8 * 64 : 1];
+    static_assert(UP || G::USTEP * 4 >= 2 * 4 * 8 * 64, "the epilogue exchange of a wave pair fits a U buffer");
     static_assert(G::XSTEP >= kW4Waves * kW4RB * 4 * 3, "the GroupNorm quads fit an input buffer");
-    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) w4_body<TCW, 1, RES, SPLIT>(p, lx0, lx1, lu0, lu1);
-    else w4_body<TCW, 0, RES, SPLIT>(p, lx0, lx1, lu0, lu1);
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & 1) w4_body<TCW, UP, 1, RES, SPLIT>(p, lx0, lx1, lu0, lu1, lxb);
+    else w4_body<TCW, UP, 0, RES, SPLIT>(p, lx0, lx1, lu0, lu1, lxb);
 }
 
 // Packed U: [workgroup block of 32 output channels][step = (dt, channel
 // quad)][row block b][q][lane][4] with lane = (channel of the quad) * 16 +
-// (output channel within the row block).  Float4s q = 5 H + k / 4 hold
-// product k = 6 c + r of half H, i.e. point (r, 3 H + c) of the transform, in
-// component k % 4 (the two components past product 17 are zero); zero where
-// the output or input channel is out of range and in the padding, so a
-// workgroup's rows of one step are contiguous.  One thread per (block, step,
-// row block, lane).
+// (output channel within the row block).  A plain input's float4s q = 5 H +
+// k / 4 hold product k = 6 c + r of half H, i.e. point (r, 3 H + c) of the
+// transform, in component k % 4 (the two components past product 17 are
+// zero); an upsampled input's float4s q = 4 H + k / 4 hold product k of half
+// H (w4u_row, w4u_col over the points {0, 1, 3, 4, 5}), scaled by -3 for each
+// index that is point 3.  Zero where the output or input channel is out of
+// range and in the padding, so a workgroup's rows of one step are
+// contiguous.  One thread per (block, step, row block, lane).
+template <bool UP>
 __global__ __launch_bounds__(256) void pack_wino4_kernel(const float *__restrict__ w, float *__restrict__ dst, int cout,
                                                          int cin, int kt, int nquads, long long total) {
+    using S = W4Shape<UP>;
     const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
     if (id >= total) return;
     const int lane = (int)(id & 63);
@@ -550,19 +686,32 @@ __global__ __launch_bounds__(256) void pack_wino4_kernel(const float *__restrict
     for (int x = 0; x < 6; ++x)
 #pragma unroll
         for (int j = 0; j < 3; ++j) t[x][j] = G[x][0] * g[0][j] + G[x][1] * g[1][j] + G[x][2] * g[2][j];
-    float u[kW4UQ * 4];
+    auto U = [&](int x, int y) { return t[x][0] * G[y][0] + t[x][1] * G[y][1] + t[x][2] * G[y][2]; };
+    float u[S::UQ * 4];
 #pragma unroll
-    for (int k = 0; k < kW4UQ * 4; ++k) u[k] = 0.f;
+    for (int k = 0; k < S::UQ * 4; ++k) u[k] = 0.f;
+    if (!UP) {
 #pragma unroll
-    for (int x = 0; x < 6; ++x)
+        for (int x = 0; x < 6; ++x)
 #pragma unroll
-        for (int y = 0; y < 6; ++y) {
-            const int h = y / 3, k = 6 * (y % 3) + x;   // half, product of the half
-            u[4 * kW4NQ * h + k] = (float)(t[x][0] * G[y][0] + t[x][1] * G[y][1] + t[x][2] * G[y][2]);
-        }
-    float *out = dst + bsb * (kW4UQ * 256) + lane * 4;
+            for (int y = 0; y < 6; ++y) {
+                const int h = y / 3, k = 6 * (y % 3) + x;   // half, product of the half
+                u[4 * S::Q1 * h + k] = (float)U(x, y);
+            }
+    } else {
+        const int pts[5] = {0, 1, 3, 4, 5};
+        const double f[5] = {1.0, 1.0, -3.0, 1.0, 1.0};   // point 3 reads -3 x the transformed input of point 4
 #pragma unroll
-    for (int q = 0; q < kW4UQ; ++q)
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int k = 0; k < w4u_count(h); ++k) {
+                const int a = w4u_row(h, k), cc = w4u_col(h, k);
+                u[4 * S::Q1 * h + k] = (float)(f[a] * f[cc] * U(pts[a], pts[cc]));
+            }
+    }
+    float *out = dst + bsb * (S::UQ * 256) + lane * 4;
+#pragma unroll
+    for (int q = 0; q < S::UQ; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[q * 256 + e] = u[4 * q + e];
 }
@@ -583,27 +732,34 @@ W4Grid w4_grid(int cout, int H, int W) {
     return g;
 }
 
-template <int TCW>
+template <int TCW, bool UP>
 void w4_launch_t(const WParams &p, bool res, bool split, dim3 grid, hipStream_t s) {
-    if (split) hipLaunchKernelGGL((conv3x3_wino4<TCW, false, true>), grid, dim3(kW4Threads), 0, s, p);
-    else if (res) hipLaunchKernelGGL((conv3x3_wino4<TCW, true, false>), grid, dim3(kW4Threads), 0, s, p);
-    else hipLaunchKernelGGL((conv3x3_wino4<TCW, false, false>), grid, dim3(kW4Threads), 0, s, p);
+    if (split) hipLaunchKernelGGL((conv3x3_wino4<TCW, UP, false, true>), grid, dim3(kW4Threads), 0, s, p);
+    else if (res) hipLaunchKernelGGL((conv3x3_wino4<TCW, UP, true, false>), grid, dim3(kW4Threads), 0, s, p);
+    else hipLaunchKernelGGL((conv3x3_wino4<TCW, UP, false, false>), grid, dim3(kW4Threads), 0, s, p);
+}
+
+template <int TCW>
+void w4_launch_tc(const WParams &p, bool up, bool res, bool split, dim3 grid, hipStream_t s) {
+    if (up) w4_launch_t<TCW, true>(p, res, split, grid, s);
+    else w4_launch_t<TCW, false>(p, res, split, grid, s);
 }
 
 }  // namespace
 
-size_t conv3x3_wino4_packed_floats(int cout, int cin, int kt) {
+size_t conv3x3_wino4_packed_floats(int cout, int cin, int kt, int up) {
     const size_t blocks = (size_t)(cout + kW4RB * kW4Blk - 1) / (kW4RB * kW4Blk);
     const size_t nsteps = (size_t)kt * ((cin + kWCh - 1) / kWCh);
-    return blocks * nsteps * kW4RB * kW4UQ * 256;
+    return blocks * nsteps * kW4RB * (up ? W4Shape<true>::UQ : W4Shape<false>::UQ) * 256;
 }
 
-int32_t pack_conv3x3_wino4(const float *w, int cout, int cin, int kt, float *dst, hipStream_t s) {
+int32_t pack_conv3x3_wino4(const float *w, int cout, int cin, int kt, int up, float *dst, hipStream_t s) {
     const int nquads = (cin + kWCh - 1) / kWCh;
     const long long blocks = (cout + kW4RB * kW4Blk - 1) / (kW4RB * kW4Blk);
     const long long total = blocks * kt * nquads * kW4RB * 64;
     const dim3 grid((unsigned)((total + 255) / 256));
-    hipLaunchKernelGGL(pack_wino4_kernel, grid, dim3(256), 0, s, w, dst, cout, cin, kt, nquads, total);
+    if (up) hipLaunchKernelGGL(pack_wino4_kernel<true>, grid, dim3(256), 0, s, w, dst, cout, cin, kt, nquads, total);
+    else hipLaunchKernelGGL(pack_wino4_kernel<false>, grid, dim3(256), 0, s, w, dst, cout, cin, kt, nquads, total);
     return check_launch("pack_conv3x3_wino4");
 }
 
@@ -628,12 +784,17 @@ int conv3x3_wino4_gn_records(const ConvLaunch &a) {
 int conv3x3_wino4_tcw(const ConvLaunch &a) { return w4_tcw(a.W); }
 
 int32_t launch_conv3x3_wino4_main(const ConvLaunch &a, hipStream_t s) {
-    if (a.denorm || a.gn_coef || a.upsample) {
-        set_error("conv3x3_wino4: a plain input only (no de-normalisation, GroupNorm on load or upsampling)");
+    if (a.denorm || a.gn_coef) {
+        set_error("conv3x3_wino4: no de-normalisation or GroupNorm on load");
         return VAE_ERR_UNSUPPORTED;
     }
-    if (a.wino != 3) {
-        set_error("conv3x3_wino4: weights not packed by pack_conv3x3_wino4");
+    if ((a.wino == 4) != (a.upsample != 0) || a.wino < 3) {
+        set_error("conv3x3_wino4: weights not packed by pack_conv3x3_wino4 for %s input",
+                  a.upsample ? "an upsampled" : "a plain");
+        return VAE_ERR_INVALID_ARG;
+    }
+    if (a.upsample && ((a.H | a.W) & 1)) {
+        set_error("conv3x3_wino4: an upsampled input has even sizes");
         return VAE_ERR_INVALID_ARG;
     }
     WParams p;
@@ -647,11 +808,11 @@ int32_t launch_conv3x3_wino4_main(const ConvLaunch &a, hipStream_t s) {
     p.cout = a.cout;
     p.H = a.H;
     p.W = a.W;
-    p.Hin = a.H;
-    p.Win = a.W;
+    p.Hin = a.upsample ? a.H / 2 : a.H;
+    p.Win = a.upsample ? a.W / 2 : a.W;
     p.kt = a.kt;
     p.nquads = (a.cin + kWCh - 1) / kWCh;
-    p.in_fstride = (long long)a.H * a.W;
+    p.in_fstride = (long long)p.Hin * p.Win;
     p.in_cstride = p.in_fstride * a.T;
     p.out_fstride = (long long)a.H * a.W;
     p.out_cstride = p.out_fstride * a.T;
@@ -690,11 +851,11 @@ int32_t launch_conv3x3_wino4_main(const ConvLaunch &a, hipStream_t s) {
         p.gn_cpg = a.cout / 32;
         p.gn_nrec = g.tiles_x * g.tiles_y * (int)grid.z;
     }
-    const bool res = a.res != nullptr, split = p.ksplit > 1;
+    const bool up = a.upsample != 0, res = a.res != nullptr, split = p.ksplit > 1;
     switch (g.tcw) {
-    case 16: w4_launch_t<16>(p, res, split, grid, s); break;
-    case 8: w4_launch_t<8>(p, res, split, grid, s); break;
-    default: w4_launch_t<4>(p, res, split, grid, s); break;
+    case 16: w4_launch_tc<16>(p, up, res, split, grid, s); break;
+    case 8: w4_launch_tc<8>(p, up, res, split, grid, s); break;
+    default: w4_launch_tc<4>(p, up, res, split, grid, s); break;
     }
     return check_launch("conv3x3_wino4");
 }

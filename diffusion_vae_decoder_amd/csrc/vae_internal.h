@@ -47,8 +47,8 @@ struct ConvLaunch {
                            // [32][conv3x3_gn_records()] of (count, mean, M2, 0); M2 is the sum of
                            // squared deviations from the record's own mean
     int wino;              // wpk layout: 0 pack_conv3x3 (implicit GEMM); 1, 2 pack_conv3x3_wino
-                           // (Winograd F(2x2,3x3)) for a plain, an upsampled input; 3
-                           // pack_conv3x3_wino4 (Winograd F(4x4,3x3), a plain input only)
+                           // (Winograd F(2x2,3x3)) for a plain, an upsampled input; 3, 4
+                           // pack_conv3x3_wino4 (Winograd F(4x4,3x3)) for a plain, an upsampled input
 };
 
 // Bytes of the packed weights for a conv with `cout` x `cin` x (kt x 3 x 3).
@@ -84,12 +84,12 @@ int conv3x3_wino_ksplit(const ConvLaunch &a);
 int conv3x3_wino_gn_records(const ConvLaunch &a);
 int conv3x3_wino_tcw(const ConvLaunch &a);   // tiles per row of its workgroup block
 
-// Winograd F(4x4, 3x3) form (conv_wino4.hip) for a plain input: weights
-// packed by pack_conv3x3_wino4; same split-K workspace, reduction and
-// GroupNorm records as the forms above; no upsampling, de-normalisation or
-// GroupNorm on load.
-size_t conv3x3_wino4_packed_floats(int cout, int cin, int kt);
-int32_t pack_conv3x3_wino4(const float *w, int cout, int cin, int kt, float *dst, hipStream_t s);
+// Winograd F(4x4, 3x3) form (conv_wino4.hip): weights packed by
+// pack_conv3x3_wino4 (`up`: for an upsampled input, which only this packing
+// may then be used with); same split-K workspace, reduction and GroupNorm
+// records as the forms above; no de-normalisation or GroupNorm on load.
+size_t conv3x3_wino4_packed_floats(int cout, int cin, int kt, int up);
+int32_t pack_conv3x3_wino4(const float *w, int cout, int cin, int kt, int up, float *dst, hipStream_t s);
 int32_t launch_conv3x3_wino4_main(const ConvLaunch &a, hipStream_t s);
 int conv3x3_wino4_ksplit(const ConvLaunch &a);
 int conv3x3_wino4_gn_records(const ConvLaunch &a);

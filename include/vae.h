@@ -111,12 +111,11 @@ int32_t vae_abi_version(void);
 
 /* The form of the 3x3 convolutions (every 3x3 conv but conv_in, which always
  * runs as an implicit GEMM that de-normalises the latent while loading it):
- *   VAE_CONV3X3_WINOGRAD_4X4   (default) Winograd F(4x4, 3x3) on FP32 MFMA for
- *                              convs on a plain input: 36 of the direct conv's
- *                              144 multiplies per 4x4 outputs and input
- *                              channel, results within about 1e-5 of the
- *                              output's magnitude of the exact conv; convs on
- *                              a nearest-x2 input use F(2x2, 3x3);
+ *   VAE_CONV3X3_WINOGRAD_4X4   (default) Winograd F(4x4, 3x3) on FP32 MFMA:
+ *                              36 of the direct conv's 144 multiplies per 4x4
+ *                              outputs and input channel (25 on a nearest-x2
+ *                              input), results within about 1e-5 of the
+ *                              output's magnitude of the exact conv;
  *   VAE_CONV3X3_WINOGRAD_2X2   Winograd F(2x2, 3x3) on FP32 MFMA for every
  *                              conv: 16 of 36 multiplies per 2x2 outputs and
  *                              input channel (9 on a nearest-x2 input); about

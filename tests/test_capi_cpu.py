@@ -238,9 +238,10 @@ def test_decoder_pack_and_validation(lib):
     # about 50M parameters, of which 48.3M in 3x3 convs; the F(4x4) Winograd
     # packing of the convs on a plain input (43M parameters) holds 40 floats
     # per (output, input channel) pair instead of 9 (36 transform points, padded
-    # to whole float4s per half), the F(2x2) packing of the three upsample
-    # convs (5.3M parameters) 10: about 198M floats in all
-    assert 197_000_000 * 4 < nb.value < 199_000_000 * 4
+    # to whole float4s per half), that of the three convs on a nearest-x2 input
+    # (5.3M parameters) 28 (25 distinct products, 13 + 12 per half, padded to
+    # whole float4s): about 208.5M floats in all
+    assert 208_000_000 * 4 < nb.value < 209_000_000 * 4
     h = c_void_p()
     assert lib.vae_decoder_create(byref(h), byref(w), FAKE, nb.value - 1, NULL) == VAE_ERR_WORKSPACE
     assert lib.vae_decoder_create(byref(h), byref(w), FAKE + 4, nb.value, NULL) == VAE_ERR_INVALID_ARG
