@@ -466,12 +466,19 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
     const float *ublk = p.u + (size_t)cb * nsteps * (G::UROWS * 256);
     // The barrier between steps orders only direct loads (each wave has
     // waited for its own) and LDS reads, so it needs no memory fence: a
-    // compiler-only barrier keeps the accesses on their side of it.
+    // compiler-only barrier keeps the accesses on their side of it.  The
+    // scheduling barriers pin the order of the whole step: the next step's
+    // loads are issued before any of this step's MFMAs, and the wait for them
+    // comes after the last one (left free, the scheduler moves the wait and the
+    // barrier, which touch no registers, into the middle of the MFMAs and the
+    // loads down to just before the wait, exposing their latency every step).
     auto next = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto step = [&](const float *lx, const floatx4 *lu) {
         if constexpr (UP) w4_step_up<TCW, H>(lx, lu, pb, lane, acc);
@@ -481,9 +488,11 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
     next();
     for (int k = 0; k < nst; k += 2) {
         w4_stage<TCW, UP>(p, frame, s0 + k + 1, s1, ublk, cur, lx1, lu1, soffd);
+        __builtin_amdgcn_sched_barrier(0);
         step(lx0, lu0);
         next();
         w4_stage<TCW, UP>(p, frame, s0 + k + 2, s1, ublk, cur, lx0, lu0, soffd);
+        __builtin_amdgcn_sched_barrier(0);
         step(lx1, lu1);
         next();
     }
@@ -766,13 +775,23 @@ int32_t pack_conv3x3_wino4(const float *w, int cout, int cin, int kt, int up, fl
 int conv3x3_wino4_ksplit(const ConvLaunch &a) {
     const W4Grid g = w4_grid(a.cout, a.H, a.W);
     const long long base = (long long)g.tiles_x * g.tiles_y * g.ncb * a.T;
-    if (base >= 2 * kW4Slots) return 1;
     const int nsteps = a.kt * ((a.cin + kWCh - 1) / kWCh);
-    long long s = (2 * kW4Slots + base - 1) / base;   // about two rounds of workgroups
-    if (s > nsteps / 4) s = nsteps / 4;                // each split keeps >= 4 steps
-    if (s > 16) s = 16;
-    if (s * a.T > 65535) s = 65535 / a.T;
-    return s < 1 ? 1 : (int)s;
+    auto cap = [&](long long s) {
+        if (s > nsteps / 4) s = nsteps / 4;            // each split keeps >= 4 steps
+        if (s > 16) s = 16;
+        if (s * a.T > 65535) s = 65535 / a.T;
+        return s < 1 ? 1LL : s;
+    };
+    // Candidates: the fewest splits that fill one round of resident workgroups,
+    // and twice that.  Cost, in full-K workgroup times: rounds of workgroups
+    // over splits, with the doubled split charged 15% for its partial sums and
+    // their reduction (measured 7-32% per doubling at equal rounds per split).
+    const long long s1 = cap(base >= kW4Slots ? 1 : (kW4Slots + base - 1) / base);
+    const long long s2 = cap(2 * s1);
+    auto cost = [&](long long s) {
+        return (double)((base * s + kW4Slots - 1) / kW4Slots) / (double)s * (s > s1 ? 1.15 : 1.0);
+    };
+    return (int)(cost(s2) < cost(s1) ? s2 : s1);
 }
 
 int conv3x3_wino4_gn_records(const ConvLaunch &a) {

@@ -355,9 +355,14 @@ struct Runner {
     ProfEntry *begin(const char *kernel, const std::string &layer, double flops, double bytes) {
         if (!d->profiling || rc != VAE_OK) return nullptr;
         if (d->prof_used == d->prof.size()) {
+            // timing-only events: no system-scope fence when they are recorded (a
+            // cache writeback per event would stall the stream between launches);
+            // their times are read only after the caller has synchronised the device
             ProfEntry e;
-            if ((rc = hip_status(hipEventCreate(&e.start), "hipEventCreate")) != VAE_OK) return nullptr;
-            if ((rc = hip_status(hipEventCreate(&e.stop), "hipEventCreate")) != VAE_OK) return nullptr;
+            if ((rc = hip_status(hipEventCreateWithFlags(&e.start, hipEventDisableSystemFence),
+                                 "hipEventCreateWithFlags")) != VAE_OK) return nullptr;
+            if ((rc = hip_status(hipEventCreateWithFlags(&e.stop, hipEventDisableSystemFence),
+                                 "hipEventCreateWithFlags")) != VAE_OK) return nullptr;
             d->prof.push_back(e);
         }
         ProfEntry *e = &d->prof[d->prof_used++];

@@ -314,7 +314,9 @@ typedef struct vae_prof_record {
 /* Clears the recorded launches.  on != 0: the following vae_decode calls
  * bracket every launch with HIP events on their stream and append one
  * record per launch (events are created on first use; a failure to create
- * one is reported as VAE_ERR_HIP by vae_decode). */
+ * one is reported as VAE_ERR_HIP by vae_decode).  The events only time: they
+ * are recorded without a system-scope memory fence, so they order nothing for
+ * the host; synchronise the stream before reading the decode's output. */
 int32_t vae_decoder_set_profiling(vae_decoder *d, int32_t on);
 
 /* Synchronises on the recorded events and copies up to `max` records
