@@ -106,12 +106,22 @@ def test_conv3x3(api, algo, cin, cout, h, w):
     assert rel_err(host(y), oracle.conv2d(x, wt, b)) <= LAYER_TOL
 
 
-@pytest.mark.parametrize("cin,cout,h,w", [(32, 64, 9, 13), (64, 128, 16, 16), (16, 32, 4, 4), (128, 128, 32, 32)])
-def test_conv3x3_upsample_folded(api, algo, cin, cout, h, w):
-    x = vaegen.activation(2, "xu", (cin, h, w))
-    wt, b = conv_params(2, "cu", cin, cout, 3)
-    y = api.conv2d(dev(x), dev(wt), dev(b), upsample2x=True, out=nan_like((cout, 2 * h, 2 * w)))
-    ref = oracle.conv2d(oracle.upsample_nearest2x(x), wt, b)
+@pytest.mark.parametrize("cin,cout,h,w,res", [
+    (32, 64, 9, 13, False),      # ragged source: partial output tiles
+    (64, 128, 16, 16, False),
+    (16, 32, 4, 4, False),
+    (128, 128, 32, 32, False),
+    (30, 40, 7, 5, False),       # last channel quad partial, cout not a multiple of 32
+    (512, 64, 6, 10, False),     # long K on a small image: split along K
+    (48, 96, 11, 9, True),       # residual added in the epilogue
+])
+def test_conv3x3_upsample_folded(api, algo, cin, cout, h, w, res):
+    x = vaegen.activation(2, f"xu{cin}_{h}_{w}", (cin, h, w))
+    wt, b = conv_params(2, f"cu{cin}_{cout}", cin, cout, 3)
+    r = vaegen.activation(2, f"ru{cout}_{h}_{w}", (cout, 2 * h, 2 * w)) if res else None
+    y = api.conv2d(dev(x), dev(wt), dev(b), upsample2x=True, residual=dev(r) if res else None,
+                   out=nan_like((cout, 2 * h, 2 * w)))
+    ref = oracle.conv2d(oracle.upsample_nearest2x(x), wt, b) + (r if res else 0.0)
     assert rel_err(host(y), ref) <= LAYER_TOL
 
 
