@@ -12,10 +12,11 @@
 // The softmax never gets a pass of its own.  The scores are produced
 // transposed, so the 32 scores of one query in an MFMA tile sit in one lane:
 // the score GEMM's epilogue reduces them to (max, sum of exp(s - max)) per
-// query and 128-key block; softmax_merge combines the blocks of every query
-// in a fixed order into (max, 1 / sum); and the P V GEMM exponentiates and
-// scales the scores as it loads them.  The n x n score matrix is written
-// once and read once.
+// query and 128-key block and stores exp(s - block max) in place of the
+// scores; softmax_merge combines the blocks of every query in a fixed order
+// into (max, 1 / sum); and the P V GEMM rescales each 128-key block of those
+// exponentials to the query's max and sum as it loads them (one multiply per
+// score).  The n x n matrix is written once and read once.
 //
 // Workspace: xn [c, n] | QKV [3c, n] | St [n, n] | O [c, n] |
 //            column statistics [ceil(n/128)][n] x 2 | merged [n] x 2 | GroupNorm partials |
@@ -104,7 +105,8 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
     if ((rc = launch_gemm(g, s)) != VAE_OK) return rc;
 
     const float *Q = qkv, *K = qkv + (size_t)c * n, *V = qkv + (size_t)2 * c * n;
-    // St[u, t] = sum_ch K[ch, u] Q[ch, t] / sqrt(c), with per-(key block, query) statistics
+    // s[u, t] = sum_ch K[ch, u] Q[ch, t] / sqrt(c); St[u, t] = exp(s[u, t] - mb) with mb the max
+    // of query t's scores over u's 128-key block, and per-(key block, query) (mb, sum)
     g = GemmLaunch{};
     g.A = K; g.lda = n; g.a_km = 1;
     g.B = Q; g.ldb = n; g.b_nk = 0;
@@ -117,13 +119,14 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
                        reinterpret_cast<const floatx2 *>(colstat), blocks, (int)n, reinterpret_cast<floatx2 *>(stat));
     if ((rc = check_launch("softmax_merge")) != VAE_OK) return rc;
 
-    // O[ch, t] = sum_u V[ch, u] P[t, u], P[t, u] = exp(St[u, t] - m_t) / l_t applied on load
+    // O[ch, t] = sum_u V[ch, u] P[t, u], P[t, u] = St[u, t] exp(mb - m_t) / l_t applied on load
     g = GemmLaunch{};
     g.A = V; g.lda = n; g.a_km = 0;
     g.B = St; g.ldb = n; g.b_nk = 0;
     g.C = O; g.ldc = n;
     g.M = c; g.N = (int)n; g.K = (int)n; g.alpha = 1.f;
     g.bsoft = stat;
+    g.bsoft_blk = colstat;
     g.part = part;
     if ((rc = launch_gemm(g, s)) != VAE_OK) return rc;
 

@@ -20,11 +20,14 @@
 //
 // Two attention-only variants split a row softmax across the two products
 // that surround it (the score matrix is written once and read once):
-//   - EPI_COLSTAT: besides C, each workgroup writes for every column n of its
-//     tile the (max, sum of exp(c - max)) over its valid rows m, at
-//     colstat[blockIdx.y * N + n];
-//   - B_SOFTMAX: B(k, n) (KN) is replaced on load by exp(B(k, n) - mx[n]) *
-//     inv[n] with (mx, inv) = bsoft[n], the merged statistics of column n.
+//   - EPI_COLSTAT: each workgroup takes, for every column n of its tile, the
+//     maximum mb over its valid rows m, stores exp(c - mb) in place of c (the
+//     exponentials are needed here for the sums anyway) and writes (mb, sum of
+//     exp(c - mb)) at colstat[blockIdx.y * N + n];
+//   - B_SOFTMAX: such a B(k, n) (KN) is scaled on load by exp(mb - mx[n]) *
+//     inv[n], with (mx, inv) = bsoft[n] the merged statistics of column n and
+//     mb = bsblk[(k / 128) * N + n] the maximum of k's 128-row block: one
+//     multiply per element, the factor recomputed once per 128 rows.
 
 #include "vae_internal.h"
 
@@ -44,6 +47,7 @@ struct Params {
     float *C;
     floatx2 *colstat;
     const floatx2 *bsoft;
+    const floatx2 *bsblk;   // B_SOFTMAX: the block statistics EPI_COLSTAT wrote for B
     float *part;       // split K: partial sums [ksplit][M][N]
     int M, N, K, ksplit;
     long long lda, ldb, ldc, ldr;
@@ -111,20 +115,30 @@ __device__ __attribute__((always_inline)) inline void tile_load_full(const float
 }
 
 // B_SOFTMAX: this thread's four columns n0 + (tid & 31) * 4 + e are the same
-// for every chunk; entries outside the matrix become 0.
+// for every chunk, and a chunk's 16 rows lie in one 128-row block, whose
+// factors f are current; entries outside the matrix become 0.
 template <bool FULL>
 __device__ __attribute__((always_inline)) inline void softmax_on_load(floatx4 (&r)[2], int k0, int n,
-                                                                      int K, int N, const float (&mx)[4],
-                                                                      const float (&inv)[4]) {
+                                                                      int K, int N, const float (&f)[4]) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int k = k0 + ((threadIdx.x + q * kThreads) >> 5);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float p = __expf(r[q][e] - mx[e]) * inv[e];
-            r[q][e] = (FULL || (k < K && n + e < N)) ? p : 0.f;
+            const float v = r[q][e] * f[e];
+            r[q][e] = (FULL || (k < K && n + e < N)) ? v : 0.f;
         }
     }
+}
+
+// The factors exp(mb - mx) * inv of the thread's four columns for the 128-row
+// block of B that holds row k0.
+__device__ __attribute__((always_inline)) inline void softmax_factors(const floatx2 *bsblk, int k0, int n, int N,
+                                                                      const float (&mx)[4], const float (&inv)[4],
+                                                                      float (&f)[4]) {
+    const long long row = (long long)(k0 >> 7) * N;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __expf(bsblk[row + (n + e < N ? n + e : N - 1)][0] - mx[e]) * inv[e];
 }
 
 template <bool TRANS>
@@ -197,7 +211,12 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
         tile_load<A_MK, VEC>(p.A, p.lda, kb, m0, p.K, p.M, ra);
         tile_load<B_NK, VEC>(p.B, p.ldb, kb, n0, p.K, p.N, rb);
     }
-    if (BSM) softmax_on_load<FULL>(rb, kb, sn, p.K, p.N, smx, sinv);
+    float sf[4];          // B_SOFTMAX factors of the current 128-row block of B
+    int sblk = kb >> 7;
+    if (BSM) {
+        softmax_factors(p.bsblk, kb, sn, p.N, smx, sinv, sf);
+        softmax_on_load<FULL>(rb, kb, sn, p.K, p.N, sf);
+    }
     tile_store<A_MK>(As[0], ra);
     tile_store<B_NK>(Bs[0], rb);
     __syncthreads();
@@ -227,7 +246,14 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
             acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
         }
         if (it + 1 < n_iter) {
-            if (BSM) softmax_on_load<FULL>(rb, kb + (it + 1) * BK, sn, p.K, p.N, smx, sinv);
+            if (BSM) {
+                const int k1 = kb + (it + 1) * BK;
+                if ((k1 >> 7) != sblk) {
+                    sblk = k1 >> 7;
+                    softmax_factors(p.bsblk, k1, sn, p.N, smx, sinv, sf);
+                }
+                softmax_on_load<FULL>(rb, k1, sn, p.K, p.N, sf);
+            }
             tile_store<A_MK>(As[buf ^ 1], ra);
             tile_store<B_NK>(Bs[buf ^ 1], rb);
         }
@@ -251,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
                     float v = p.alpha * acc[i][j][r];
                     if (p.bias) v += p.bias[m];
                     if (RES) v += p.R[(long long)m * p.ldr + n];
-                    p.C[(long long)m * p.ldc + n] = v;
+                    if (EPI != EPI_COLSTAT) p.C[(long long)m * p.ldc + n] = v;   // COLSTAT stores below
                     acc[i][j][r] = v;
                 }
             }
@@ -288,14 +314,20 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
             const int nl = wn * 64 + j * 32 + l32;
             cm[j] = fmaxf(red[nl], red[128 + nl]);
         }
+        // C holds exp(c - column maximum of the block); the sums are of those
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                 if (FULL || m < p.M) {
-                    sm[0] += __expf(acc[i][0][r] - cm[0]);
-                    sm[1] += __expf(acc[i][1][r] - cm[1]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int n = n0 + wn * 64 + j * 32 + l32;
+                        const float e = __expf(acc[i][j][r] - cm[j]);
+                        sm[j] += e;
+                        if (FULL || n < p.N) p.C[(long long)m * p.ldc + n] = e;
+                    }
                 }
             }
 #pragma unroll
@@ -375,6 +407,7 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
         return VAE_ERR_WORKSPACE;
     }
     p.bsoft = reinterpret_cast<const floatx2 *>(g.bsoft);
+    p.bsblk = reinterpret_cast<const floatx2 *>(g.bsoft_blk);
     p.M = g.M;
     p.N = g.N;
     p.K = g.K;
@@ -398,7 +431,8 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
     if (g.colstat || g.bsoft) {
         // the two halves of the attention softmax: scores k^T q (A = k stored KM,
         // B = q stored KN) and P v (A = v stored MK, B = the scores stored KN)
-        if (res || b_nk || (g.colstat && g.bsoft) || (g.colstat && a_mk) || (g.bsoft && !a_mk)) {
+        if (res || b_nk || (g.colstat && g.bsoft) || (g.colstat && a_mk) || (g.bsoft && !a_mk) ||
+            (g.bsoft && !g.bsoft_blk)) {
             set_error("gemm: unsupported softmax-split configuration");
             return VAE_ERR_UNSUPPORTED;
         }

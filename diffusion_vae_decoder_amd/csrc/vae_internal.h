@@ -139,9 +139,12 @@ struct GemmLaunch {
     int a_km, b_nk;
     float alpha;
     // Row softmax split over two products (attention only; see gemm.hip):
-    float *colstat;        // if set: (max, sum exp(c - max)) of each column n over each 128-row block,
+    float *colstat;        // if set: C holds exp(c - mb) with mb the maximum of column n over its
+                           // 128-row block, and colstat the (mb, sum exp(c - mb)) of each block,
                            // [ceil(M / 128)][N] pairs; needs a_km, KN B and no residual
-    const float *bsoft;    // if set: B(k, n) -> exp(B(k, n) - bsoft[2n]) * bsoft[2n + 1]; needs MK A, KN B
+    const float *bsoft;    // if set: B(k, n) -> B(k, n) * exp(blk - bsoft[2n]) * bsoft[2n + 1], with
+                           // blk = bsoft_blk[2 ((k / 128) N + n)]; needs MK A, KN B
+    const float *bsoft_blk;
     float *part;           // K-split partial sums, gemm_partial_floats() floats (nullptr if 0); C's ldc must be N
 };
 int32_t launch_gemm(const GemmLaunch &g, hipStream_t s);
