@@ -367,6 +367,17 @@ def test_decode_ragged_latent(decoder, params):
     assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
 
 
+@pytest.mark.parametrize("h,w", [(1, 1), (1, 7), (3, 1)])
+def test_decode_degenerate_latent(decoder, params, h, w):
+    # one token (the attention's softmax over a single key), one latent row,
+    # one latent column: every layer smaller than a tile in at least one axis
+    z = vaegen.latent(9, h, w)
+    rgb = decoder.decode(dev(z), out=nan_like((3, 8 * h, 8 * w)))
+    ref = oracle.decode(z, params, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    cos, mx = rgb_metrics(host(rgb), ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
 @pytest.mark.parametrize("name,h", [("decode_256", 32), ("decode_1024", 128)])
 def test_decode_full_size_against_stored_oracle(decoder, name, h):
     path = os.path.join(GOLDEN, name + ".npz")
