@@ -307,8 +307,12 @@ class Decoder:
         return nb.value
 
     def decode(self, latent: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """latent [c, h, w] -> rgb [3, 8h, 8w]; for a 3-D decoder [c, t, h, w] -> [3, t, 8h, 8w]."""
-        _dev(latent, "latent")
+        """latent [c, h, w] -> rgb [3, 8h, 8w]; for a 3-D decoder [c, t, h, w] -> [3, t, 8h, 8w].
+
+        The latent's rank, channel count (conv_in's inputs) and device are
+        checked here: vae_decode takes no channel count, so a latent with
+        fewer channels would be read past its end."""
+        self._check_latent(latent)
         if self.causal3d:
             c, t, h, w = latent.shape
         else:
@@ -327,6 +331,20 @@ class Decoder:
             check(self._lib.vae_decode(self._h, latent.data_ptr(), h, w, rgb.data_ptr(), self._ws.data_ptr(),
                                        self._ws.numel(), _stream()))
         return rgb
+
+    def _check_latent(self, latent) -> None:
+        if not isinstance(latent, torch.Tensor):
+            raise TypeError("latent must be a torch.Tensor")
+        rank = 4 if self.causal3d else 3
+        if latent.dim() != rank:
+            raise ValueError(f"latent must have {rank} dimensions ({'[c, t, h, w]' if self.causal3d else '[c, h, w]'}), "
+                             f"got shape {tuple(latent.shape)}")
+        if latent.shape[0] != self.latent_channels:
+            raise ValueError(f"latent has {latent.shape[0]} channels; the decoder's conv_in takes "
+                             f"{self.latent_channels}")
+        _dev(latent, "latent")
+        if latent.device != self.device:
+            raise ValueError(f"latent is on {latent.device}, the decoder's weights on {self.device}")
 
     def set_groupnorm_fusion(self, on: bool) -> None:
         """Apply GroupNorm + SiLU while each conv loads its input (off by default)."""

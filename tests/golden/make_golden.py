@@ -3,13 +3,19 @@
 Calls only the float64 oracle (oracle/) on inputs from the seeded generator
 (vaegen/, seed 0); nothing here touches the GPU path.  Run from the repo root:
 
-    python tests/golden/make_golden.py [decode256] [decode1024] [stack3d]
+    python tests/golden/make_golden.py [decode1024] [stack3d]
 
 Outputs (numpy .npz, float64):
-  decode_256.npz   latent [16,32,32]  -> RGB [3,256,256], every 4th pixel per axis
-  decode_1024.npz  latent [16,128,128] -> RGB [3,1024,1024], every 16th pixel per axis
+  decode_1024.npz  latent [16,128,128] -> RGB [3,1024,1024]: a lattice of
+                   rows and columns that covers every residue mod 4 (the
+                   first four rows and columns of every 32-row / 32-column
+                   band, so each 4 x 4 output block position of the
+                   Winograd tiling appears), the whole first and last rows
+                   and columns, and 16384 pseudo-random pixels
   stack3d.npz      x [128,17,256,256] -> 4-layer causal stack, 4096 sampled elements
 Each file also holds max|ref| and the L2 norm of the whole reference output.
+The 256 x 256 decode is compared on every pixel by running the oracle inside
+the test, so it has no stored file.
 """
 from __future__ import annotations
 
@@ -39,15 +45,28 @@ def keep_heap():
         pass
 
 
-def decode(h: int, stride: int, name: str):
+def lattice(n: int) -> np.ndarray:
+    """Indices 32 k + r, r = 0..3, plus the last index: every residue mod 4."""
+    idx = sorted({b + r for b in range(0, n, 32) for r in range(4) if b + r < n} | {n - 1})
+    return np.array(idx, dtype=np.int64)
+
+
+def decode1024():
+    h = 128
     p = vaegen.decoder_params(SEED)
     z = vaegen.latent(SEED, h, h)
     t = time.time()
     y = oracle.decode(z, p, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
-    print(f"{name}: oracle decode {h}x{h} took {time.time() - t:.1f} s", flush=True)
-    np.savez_compressed(os.path.join(HERE, name), sample=y[:, ::stride, ::stride], stride=stride,
-                        shape=np.array(y.shape), max_abs=np.abs(y).max(), l2=np.sqrt((y * y).sum()),
-                        seed=SEED)
+    print(f"decode_1024: oracle decode {h}x{h} took {time.time() - t:.1f} s", flush=True)
+    c, H, W = y.shape
+    rows, cols = lattice(H), lattice(W)
+    rng = np.random.default_rng(20241)
+    pix = np.stack([rng.integers(0, c, 16384), rng.integers(0, H, 16384), rng.integers(0, W, 16384)], axis=1)
+    np.savez_compressed(os.path.join(HERE, "decode_1024"), rows=rows, cols=cols,
+                        lattice=y[:, rows][:, :, cols], first_row=y[:, 0, :], last_row=y[:, H - 1, :],
+                        first_col=y[:, :, 0], last_col=y[:, :, W - 1], pixels=pix,
+                        pixel_values=y[pix[:, 0], pix[:, 1], pix[:, 2]], shape=np.array(y.shape),
+                        max_abs=np.abs(y).max(), l2=np.sqrt((y * y).sum()), seed=SEED)
 
 
 def stack3d():
@@ -68,10 +87,8 @@ def stack3d():
 
 if __name__ == "__main__":
     keep_heap()
-    which = sys.argv[1:] or ["decode256", "decode1024", "stack3d"]
-    if "decode256" in which:
-        decode(32, 4, "decode_256")
+    which = sys.argv[1:] or ["decode1024", "stack3d"]
     if "decode1024" in which:
-        decode(128, 16, "decode_1024")
+        decode1024()
     if "stack3d" in which:
         stack3d()

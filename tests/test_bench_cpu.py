@@ -94,3 +94,59 @@ def test_committed_counter_summary_names_its_kernel():
     assert float(vals["traffic_bytes_per_launch"]) > 0
     assert len(vals["kernel_source_sha256"]) == 64
     int(vals["kernel_source_sha256"], 16)
+
+
+def test_roofline_of_a_winograd_kernel_counts_executed_products():
+    # 14 launches of the F(4x4) conv at 270.58 GFLOP of direct-conv work in
+    # 0.807 ms each: the MFMA pipes run 36/144 of those multiplies, so the
+    # fraction of the FP32 MFMA peak is 0.533, never above 1
+    k = {"ms": 14 * 0.807, "flops": 14 * 270.582939648e9, "bytes": 14 * 4.84e8, "n": 14}
+    r = bench.roofline("conv3x3_wino4<16,plain>", k, 1, "decode256")
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["flops_per_launch"] == pytest.approx(270.582939648e9 * 36 / 144)
+    assert r["achieved"] == pytest.approx(r["flops_per_launch"] / 0.807e-3 / 1e12)
+    assert r["frac"] == pytest.approx(r["achieved"] / 157.3)
+    assert 0.5 < r["frac"] <= 1.0
+    assert r["direct_equivalent_tflops"] == pytest.approx(r["achieved"] * 4)
+    assert r["launches_per_step"] == 14
+
+
+@pytest.mark.parametrize("name", ["conv3x3_wino4<16,plain>", "conv3x3_wino4<16,up2x>", "conv3x3_wino<16,plain>",
+                                  "conv3x3_mfma<32,plain>", "gemm_mfma"])
+def test_roofline_fraction_never_exceeds_one_at_the_peak(name):
+    # a launch that executes exactly the peak's worth of MFMA work in its time
+    # sits at frac 1, whatever its direct-conv count
+    f = bench.mfma_fraction(name)
+    ms = 1.0
+    direct = 157.3e12 * ms / 1e3 / f
+    r = bench.roofline(name, {"ms": ms, "flops": direct, "bytes": 1.0, "n": 1}, 1, "decode256")
+    assert r["frac"] == pytest.approx(1.0)
+
+
+def test_roofline_of_a_memory_bound_kernel():
+    r = bench.roofline("groupnorm_silu", {"ms": 2.0, "flops": 0.0, "bytes": 2 * 4e9, "n": 2}, 1, "decode1024")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["achieved"] == pytest.approx(4e9 / 1e-3 / 1e9)
+    assert r["frac"] == pytest.approx(r["achieved"] / 8000.0)
+
+
+def test_decode_flops_follow_the_architecture():
+    # per-conv 2 Cin Cout k^2 H W plus attention 8 N c^2 + 4 N^2 c, summed
+    # over the chain; the 1024x1024 total equals the one the decoder's own
+    # per-launch records add up to (10.472 TFLOP)
+    import vaegen
+    p = vaegen.decoder_params(0)
+    assert bench.decode_flops(p, 128, 128) == 10472204009472.0
+    n, c = 32 * 32, 512
+    attn = 8.0 * n * c * c + 4.0 * n * n * c
+    assert bench.decode_flops(p, 32, 32) - attn == pytest.approx(618.0e9, rel=1e-3)
+    # conv FLOPs scale with the latent area
+    a8 = bench.decode_flops(p, 8, 8) - (8.0 * 64 * c * c + 4.0 * 64 * 64 * c)
+    assert bench.decode_flops(p, 32, 32) - attn == pytest.approx(16 * a8)
+
+
+def test_form_fractions():
+    assert bench.form_fraction("winograd_4x4") == 36 / 144
+    assert bench.form_fraction("winograd_4x4", upsample=True) == 25 / 144
+    assert bench.form_fraction("winograd_2x2") == 16 / 36
+    assert bench.form_fraction("implicit_gemm") == 1.0

@@ -277,3 +277,29 @@ def test_decoder3d_pack_and_validation(lib):
     assert lib.vae_decode3d(NULL, FAKE, 2, 8, 8, FAKE, FAKE, 1, NULL) == VAE_ERR_INVALID_ARG
     nb = c_size_t()
     assert lib.vae_decoder3d_workspace_bytes(NULL, 2, 8, 8, byref(nb)) == VAE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("causal3d, shape, match", [
+    (False, (4, 8, 8), "4 channels"),          # a 4-channel latent for a 16-channel conv_in
+    (False, (16, 8), "3 dimensions"),
+    (False, (16, 2, 8, 8), "3 dimensions"),
+    (True, (16, 8, 8), "4 dimensions"),
+    (True, (8, 2, 8, 8), "8 channels"),
+])
+def test_decoder_rejects_a_mismatched_latent_before_any_launch(causal3d, shape, match):
+    # the decoder object is built without the library (no GPU here): the
+    # check runs before any call into it, so a wrong latent never reaches
+    # vae_decode, which takes no channel count and would read past the tensor
+    import torch
+    from diffusion_vae_decoder_amd import api
+
+    d = object.__new__(api.Decoder)
+    d.causal3d = causal3d
+    d.latent_channels = 16
+    d.device = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match=match):
+        d.decode(torch.zeros(shape))
+    # the right shape on the wrong device is refused as well
+    ok = (16, 2, 8, 8) if causal3d else (16, 8, 8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        d.decode(torch.zeros(ok))

@@ -66,6 +66,11 @@ SWEEP = [  # (cin, cout, h, w, k)
     (128, 128, 512, 512, 3),
     (256, 128, 512, 512, 3),
     (256, 128, 512, 512, 1),
+    # the other distinct layer shapes of the 1024 x 1024 decode
+    (512, 512, 256, 256, 3),     # up_blocks.1 resnets
+    (512, 256, 512, 512, 3),     # up_blocks.2.resnets.0.conv1
+    (512, 256, 512, 512, 1),     # its 1x1 shortcut
+    (256, 256, 512, 512, 3),     # up_blocks.2 resnets
 ]
 
 
@@ -110,6 +115,42 @@ def test_upsample_conv_at_decoder_size(api):
     err = sampled_rel_err(g, lambda o, i, j: oracle.conv2d_at(x, wt, b, o, i, j, upsample2x=True),
                           sample_points((256, 1024, 1024), 384, rng))
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("c,h", [(512, 128), (512, 256)])
+def test_upsample_conv_at_other_decoder_sizes(api, c, h):
+    # the first two upsample convs of the 1024 x 1024 decode: 512 channels,
+    # 128x128 -> 256x256 and 256x256 -> 512x512
+    x = vaegen.activation(SEED, f"up{c}.{h}.x", (c, h, h))
+    p = vaegen.conv_params(SEED, f"up{c}.{h}.conv", c, c, 3)
+    wt, b = p[f"up{c}.{h}.conv.weight"], p[f"up{c}.{h}.conv.bias"]
+    y = torch.full((c, 2 * h, 2 * h), float("nan"), device="cuda")
+    api.conv2d(dev(x), dev(wt), dev(b), upsample2x=True, out=y)
+    torch.cuda.synchronize()
+    g = y.cpu().numpy()
+    assert not np.isnan(g).any()
+    rng = np.random.default_rng(c + h)
+    err = sampled_rel_err(g, lambda o, i, j: oracle.conv2d_at(x, wt, b, o, i, j, upsample2x=True),
+                          sample_points((c, 2 * h, 2 * h), 384, rng))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("h,w", [(96, 128), (128, 128)])
+def test_attention_at_decoder_size(api, h, w):
+    # c = 512 over 12288 and 16384 tokens (the 1024 x 1024 decode's mid
+    # attention): whole tiles, so the score and P.V products take their
+    # full-tile paths and P.V is not split along its keys; compared element
+    # by element with the oracle
+    c = 512
+    p = vaegen.attention_params(SEED, "fa", c)
+    x = vaegen.activation(SEED, f"fa.x.{h}", (c, h, w))
+    y = torch.full((c, h, w), float("nan"), device="cuda")
+    api.attention(dev(x), {k: dev(v) for k, v in p.items()}, "fa", out=y)
+    torch.cuda.synchronize()
+    g = y.cpu().numpy().astype(np.float64)
+    assert not np.isnan(g).any()
+    ref = oracle.attention(x, p, "fa")
+    assert float(np.abs(g - ref).max() / np.abs(ref).max()) <= TOL
 
 
 def test_residual_conv_at_decoder_size(api):
