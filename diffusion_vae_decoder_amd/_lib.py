@@ -65,6 +65,8 @@ SIGNATURES = {
     "vae_groupnorm_workspace_bytes": (c_int32, [c_int32, c_int64, POINTER(c_size_t)]),
     "vae_groupnorm_silu": (c_int32, [c_void_p, c_int32, c_int64, POINTER(VaeNorm), c_int32, c_void_p,
                                      c_void_p, c_void_p, c_size_t, c_void_p]),
+    "vae_groupnorm_silu_noalloc": (c_int32, [c_void_p, c_int32, c_int64, POINTER(VaeNorm), c_int32, c_void_p,
+                                             c_void_p, c_void_p]),
     "vae_conv2d_groupnorm_workspace_bytes": (c_int32, [POINTER(VaeConv), c_int32, c_int32, c_int32,
                                                        POINTER(c_size_t)]),
     "vae_conv2d_groupnorm_silu": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(VaeConv), c_int32,

@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import VaeAttn, VaeConv, VaeError, VaeNorm, VaeProfRecord, VaeResnet, VaeUp, VaeWeights, check
 
 __all__ = [
-    "VaeError", "conv2d", "conv_in", "groupnorm_silu", "upsample_nearest2x", "attention",
+    "VaeError", "conv2d", "conv_in", "groupnorm_silu", "groupnorm_silu_noalloc", "upsample_nearest2x", "attention",
     "conv3d_causal", "Decoder", "CONV3X3_ALGORITHMS", "set_conv3x3_algorithm", "get_conv3x3_algorithm",
 ]
 
@@ -148,6 +148,23 @@ def groupnorm_silu(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, sil
     ws = _ws(nb.value, x.device)
     check(lib.vae_groupnorm_silu(x.data_ptr(), c, spatial, byref(norm), int(bool(silu)), _ptr(residual),
                                  y.data_ptr(), _ptr(ws), nb.value, _stream()))
+    return y
+
+
+def groupnorm_silu_noalloc(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, silu: bool = True,
+                           residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """:func:`groupnorm_silu` through the entry point that allocates nothing
+    (its partial sums in the library's static device buffer).  With ``out``
+    given, this call allocates nothing either."""
+    lib = _lib_()
+    _dev(x, "x")
+    c = x.shape[0]
+    norm = _norm(gamma, beta)
+    if residual is not None:
+        _dev(residual, "residual")
+    y = torch.empty_like(x) if out is None else _dev(out, "out")
+    check(lib.vae_groupnorm_silu_noalloc(x.data_ptr(), c, x.numel() // c, byref(norm), int(bool(silu)),
+                                         _ptr(residual), y.data_ptr(), _stream()))
     return y
 
 

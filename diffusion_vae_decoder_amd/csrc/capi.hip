@@ -29,6 +29,31 @@ int32_t hip_status(hipError_t e, const char *what) {
 
 int32_t check_launch(const char *what) { return hip_status(hipGetLastError(), what); }
 
+int32_t check_groupnorm_args(const char *who, const float *x, int c, long long spatial, const vae_norm *norm,
+                             const float *y) {
+    if (!x || !y || !norm || !norm->gamma || !norm->beta) {
+        set_error("%s: NULL pointer", who);
+        return VAE_ERR_INVALID_ARG;
+    }
+    if (c <= 0 || spatial <= 0) {
+        set_error("%s: sizes must be positive", who);
+        return VAE_ERR_INVALID_ARG;
+    }
+    if (norm->channels != c) {
+        set_error("%s: norm has %d channels, tensor %d", who, norm->channels, c);
+        return VAE_ERR_INVALID_ARG;
+    }
+    if (c % 32) {
+        set_error("%s: channels %d not divisible by 32", who, c);
+        return VAE_ERR_UNSUPPORTED;
+    }
+    if ((long long)c * spatial > (1LL << 34)) {
+        set_error("%s: tensor too large", who);
+        return VAE_ERR_UNSUPPORTED;
+    }
+    return VAE_OK;
+}
+
 }  // namespace vae
 
 using namespace vae;
@@ -210,11 +235,8 @@ int32_t vae_groupnorm_workspace_bytes(int32_t c, int64_t spatial, size_t *bytes)
 int32_t vae_groupnorm_silu(const float *x, int32_t c, int64_t spatial, const vae_norm *norm,
                            int32_t apply_silu, const float *residual, float *y, void *ws,
                            size_t ws_bytes, void *stream) {
-    if (!x || !y || !norm || !norm->gamma || !norm->beta) return bad("vae_groupnorm_silu: NULL pointer");
-    if (c <= 0 || spatial <= 0) return bad("vae_groupnorm_silu: sizes must be positive");
-    if (norm->channels != c) return bad("vae_groupnorm_silu: norm has %d channels, tensor %d", norm->channels, c);
-    if (c % 32) return unsupported("vae_groupnorm_silu: channels %d not divisible by 32", c);
-    if ((long long)c * spatial > kMaxElems) return unsupported("vae_groupnorm_silu: tensor too large");
+    int32_t rc = check_groupnorm_args("vae_groupnorm_silu", x, c, spatial, norm, y);
+    if (rc) return rc;
     const size_t need = groupnorm_ws_bytes(c, spatial);
     if (!ws || ws_bytes < need)
         return set_error("vae_groupnorm_silu: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;

@@ -19,6 +19,10 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 void set_error(const char *fmt, ...);
 int32_t hip_status(hipError_t e, const char *what);
 int32_t check_launch(const char *what);
+// Argument checks of the GroupNorm entry points (NULLs, sizes, channel count,
+// c % 32); sets the message under `who` and returns its code.
+int32_t check_groupnorm_args(const char *who, const float *x, int c, long long spatial, const vae_norm *norm,
+                             const float *y);
 
 // ------------------------------------------------------------------ conv
 // Geometry of the implicit-GEMM 3x3 conv: a workgroup computes 128 output

@@ -179,6 +179,20 @@ int32_t vae_groupnorm_silu(const float *x, int32_t c, int64_t spatial, const vae
                            int32_t apply_silu, const float *residual, float *y,
                            void *ws, size_t ws_bytes, void *stream);
 
+/* vae_groupnorm_silu without a workspace argument, for callers that cannot
+ * allocate memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels and results as
+ * vae_groupnorm_silu; its partial sums live in a static device buffer of the
+ * library (36 KiB per GPU, held until the process ends; every GroupNorm
+ * needs at most 33,024 bytes of it, and a larger need is refused with
+ * VAE_ERR_UNSUPPORTED).  The buffer is looked up on the first call on each
+ * device (the current device) and shared by every later call on that GPU:
+ * calls that overlap in time on one GPU race on it, so callers serialise
+ * them (one stream, or events).  Nothing is allocated, by the library or
+ * through torch. */
+int32_t vae_groupnorm_silu_noalloc(const float *x, int32_t c, int64_t spatial, const vae_norm *norm,
+                                   int32_t apply_silu, const float *residual, float *y, void *stream);
+
 /* Workspace for vae_conv2d_groupnorm_silu (same arguments as
  * vae_conv2d_workspace_bytes; kernel 3, out_channels % 32 == 0). */
 int32_t vae_conv2d_groupnorm_workspace_bytes(const vae_conv *conv, int32_t h, int32_t w, int32_t upsample2x,
