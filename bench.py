@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--conv3x3", default=None,
                     help="form of the 3x3 convs (winograd_2x2, implicit_gemm, winograd_4x4); default: the library's")
+    ap.add_argument("--layer-table", default=None,
+                    help="write the timed decodes' per-layer average launch times (JSON) to this file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the decodes, run one plain device copy of this many MiB "
                          "(reference dispatch for calibrating HBM byte counters)")
@@ -510,6 +512,13 @@ def main():
     dec.set_profiling(False)
     ms_per_step = wall * 1e3 / args.steps
 
+    if args.layer_table:
+        layers = {}
+        for r in recs:
+            e = layers.setdefault((r["layer"], r["kernel"]), {"ms": 0.0, "flops": r["flops"], "bytes": r["bytes"]})
+            e["ms"] += r["ms"] / args.steps
+        with open(args.layer_table, "w") as f:
+            json.dump([{"layer": l, "kernel": k, **v} for (l, k), v in layers.items()], f, indent=0)
     flops_per_step = sum(r["flops"] for r in recs) / args.steps
     by_kernel = {}
     for r in recs:

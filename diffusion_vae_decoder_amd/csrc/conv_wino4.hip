@@ -504,11 +504,26 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
     // rows 2 and 3) and adds the partner's share to its own rows.
     const long long fo = (long long)frame * p.out_fstride;
     const bool rowvec = (p.W & 3) == 0 && X0 < p.W;   // 4 outputs of a row in range, 16-byte aligned
+    const bool full = Y0 + 2 * H + 1 < p.H && X0 + 3 < p.W;   // the lane's two rows of 4 outputs in range
     // [receiving half][i][row][col][lane]: a U buffer, or the upsampled kernel's own exchange area
     float *xb = UP ? lxb + wtg * (2 * 4 * 8 * 64) : reinterpret_cast<float *>(wtg == 0 ? lu0 : lu1);
     float gs[kW4RB][3];   // per row block: (count, mean, sum of squared deviations) of the lane's outputs
 #pragma unroll
     for (int b = 0; b < kW4RB; ++b) {
+        // the row block's residual rows are requested before its output
+        // transform, so their latency overlaps that arithmetic
+        floatx4 r4[4][2];
+        if (RES && !SPLIT && rowvec) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (cb * kW4RB + b) * kW4Blk + 4 * g4 + i;
+                const long long cbase = (long long)(o < p.cout ? o : p.cout - 1) * p.out_cstride + fo;
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+                    r4[i][a] = *reinterpret_cast<const floatx4 *>(p.res + cbase +
+                                                                 (long long)min(Y0 + 2 * H + a, p.H - 1) * p.W + X0);
+            }
+        }
         float y[4][4][4];   // [i][row][col]
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -550,9 +565,8 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
                 for (int x = 0; x < 4; ++x) v[a][x] = y[i][2 * H + a][x] + bo;
                 if (rowvec) {
                     if (RES && !SPLIT) {
-                        const floatx4 r4 = *reinterpret_cast<const floatx4 *>(p.res + rb + X0);
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) v[a][x] += r4[x];
+                        for (int x = 0; x < 4; ++x) v[a][x] += r4[i][a][x];
                     }
                     if (rv) {
                         float *dst = SPLIT ? p.part + split * p.part_stride + rb + X0 : p.y + rb + X0;
@@ -572,26 +586,42 @@ __device__ __attribute__((always_inline)) inline void w4_body(const WParams &p, 
                 }
             }
             if (!SPLIT && p.gn_rec) {
-                // the channel's valid outputs among the wave's rows of the tile
-                float cnt = 0.f, sum = 0.f;
+                // the channel's valid outputs among the wave's rows of the tile:
+                // all 8 of them away from the bottom and right edges
+                float cnt = 0.f, sum = 0.f, m2 = 0.f, mean = 0.f;
+                if (ovalid && full) {
+                    cnt = 8.f;
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
+                    for (int a = 0; a < 2; ++a)
 #pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        if (ovalid && Y0 + 2 * H + a < p.H && X0 + x < p.W) {
-                            cnt += 1.f;
-                            sum += v[a][x];
-                        }
-                const float mean = cnt > 0.f ? sum / cnt : 0.f;
-                float m2 = 0.f;
+                        for (int x = 0; x < 4; ++x) sum += v[a][x];
+                    mean = sum * 0.125f;
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
+                    for (int a = 0; a < 2; ++a)
 #pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        if (ovalid && Y0 + 2 * H + a < p.H && X0 + x < p.W) {
+                        for (int x = 0; x < 4; ++x) {
                             const float dv = v[a][x] - mean;
                             m2 += dv * dv;
                         }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < 2; ++a)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            if (ovalid && Y0 + 2 * H + a < p.H && X0 + x < p.W) {
+                                cnt += 1.f;
+                                sum += v[a][x];
+                            }
+                    mean = cnt > 0.f ? sum * __builtin_amdgcn_rcpf(cnt) : 0.f;
+#pragma unroll
+                    for (int a = 0; a < 2; ++a)
+#pragma unroll
+                        for (int x = 0; x < 4; ++x)
+                            if (ovalid && Y0 + 2 * H + a < p.H && X0 + x < p.W) {
+                                const float dv = v[a][x] - mean;
+                                m2 += dv * dv;
+                            }
+                }
                 wino_chan_merge(gs[b], cnt, mean, m2);
             }
         }

@@ -74,7 +74,9 @@ __device__ __attribute__((always_inline)) inline void wino_dma16(__amdgpu_buffer
 __device__ __attribute__((always_inline)) inline void wino_chan_merge(float (&a)[3], float nb, float mb, float qb) {
     const float nt = a[0] + nb;
     const float delta = mb - a[1];
-    const float fb = nt > 0.f ? nb / nt : 0.f;
+    // counts are whole numbers: a hardware reciprocal (1 ulp) instead of a
+    // full-precision division, which costs about ten instructions
+    const float fb = nt > 0.f ? nb * __builtin_amdgcn_rcpf(nt) : 0.f;
     a[2] = (a[2] + qb) + delta * delta * a[0] * fb;
     a[1] = a[1] + delta * fb;
     a[0] = nt;
