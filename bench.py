@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--conv3x3", default=None,
                     help="form of the 3x3 convs (winograd_2x2, implicit_gemm, winograd_4x4); default: the library's")
+    ap.add_argument("--attention", default=None, choices=["split_softmax", "streaming"],
+                    help="form of the decoder's mid-block attention; default: the library's")
     ap.add_argument("--layer-table", default=None,
                     help="write the timed decodes' per-layer average launch times (JSON) to this file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -485,6 +487,8 @@ def main():
     # first call: weight packing (weights already on the device), then the first decode
     t0 = time.perf_counter()
     dec = api.Decoder(dev_params, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    if args.attention:
+        dec.set_attention(args.attention)
     torch.cuda.synchronize()
     create_ms = (time.perf_counter() - t0) * 1e3
     z = torch.from_numpy(vaegen.latent(args.seed, h, h)).cuda()
@@ -559,7 +563,8 @@ def main():
         "data": "synthetic (seeded SplitMix64 latent N(0,1) and weights at the stated init; no trained weights)",
         "config": {"workload": f"FLUX-class AutoencoderKL decode, latent [16,{h},{h}] -> RGB [3,{ho},{wo}], "
                                "batch 1, f32 NCHW", "latent": [16, h, h], "rgb": [co, ho, wo],
-                   "flops_per_decode": flops_per_step, "conv3x3_form": api.get_conv3x3_algorithm()},
+                   "flops_per_decode": flops_per_step, "conv3x3_form": api.get_conv3x3_algorithm(),
+                   "attention_form": dec.get_attention()},
         "conv3x3": {"ms_per_step": conv_ms / args.steps, "direct_equivalent_tflops": conv_fl / (conv_ms / 1e3) / 1e12,
                     "mfma_executed_tflops": cr["mfma_executed_tflops"], "frac_fp32_mfma_peak": cr["frac_fp32_mfma_peak"]},
         "roofline": roof,

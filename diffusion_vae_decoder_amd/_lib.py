@@ -16,7 +16,7 @@ VAE_ERR_INVALID_ARG = -1
 VAE_ERR_UNSUPPORTED = -2
 VAE_ERR_WORKSPACE = -3
 VAE_ERR_HIP = -4
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class VaeConv(ctypes.Structure):
@@ -76,6 +76,9 @@ SIGNATURES = {
     "vae_attention_workspace_bytes": (c_int32, [c_int32, c_int32, c_int32, POINTER(c_size_t)]),
     "vae_attention": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(VaeAttn), c_void_p,
                                 c_void_p, c_size_t, c_void_p]),
+    "vae_attention_streaming_workspace_bytes": (c_int32, [c_int32, c_int32, c_int32, POINTER(c_size_t)]),
+    "vae_attention_streaming": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(VaeAttn), c_void_p,
+                                          c_void_p, c_size_t, c_void_p]),
     "vae_conv3d_causal_workspace_bytes": (c_int32, [POINTER(VaeConv), c_int32, c_int32, c_int32,
                                                     POINTER(c_size_t)]),
     "vae_conv3d_causal": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(VaeConv),
@@ -94,6 +97,8 @@ SIGNATURES = {
     "vae_decoder_destroy": (None, [c_void_p]),
     "vae_decoder_set_groupnorm_fusion": (c_int32, [c_void_p, c_int32]),
     "vae_decoder_set_graph": (c_int32, [c_void_p, c_int32]),
+    "vae_decoder_set_attention": (c_int32, [c_void_p, c_int32]),
+    "vae_decoder_get_attention": (c_int32, [c_void_p]),
     "vae_set_conv3x3_algorithm": (c_int32, [c_int32]),
     "vae_get_conv3x3_algorithm": (c_int32, []),
     "vae_decoder_set_profiling": (c_int32, [c_void_p, c_int32]),

@@ -19,12 +19,15 @@ from ._lib import VaeAttn, VaeConv, VaeError, VaeNorm, VaeProfRecord, VaeResnet,
 
 __all__ = [
     "VaeError", "conv2d", "conv_in", "groupnorm_silu", "groupnorm_silu_noalloc", "upsample_nearest2x", "attention",
+    "attention_streaming", "ATTENTION_FORMS",
     "conv3d_causal", "Decoder", "CONV3X3_ALGORITHMS", "set_conv3x3_algorithm", "get_conv3x3_algorithm",
 ]
 
 # Forms of the 3x3 convolutions (vae_set_conv3x3_algorithm): Winograd
 # F(2x2, 3x3), the implicit GEMM of the direct conv, Winograd F(4x4, 3x3).
 CONV3X3_ALGORITHMS = {"winograd_2x2": 0, "implicit_gemm": 1, "winograd_4x4": 2}
+# Forms of the decoder's mid-block attention (vae_decoder_set_attention).
+ATTENTION_FORMS = {"split_softmax": 0, "streaming": 1}
 
 
 def set_conv3x3_algorithm(name: str) -> None:
@@ -203,6 +206,14 @@ def upsample_nearest2x(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> t
     return y
 
 
+def _attn(p: Dict[str, torch.Tensor], prefix: str) -> VaeAttn:
+    return VaeAttn(_norm(p[prefix + ".group_norm.weight"], p[prefix + ".group_norm.bias"]),
+                   _conv(p[prefix + ".to_q.weight"], p[prefix + ".to_q.bias"]),
+                   _conv(p[prefix + ".to_k.weight"], p[prefix + ".to_k.bias"]),
+                   _conv(p[prefix + ".to_v.weight"], p[prefix + ".to_v.bias"]),
+                   _conv(p[prefix + ".to_out.0.weight"], p[prefix + ".to_out.0.bias"]))
+
+
 def attention(x: torch.Tensor, p: Dict[str, torch.Tensor], prefix: str,
               out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Mid-block attention; ``p`` holds diffusers-named tensors under ``prefix``
@@ -210,16 +221,28 @@ def attention(x: torch.Tensor, p: Dict[str, torch.Tensor], prefix: str,
     lib = _lib_()
     _dev(x, "x")
     c, h, w = x.shape
-    a = VaeAttn(_norm(p[prefix + ".group_norm.weight"], p[prefix + ".group_norm.bias"]),
-                _conv(p[prefix + ".to_q.weight"], p[prefix + ".to_q.bias"]),
-                _conv(p[prefix + ".to_k.weight"], p[prefix + ".to_k.bias"]),
-                _conv(p[prefix + ".to_v.weight"], p[prefix + ".to_v.bias"]),
-                _conv(p[prefix + ".to_out.0.weight"], p[prefix + ".to_out.0.bias"]))
+    a = _attn(p, prefix)
     y = _out(out, (c, h, w), x.device)
     nb = c_size_t()
     check(lib.vae_attention_workspace_bytes(c, h, w, byref(nb)))
     ws = _ws(nb.value, x.device)
     check(lib.vae_attention(x.data_ptr(), c, h, w, byref(a), y.data_ptr(), _ptr(ws), nb.value, _stream()))
+    return y
+
+
+def attention_streaming(x: torch.Tensor, p: Dict[str, torch.Tensor], prefix: str,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """:func:`attention` with a streaming softmax (no score matrix in memory);
+    128, 256 or 512 channels."""
+    lib = _lib_()
+    _dev(x, "x")
+    c, h, w = x.shape
+    a = _attn(p, prefix)
+    y = _out(out, (c, h, w), x.device)
+    nb = c_size_t()
+    check(lib.vae_attention_streaming_workspace_bytes(c, h, w, byref(nb)))
+    ws = _ws(nb.value, x.device)
+    check(lib.vae_attention_streaming(x.data_ptr(), c, h, w, byref(a), y.data_ptr(), _ptr(ws), nb.value, _stream()))
     return y
 
 
@@ -366,6 +389,15 @@ class Decoder:
     def set_groupnorm_fusion(self, on: bool) -> None:
         """Apply GroupNorm + SiLU while each conv loads its input (off by default)."""
         check(self._lib.vae_decoder_set_groupnorm_fusion(self._h, int(bool(on))))
+
+    def set_attention(self, form: str) -> None:
+        """The mid-block attention's form: "split_softmax" (default) or "streaming"."""
+        if form not in ATTENTION_FORMS:
+            raise ValueError(f"unknown attention form {form!r}; expected one of {sorted(ATTENTION_FORMS)}")
+        check(self._lib.vae_decoder_set_attention(self._h, ATTENTION_FORMS[form]))
+
+    def get_attention(self) -> str:
+        return {v: k for k, v in ATTENTION_FORMS.items()}[self._lib.vae_decoder_get_attention(self._h)]
 
     def set_graph(self, on: bool) -> None:
         """Replay decodes with the same buffers and sizes from a captured HIP graph."""

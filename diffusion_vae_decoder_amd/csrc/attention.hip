@@ -141,4 +141,99 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
     return launch_gemm(g, s);
 }
 
+// ---------------------------------------------------------------------------
+// The streaming-softmax form (attention_flash.hip): the scores never reach
+// memory.  Workspace: xn [c, n] | Q [c, n] | V [c, n] | K^T [n, c] | O [c, n] |
+// per-range outputs [R][c][n] and (m, l) [R][n] (R > 1) | GroupNorm partials |
+// K-split partial sums of the projections.
+//
+// K^T is produced without the key bias: it adds q . b_k to every score of
+// query q, a per-query constant that the softmax removes exactly.
+
+namespace {
+size_t flash_split_floats(int c, long long n) {
+    size_t f = gemm_partial_floats(c, (int)n, c, false);                     // Q, V, output projection
+    const size_t kt = gemm_partial_floats((int)n, c, c, false);              // K^T
+    return f > kt ? f : kt;
+}
+}  // namespace
+
+size_t attention_streaming_ws_bytes(int c, long long n) {
+    const int R = attention_flash_ranges(n);
+    size_t b = 0;
+    b += 5 * align256((size_t)c * n * 4);                         // xn, Q, V, K^T, O
+    if (R > 1) b += align256((size_t)R * c * n * 4) + align256((size_t)R * n * 8);
+    b += align256(groupnorm_ws_bytes(c, n));
+    b += align256(flash_split_floats(c, n) * 4);
+    return b;
+}
+
+int32_t launch_attention_streaming(const float *x, int c, int h, int w, const float *gn_gamma,
+                                   const float *gn_beta, const float *wqkv, const float *bqkv,
+                                   const float *wo, const float *bo, float *y, void *ws, hipStream_t s) {
+    const long long n = (long long)h * w;
+    if (!attention_flash_supported(c)) {
+        set_error("attention (streaming): %d channels; supported: 128, 256, 512", c);
+        return VAE_ERR_UNSUPPORTED;
+    }
+    if ((long long)c * n * 4 >= (1LL << 31)) {
+        set_error("attention (streaming): %lld tokens of %d channels exceed 2 GiB per operand", n, c);
+        return VAE_ERR_UNSUPPORTED;
+    }
+    const int R = attention_flash_ranges(n);
+    const size_t a = align256((size_t)c * n * 4);
+    char *p = static_cast<char *>(ws);
+    float *xn = reinterpret_cast<float *>(p);
+    float *Q = reinterpret_cast<float *>(p + a);
+    float *V = reinterpret_cast<float *>(p + 2 * a);
+    float *KT = reinterpret_cast<float *>(p + 3 * a);
+    float *O = reinterpret_cast<float *>(p + 4 * a);
+    p += 5 * a;
+    float *Op = nullptr, *ml = nullptr;
+    if (R > 1) {
+        Op = reinterpret_cast<float *>(p);
+        p += align256((size_t)R * c * n * 4);
+        ml = reinterpret_cast<float *>(p);
+        p += align256((size_t)R * n * 8);
+    }
+    void *gnws = p;
+    p += align256(groupnorm_ws_bytes(c, n));
+    float *part = reinterpret_cast<float *>(p);
+
+    int32_t rc = launch_groupnorm(x, c, n, gn_gamma, gn_beta, /*silu=*/0, nullptr, xn, gnws, s);
+    if (rc != VAE_OK) return rc;
+    const size_t cc = (size_t)c * c;
+    // Q = Wq xn + bq and V = Wv xn + bv, channel-major [c, n]
+    for (int which : {0, 2}) {
+        GemmLaunch g{};
+        g.A = wqkv + which * cc; g.lda = c; g.a_km = 0;
+        g.B = xn; g.ldb = n; g.b_nk = 0;
+        g.bias = bqkv + (size_t)which * c;
+        g.C = which == 0 ? Q : V; g.ldc = n;
+        g.M = c; g.N = (int)n; g.K = c; g.alpha = 1.f;
+        g.part = part;
+        if ((rc = launch_gemm(g, s)) != VAE_OK) return rc;
+    }
+    // K^T[t, ch] = sum_k xn[k, t] Wk[ch, k], token-major [n, c]
+    {
+        GemmLaunch g{};
+        g.A = xn; g.lda = n; g.a_km = 1;
+        g.B = wqkv + cc; g.ldb = c; g.b_nk = 1;
+        g.C = KT; g.ldc = c;
+        g.M = (int)n; g.N = c; g.K = c; g.alpha = 1.f;
+        g.part = part;
+        if ((rc = launch_gemm(g, s)) != VAE_OK) return rc;
+    }
+    if ((rc = launch_attention_flash_core(Q, KT, V, O, Op, ml, c, n, s)) != VAE_OK) return rc;
+    // y = x + Wo O + bo
+    GemmLaunch g{};
+    g.A = wo; g.lda = c; g.a_km = 0;
+    g.B = O; g.ldb = n; g.b_nk = 0;
+    g.bias = bo; g.R = x; g.ldr = n;
+    g.C = y; g.ldc = n;
+    g.M = c; g.N = (int)n; g.K = c; g.alpha = 1.f;
+    g.part = part;
+    return launch_gemm(g, s);
+}
+
 }  // namespace vae

@@ -337,38 +337,85 @@ int32_t vae_attention_workspace_bytes(int32_t c, int32_t h, int32_t w, size_t *b
     return VAE_OK;
 }
 
-int32_t vae_attention(const float *x, int32_t c, int32_t h, int32_t w, const vae_attn *attn, float *y,
-                      void *ws, size_t ws_bytes, void *stream) {
-    if (!x || !y || !attn) return bad("vae_attention: NULL pointer");
-    int32_t rc = check_plane("vae_attention", c, h, w);
+namespace {
+// Checks shared by the two attention entry points; `streaming` adds the
+// channel counts the streaming kernel supports.
+int32_t check_attention(const char *who, const float *x, int32_t c, int32_t h, int32_t w, const vae_attn *attn,
+                        const float *y, bool streaming) {
+    if (!x || !y || !attn) return bad("%s: NULL pointer", who);
+    int32_t rc = check_plane(who, c, h, w);
     if (rc) return rc;
-    if ((long long)h * w > (1LL << 31) / 2) return unsupported("vae_attention: too many tokens");
-    if (c % 32) return unsupported("vae_attention: channels %d not divisible by 32", c);
+    if ((long long)h * w > (1LL << 31) / 2) return unsupported("%s: too many tokens", who);
+    if (c % 32) return unsupported("%s: channels %d not divisible by 32", who, c);
+    if (streaming && !attention_flash_supported(c))
+        return unsupported("%s: %d channels; the streaming form supports 128, 256 and 512", who, c);
+    if (streaming && (long long)c * h * w * 4 >= (1LL << 31))
+        return unsupported("%s: %d x %d tokens of %d channels exceed 2 GiB per operand", who, h, w, c);
     if (!attn->norm.gamma || !attn->norm.beta || attn->norm.channels != c)
-        return bad("vae_attention: norm missing or has %d channels (want %d)", attn->norm.channels, c);
+        return bad("%s: norm missing or has %d channels (want %d)", who, attn->norm.channels, c);
     const vae_conv *lin[4] = {&attn->q, &attn->k, &attn->v, &attn->out};
     for (int i = 0; i < 4; ++i) {
-        if ((rc = check_conv("vae_attention", lin[i], 1))) return rc;
+        if ((rc = check_conv(who, lin[i], 1))) return rc;
         if (lin[i]->in_channels != c || lin[i]->out_channels != c)
-            return bad("vae_attention: projection %d is %dx%d, want %dx%d", i, lin[i]->out_channels,
-                       lin[i]->in_channels, c, c);
+            return bad("%s: projection %d is %dx%d, want %dx%d", who, i, lin[i]->out_channels, lin[i]->in_channels,
+                       c, c);
     }
-    if (x == y) return bad("vae_attention: y may not alias x");
+    if (x == y) return bad("%s: y may not alias x", who);
+    return VAE_OK;
+}
+
+// q, k, v weights and biases concatenated at `dst` ([3c, c] then [3c]).
+int32_t copy_qkv(const vae_attn *attn, int c, float *wqkv, hipStream_t s, const char *who) {
+    float *bqkv = wqkv + (size_t)3 * c * c;
+    const vae_conv *lin[3] = {&attn->q, &attn->k, &attn->v};
+    const size_t cc = (size_t)c * c * 4;
+    int32_t rc;
+    for (int i = 0; i < 3; ++i) {
+        if ((rc = hip_status(hipMemcpyAsync(wqkv + (size_t)i * c * c, lin[i]->weight, cc, hipMemcpyDeviceToDevice, s), who))) return rc;
+        if ((rc = hip_status(hipMemcpyAsync(bqkv + (size_t)i * c, lin[i]->bias, (size_t)c * 4, hipMemcpyDeviceToDevice, s), who))) return rc;
+    }
+    return VAE_OK;
+}
+}  // namespace
+
+int32_t vae_attention(const float *x, int32_t c, int32_t h, int32_t w, const vae_attn *attn, float *y,
+                      void *ws, size_t ws_bytes, void *stream) {
+    int32_t rc = check_attention("vae_attention", x, c, h, w, attn, y, false);
+    if (rc) return rc;
     size_t need = 0;
     vae_attention_workspace_bytes(c, h, w, &need);
     if (!ws || ws_bytes < need)
         return set_error("vae_attention: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t base = attention_ws_bytes(c, (long long)h * w);
-    float *wqkv = reinterpret_cast<float *>(static_cast<char *>(ws) + base);
-    float *bqkv = wqkv + (size_t)3 * c * c;
-    const size_t cc = (size_t)c * c * 4;
-    for (int i = 0; i < 3; ++i) {
-        if ((rc = hip_status(hipMemcpyAsync(wqkv + (size_t)i * c * c, lin[i]->weight, cc, hipMemcpyDeviceToDevice, s), "vae_attention: copy"))) return rc;
-        if ((rc = hip_status(hipMemcpyAsync(bqkv + (size_t)i * c, lin[i]->bias, (size_t)c * 4, hipMemcpyDeviceToDevice, s), "vae_attention: copy"))) return rc;
-    }
-    return launch_attention(x, c, h, w, attn->norm.gamma, attn->norm.beta, wqkv, bqkv, attn->out.weight,
-                            attn->out.bias, y, ws, s);
+    float *wqkv = reinterpret_cast<float *>(static_cast<char *>(ws) + attention_ws_bytes(c, (long long)h * w));
+    if ((rc = copy_qkv(attn, c, wqkv, s, "vae_attention: copy"))) return rc;
+    return launch_attention(x, c, h, w, attn->norm.gamma, attn->norm.beta, wqkv, wqkv + (size_t)3 * c * c,
+                            attn->out.weight, attn->out.bias, y, ws, s);
+}
+
+int32_t vae_attention_streaming_workspace_bytes(int32_t c, int32_t h, int32_t w, size_t *bytes) {
+    if (!bytes) return bad("vae_attention_streaming_workspace_bytes: bytes is NULL");
+    int32_t rc = check_plane("vae_attention_streaming_workspace_bytes", c, h, w);
+    if (rc) return rc;
+    if (!attention_flash_supported(c))
+        return unsupported("vae_attention_streaming_workspace_bytes: %d channels; supported: 128, 256, 512", c);
+    *bytes = attention_streaming_ws_bytes(c, (long long)h * w) + (((size_t)3 * c * c + 3 * c) * 4 + 512);
+    return VAE_OK;
+}
+
+int32_t vae_attention_streaming(const float *x, int32_t c, int32_t h, int32_t w, const vae_attn *attn, float *y,
+                                void *ws, size_t ws_bytes, void *stream) {
+    int32_t rc = check_attention("vae_attention_streaming", x, c, h, w, attn, y, true);
+    if (rc) return rc;
+    size_t need = 0;
+    vae_attention_streaming_workspace_bytes(c, h, w, &need);
+    if (!ws || ws_bytes < need)
+        return set_error("vae_attention_streaming: workspace %zu bytes < %zu", ws_bytes, need), VAE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *wqkv = reinterpret_cast<float *>(static_cast<char *>(ws) + attention_streaming_ws_bytes(c, (long long)h * w));
+    if ((rc = copy_qkv(attn, c, wqkv, s, "vae_attention_streaming: copy"))) return rc;
+    return launch_attention_streaming(x, c, h, w, attn->norm.gamma, attn->norm.beta, wqkv, wqkv + (size_t)3 * c * c,
+                                      attn->out.weight, attn->out.bias, y, ws, s);
 }
 
 int32_t vae_conv3d_causal_workspace_bytes(const vae_conv *conv, int32_t t, int32_t h, int32_t w,

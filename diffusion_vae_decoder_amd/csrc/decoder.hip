@@ -235,6 +235,7 @@ struct vae_decoder {
     int kt = 1;              // 3: the causal 3-D decoder
     bool direct_out = false; // conv_out kept raw for the direct kernel
     bool gn_fused = false;   // GroupNorm + SiLU applied while the consuming conv loads its input
+    int attn_form = VAE_ATTENTION_SPLIT_SOFTMAX;
     // HIP-graph replay of the decode's launch sequence (vae_decoder_set_graph)
     struct Graph {
         bool on = false;
@@ -246,6 +247,7 @@ struct vae_decoder {
         int T = 0, h = 0, w = 0;
         hipStream_t stream = nullptr;
         bool gn_fused = false;
+        int attn_form = 0;
     } graph;
     // profiling
     bool profiling = false;
@@ -319,7 +321,8 @@ Plan plan_for(const vae_decoder *d, int T, int h, int w) {
         part(r.c2, H, W);
     };
     res(d->mid0);
-    p.attn = attention_ws_bytes(d->attn.c, (long long)T * H * W);
+    p.attn = d->attn_form == VAE_ATTENTION_STREAMING ? attention_streaming_ws_bytes(d->attn.c, (long long)T * H * W)
+                                                     : attention_ws_bytes(d->attn.c, (long long)T * H * W);
     res(d->mid1);
     for (const DUp &u : d->ups) {
         for (const DRes &r : u.res) res(r);
@@ -615,11 +618,18 @@ int32_t run_chain(vae_decoder *d, const float *latent, int T, int h, int w, floa
     if (r.rc == VAE_OK) {
         // tokens: the T*H*W positions, row-major over (t, y, x)
         const double n = (double)T * H * W, c = d->attn.c;
-        ProfEntry *e = r.begin("attention", "mid_block.attentions.0", 8.0 * n * c * c + 4.0 * n * n * c,
-                               4.0 * (2.0 * c * n + 2.0 * n * n));
+        const bool streaming = d->attn_form == VAE_ATTENTION_STREAMING;
+        // algorithmic bytes: the input read and the output written, plus (split
+        // softmax) the score matrix written and read once
+        ProfEntry *e = r.begin(streaming ? "attention_streaming" : "attention", "mid_block.attentions.0",
+                               8.0 * n * c * c + 4.0 * n * n * c,
+                               4.0 * (2.0 * c * n + (streaming ? 0.0 : 2.0 * n * n)));
         if (r.rc == VAE_OK) {
-            r.rc = launch_attention(b.X, d->attn.c, T * H, W, d->attn.n.g, d->attn.n.b, d->attn.wqkv, d->attn.bqkv,
-                                    d->attn.wo, d->attn.bo, b.Y, b.attn, r.s);
+            r.rc = streaming ? launch_attention_streaming(b.X, d->attn.c, T * H, W, d->attn.n.g, d->attn.n.b,
+                                                          d->attn.wqkv, d->attn.bqkv, d->attn.wo, d->attn.bo, b.Y,
+                                                          b.attn, r.s)
+                             : launch_attention(b.X, d->attn.c, T * H, W, d->attn.n.g, d->attn.n.b, d->attn.wqkv,
+                                                d->attn.bqkv, d->attn.wo, d->attn.bo, b.Y, b.attn, r.s);
             r.end(e);
         }
     }
@@ -685,7 +695,8 @@ int32_t decode_t(vae_decoder *d, const float *latent, int T, int h, int w, float
     }
     if (!graph) return run_chain(d, latent, T, h, w, rgb, ws, stream);
     const bool hit = g.exec && g.latent == latent && g.rgb == rgb && g.ws == ws && g.ws_bytes == ws_bytes &&
-                     g.T == T && g.h == h && g.w == w && g.stream == s && g.gn_fused == d->gn_fused;
+                     g.T == T && g.h == h && g.w == w && g.stream == s && g.gn_fused == d->gn_fused &&
+                     g.attn_form == d->attn_form;
     if (!hit) {
         if (g.exec) {
             (void)hipGraphExecDestroy(g.exec);
@@ -713,6 +724,7 @@ int32_t decode_t(vae_decoder *d, const float *latent, int T, int h, int w, float
         g.w = w;
         g.stream = s;
         g.gn_fused = d->gn_fused;
+        g.attn_form = d->attn_form;
     }
     return hip_status(hipGraphLaunch(g.exec, s), "hipGraphLaunch");
 }
@@ -817,6 +829,19 @@ int32_t vae_decoder_set_groupnorm_fusion(vae_decoder *d, int32_t on) {
     d->gn_fused = on != 0;
     return VAE_OK;
 }
+
+int32_t vae_decoder_set_attention(vae_decoder *d, int32_t form) {
+    if (!d) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_set_attention: NULL decoder");
+    if (form != VAE_ATTENTION_SPLIT_SOFTMAX && form != VAE_ATTENTION_STREAMING)
+        return fail(VAE_ERR_INVALID_ARG, "vae_decoder_set_attention: unknown form %d", form);
+    if (form == VAE_ATTENTION_STREAMING && !attention_flash_supported(d->attn.c))
+        return fail(VAE_ERR_UNSUPPORTED, "vae_decoder_set_attention: the streaming form supports 128, 256 or 512 "
+                                         "channels, the attention has %d", d->attn.c);
+    d->attn_form = form;
+    return VAE_OK;
+}
+
+int32_t vae_decoder_get_attention(const vae_decoder *d) { return d ? d->attn_form : VAE_ERR_INVALID_ARG; }
 
 int32_t vae_decoder_set_profiling(vae_decoder *d, int32_t on) {
     if (!d) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_set_profiling: NULL decoder");

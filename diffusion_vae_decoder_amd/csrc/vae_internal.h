@@ -180,4 +180,17 @@ int32_t launch_attention(const float *x, int c, int h, int w, const float *gn_ga
                          const float *gn_beta, const float *wqkv, const float *bqkv,
                          const float *wo, const float *bo, float *y, void *ws, hipStream_t s);
 
+// The streaming-softmax form of the same attention (attention_flash.hip):
+// c in {32, 64, 128, 256, 512}; the key-range count it splits n tokens into;
+// the core on Q, V [c, n] and K^T [n, c] (Op/ml: per-range partials, used when
+// the range count is above 1); and the whole layer.
+bool attention_flash_supported(int c);
+int attention_flash_ranges(long long n);
+int32_t launch_attention_flash_core(const float *Q, const float *KT, const float *V, float *O, float *Op,
+                                    float *ml, int c, long long n, hipStream_t s);
+size_t attention_streaming_ws_bytes(int c, long long n);
+int32_t launch_attention_streaming(const float *x, int c, int h, int w, const float *gn_gamma,
+                                   const float *gn_beta, const float *wqkv, const float *bqkv,
+                                   const float *wo, const float *bo, float *y, void *ws, hipStream_t s);
+
 }  // namespace vae

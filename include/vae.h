@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 7
+#define VAE_ABI_VERSION 8
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -228,6 +228,19 @@ int32_t vae_attention_workspace_bytes(int32_t c, int32_t h, int32_t w, size_t *b
 int32_t vae_attention(const float *x, int32_t c, int32_t h, int32_t w, const vae_attn *attn,
                       float *y, void *ws, size_t ws_bytes, void *stream);
 
+/* The same attention with a streaming softmax (VaeAttnRef; the online softmax
+ * of Milakov and Gimelshein, 2018): the scores of a query stay in the
+ * registers of the wave that computes them, so the [h*w, h*w] score matrix is
+ * never formed in memory, and the workspace holds only the normalised input,
+ * q, v, k (token-major), the attention output and, when the keys are split
+ * into ranges to fill the GPU, per-range partial outputs.  Same arguments and
+ * results (up to rounding) as vae_attention; c must be 128, 256 or 512
+ * (VAE_ERR_UNSUPPORTED otherwise).  The key bias is not applied: it adds one
+ * constant to all scores of a query, which the softmax removes exactly. */
+int32_t vae_attention_streaming_workspace_bytes(int32_t c, int32_t h, int32_t w, size_t *bytes);
+int32_t vae_attention_streaming(const float *x, int32_t c, int32_t h, int32_t w, const vae_attn *attn,
+                                float *y, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace for vae_conv3d_causal on [cin, t, h, w]: the repacked 3x3x3
  * weights (and split-K partial sums for small shapes). */
 int32_t vae_conv3d_causal_workspace_bytes(const vae_conv *conv, int32_t t, int32_t h, int32_t w,
@@ -301,6 +314,20 @@ void vae_decoder_destroy(vae_decoder *d);
  * has more than 512 input channels, or if the decoder's 3x3 convs were
  * packed in the F(4x4) Winograd form (VAE_CONV3X3_WINOGRAD_4X4). */
 int32_t vae_decoder_set_groupnorm_fusion(vae_decoder *d, int32_t on);
+
+/* The form of the decoder's mid-block attention:
+ *   VAE_ATTENTION_SPLIT_SOFTMAX  the score matrix in the workspace, the softmax
+ *                                split across the two products around it
+ *                                (vae_attention);
+ *   VAE_ATTENTION_STREAMING      streaming softmax, no score matrix
+ *                                (vae_attention_streaming; 128, 256 or 512
+ *                                channels, else VAE_ERR_UNSUPPORTED).
+ * The decode workspace follows the form set when it is sized.
+ * VAE_ERR_INVALID_ARG for other values. */
+#define VAE_ATTENTION_SPLIT_SOFTMAX 0
+#define VAE_ATTENTION_STREAMING 1
+int32_t vae_decoder_set_attention(vae_decoder *d, int32_t form);
+int32_t vae_decoder_get_attention(const vae_decoder *d);
 
 /* on != 0: vae_decode / vae_decode3d capture their launch sequence into a HIP
  * graph on the first call with a given (latent, rgb, workspace, sizes,

@@ -303,3 +303,28 @@ def test_decoder_rejects_a_mismatched_latent_before_any_launch(causal3d, shape, 
     ok = (16, 2, 8, 8) if causal3d else (16, 8, 8)
     with pytest.raises(ValueError, match="GPU tensor"):
         d.decode(torch.zeros(ok))
+
+
+def test_attention_streaming_validation(lib):
+    # the workspace holds no score matrix: xn, q, v, k^T and the output (five
+    # [c, n] tensors), GroupNorm partials and the concatenated q/k/v weights
+    nb = c_size_t()
+    c, n = 512, 128 * 128
+    assert lib.vae_attention_streaming_workspace_bytes(c, 128, 128, byref(nb)) == VAE_OK
+    assert 5 * 4 * c * n <= nb.value < 5 * 4 * c * n + 4 * (3 * c * c + 3 * c) + (1 << 20)
+    split = c_size_t()
+    assert lib.vae_attention_workspace_bytes(c, 128, 128, byref(split)) == VAE_OK
+    assert nb.value < split.value - 4 * n * n + (1 << 20)
+    # channel counts the streaming kernel has no form for
+    assert lib.vae_attention_streaming_workspace_bytes(64, 8, 8, byref(nb)) == VAE_ERR_UNSUPPORTED
+    a = VaeAttn(VaeNorm(FAKE, FAKE, 64), conv(64, 64, 1), conv(64, 64, 1), conv(64, 64, 1), conv(64, 64, 1))
+    assert lib.vae_attention_streaming(FAKE, 64, 4, 4, byref(a), FAKE + 64, FAKE, 1 << 30, NULL) == VAE_ERR_UNSUPPORTED
+    assert "128, 256 and 512" in err(lib)
+    a = VaeAttn(VaeNorm(FAKE, FAKE, 128), *[conv(128, 128, 1) for _ in range(4)])
+    assert lib.vae_attention_streaming(FAKE, 128, 4, 4, byref(a), FAKE + 64, FAKE, 16, NULL) == VAE_ERR_WORKSPACE
+    assert lib.vae_attention_streaming(FAKE, 128, 4, 4, byref(a), FAKE, FAKE, 1 << 30, NULL) == VAE_ERR_INVALID_ARG
+    a.v = conv(128, 64, 1)
+    assert lib.vae_attention_streaming(FAKE, 128, 4, 4, byref(a), FAKE + 64, FAKE, 1 << 30, NULL) \
+        == VAE_ERR_INVALID_ARG
+    # the decoder's form switch rejects a NULL decoder and unknown forms
+    assert lib.vae_decoder_set_attention(NULL, 1) == VAE_ERR_INVALID_ARG

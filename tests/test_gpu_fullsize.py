@@ -135,17 +135,19 @@ def test_upsample_conv_at_other_decoder_sizes(api, c, h):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("streaming", [False, True])
 @pytest.mark.parametrize("h,w", [(96, 128), (128, 128)])
-def test_attention_at_decoder_size(api, h, w):
+def test_attention_at_decoder_size(api, h, w, streaming):
     # c = 512 over 12288 and 16384 tokens (the 1024 x 1024 decode's mid
-    # attention): whole tiles, so the score and P.V products take their
-    # full-tile paths and P.V is not split along its keys; compared element
+    # attention), in both forms: with the split softmax the score and P.V
+    # products take their full-tile paths and P.V is not split along its keys;
+    # the streaming form runs one key range per query block.  Compared element
     # by element with the oracle
     c = 512
     p = vaegen.attention_params(SEED, "fa", c)
     x = vaegen.activation(SEED, f"fa.x.{h}", (c, h, w))
     y = torch.full((c, h, w), float("nan"), device="cuda")
-    api.attention(dev(x), {k: dev(v) for k, v in p.items()}, "fa", out=y)
+    (api.attention_streaming if streaming else api.attention)(dev(x), {k: dev(v) for k, v in p.items()}, "fa", out=y)
     torch.cuda.synchronize()
     g = y.cpu().numpy().astype(np.float64)
     assert not np.isnan(g).any()

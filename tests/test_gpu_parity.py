@@ -278,6 +278,41 @@ def test_attention_peaked_softmax(api):
     assert rel_err(host(y), oracle.attention(x, p, "a")) <= LAYER_TOL
 
 
+# streaming softmax: one query block with a partial key block (8x8, 7x9, 3x5),
+# a single token, ragged tails over several key blocks (12x13, 40x41), key
+# ranges split across workgroups and merged (32x32, 64x64: 16 query blocks or
+# fewer), and every supported width
+@pytest.mark.parametrize("c,h,w", [(128, 8, 8), (128, 7, 9), (512, 3, 5), (128, 1, 1), (256, 12, 13),
+                                   (512, 40, 41), (512, 32, 32), (128, 64, 64), (256, 33, 1)])
+def test_attention_streaming(api, c, h, w):
+    p = vaegen.attention_params(14, "a", c)
+    x = vaegen.activation(14, "xs", (c, h, w))
+    y = api.attention_streaming(dev(x), {k: dev(v) for k, v in p.items()}, "a", out=nan_like((c, h, w)))
+    assert rel_err(host(y), oracle.attention(x, p, "a")) <= LAYER_TOL
+
+
+def test_attention_streaming_peaked_softmax(api):
+    # queries scaled up 40x: each query's maximum moves between key blocks,
+    # so the running maximum and the output are rescaled many times
+    c, h, w = 128, 20, 20
+    p = vaegen.attention_params(13, "a", c)
+    p["a.to_q.weight"] = (p["a.to_q.weight"] * 40.0).astype(np.float32)
+    x = vaegen.activation(13, "xp", (c, h, w))
+    y = api.attention_streaming(dev(x), {k: dev(v) for k, v in p.items()}, "a", out=nan_like((c, h, w)))
+    assert rel_err(host(y), oracle.attention(x, p, "a")) <= LAYER_TOL
+
+
+def test_attention_streaming_key_bias_cancels(api):
+    # a large key bias shifts every score of a query by q . b_k, which the
+    # softmax removes; the streaming form never adds it
+    c, h, w = 128, 9, 10
+    p = vaegen.attention_params(15, "a", c)
+    p["a.to_k.bias"] = (p["a.to_k.bias"] * 500.0 + 3.0).astype(np.float32)
+    x = vaegen.activation(15, "xb", (c, h, w))
+    y = api.attention_streaming(dev(x), {k: dev(v) for k, v in p.items()}, "a", out=nan_like((c, h, w)))
+    assert rel_err(host(y), oracle.attention(x, p, "a")) <= LAYER_TOL
+
+
 # ---------------------------------------------------------------------------
 # causal 3-D conv
 # ---------------------------------------------------------------------------
@@ -395,6 +430,39 @@ def test_decode_with_groupnorm_on_load(decoder_2x2, params, h, w):
     assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
 
 
+@pytest.fixture(scope="module")
+def decoder_streaming(api, params):
+    d = api.Decoder({k: dev(v) for k, v in params.items()}, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    d.set_attention("streaming")
+    assert d.get_attention() == "streaming"
+    yield d
+    d.close()
+
+
+@pytest.mark.parametrize("h,w", [(8, 8), (5, 3), (1, 1), (32, 32)])
+def test_decode_with_streaming_attention(decoder_streaming, params, h, w):
+    z = vaegen.latent(10, h, w)
+    rgb = decoder_streaming.decode(dev(z), out=nan_like((3, 8 * h, 8 * w)))
+    ref = oracle.decode(z, params, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    cos, mx = rgb_metrics(host(rgb), ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
+def test_decode_streaming_graph_replay_matches_eager(decoder_streaming):
+    z = dev(vaegen.latent(11, 12, 12))
+    e = decoder_streaming.decode(z).cpu()
+    out = torch.empty((3, 96, 96), dtype=torch.float32, device="cuda")
+    decoder_streaming.set_graph(True)
+    try:
+        for _ in range(3):
+            decoder_streaming.decode(z, out=out)
+            assert torch.equal(out.cpu(), e)
+            torch.cuda.synchronize()
+            _ = (torch.randn(4096, device="cuda") * 2).sum().item()
+    finally:
+        decoder_streaming.set_graph(False)
+
+
 def test_decode_is_deterministic(decoder):
     z = dev(vaegen.latent(1, 16, 16))
     a = decoder.decode(z).cpu()
@@ -482,6 +550,19 @@ def test_decode_causal3d_with_groupnorm_on_load(decoder3d_2x2, params3d):
         got = host(decoder3d_2x2.decode(dev(z), out=nan_like((3, 2, 32, 32))))
     finally:
         decoder3d_2x2.set_groupnorm_fusion(False)
+    ref = oracle.decode_causal3d(z, params3d, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
+    cos, mx = rgb_metrics(got, ref)
+    assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
+def test_decode_causal3d_with_streaming_attention(decoder3d, params3d):
+    # attention over all t*h*w positions of the clip
+    z = vaegen.latent3d(4, 3, 4, 5)
+    decoder3d.set_attention("streaming")
+    try:
+        got = host(decoder3d.decode(dev(z), out=nan_like((3, 3, 32, 40))))
+    finally:
+        decoder3d.set_attention("split_softmax")
     ref = oracle.decode_causal3d(z, params3d, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR)
     cos, mx = rgb_metrics(got, ref)
     assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)

@@ -160,12 +160,16 @@ def test_resnet_layers_on_decode_activations(api, params, trace, form, name):
     assert rel_err(host(y2), r["out"]) <= LAYER_TOL
 
 
-def test_attention_on_decode_activations(api, params, trace):
+@pytest.mark.parametrize("streaming", [False, True])
+def test_attention_on_decode_activations(api, params, trace, streaming):
     x = f32(trace["mid_block.resnets.0"])
     pre = "mid_block.attentions.0"
     pa = {k: v for k, v in params.items() if k.startswith(pre)}
-    y = api.attention(dev(x), {k: dev(v) for k, v in pa.items()}, pre, out=nan_like(x.shape))
-    assert rel_err(host(y), oracle.attention(x, pa, pre)) <= LAYER_TOL
+    fn = api.attention_streaming if streaming else api.attention
+    y = fn(dev(x), {k: dev(v) for k, v in pa.items()}, pre, out=nan_like(x.shape))
+    if "attention" not in _refs:
+        _refs["attention"] = oracle.attention(x, pa, pre)
+    assert rel_err(host(y), _refs["attention"]) <= LAYER_TOL
 
 
 @pytest.mark.parametrize("block", [0, 1, 2])
