@@ -16,7 +16,7 @@ VAE_ERR_INVALID_ARG = -1
 VAE_ERR_UNSUPPORTED = -2
 VAE_ERR_WORKSPACE = -3
 VAE_ERR_HIP = -4
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class VaeConv(ctypes.Structure):
@@ -83,6 +83,11 @@ SIGNATURES = {
                                                     POINTER(c_size_t)]),
     "vae_conv3d_causal": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(VaeConv),
                                     c_void_p, c_void_p, c_size_t, c_void_p]),
+    "vae_conv3d_causal_groupnorm_workspace_bytes": (c_int32, [POINTER(VaeConv), c_int32, c_int32, c_int32,
+                                                              POINTER(c_size_t)]),
+    "vae_conv3d_causal_groupnorm_silu": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(VaeConv),
+                                                   POINTER(VaeNorm), c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                   c_size_t, c_void_p]),
     "vae_decoder_pack_bytes": (c_int32, [POINTER(VaeWeights), POINTER(c_size_t)]),
     "vae_decoder_create": (c_int32, [POINTER(c_void_p), POINTER(VaeWeights), c_void_p, c_size_t, c_void_p]),
     "vae_decoder_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_size_t)]),

@@ -20,7 +20,7 @@ from ._lib import VaeAttn, VaeConv, VaeError, VaeNorm, VaeProfRecord, VaeResnet,
 __all__ = [
     "VaeError", "conv2d", "conv_in", "groupnorm_silu", "groupnorm_silu_noalloc", "upsample_nearest2x", "attention",
     "attention_streaming", "ATTENTION_FORMS",
-    "conv3d_causal", "Decoder", "CONV3X3_ALGORITHMS", "set_conv3x3_algorithm", "get_conv3x3_algorithm",
+    "conv3d_causal", "conv3d_causal_groupnorm_silu", "Decoder", "CONV3X3_ALGORITHMS", "set_conv3x3_algorithm", "get_conv3x3_algorithm",
 ]
 
 # Forms of the 3x3 convolutions (vae_set_conv3x3_algorithm): Winograd
@@ -260,6 +260,30 @@ def conv3d_causal(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor,
     check(lib.vae_conv3d_causal(x.data_ptr(), cin, t, h, w, byref(conv), y.data_ptr(), _ptr(ws), nb.value,
                                 _stream()))
     return y
+
+
+def conv3d_causal_groupnorm_silu(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor, gamma: torch.Tensor,
+                                 beta: torch.Tensor, silu: bool = True, residual: Optional[torch.Tensor] = None,
+                                 out: Optional[torch.Tensor] = None, out_norm: Optional[torch.Tensor] = None):
+    """y = conv3d_causal(x), then z = SiLU(GroupNorm(y)) (+ residual) with the
+    group statistics from the conv's epilogue.  Returns (y, z); ``out_norm``
+    may be ``out`` (z overwrites y)."""
+    lib = _lib_()
+    _dev(x, "x")
+    cin, t, h, w = x.shape
+    conv = _conv(weight, bias)
+    norm = _norm(gamma, beta)
+    if residual is not None:
+        _dev(residual, "residual")
+    y = _out(out, (weight.shape[0], t, h, w), x.device)
+    z = _out(out_norm, (weight.shape[0], t, h, w), x.device)
+    nb = c_size_t()
+    check(lib.vae_conv3d_causal_groupnorm_workspace_bytes(byref(conv), t, h, w, byref(nb)))
+    ws = _ws(nb.value, x.device)
+    check(lib.vae_conv3d_causal_groupnorm_silu(x.data_ptr(), cin, t, h, w, byref(conv), byref(norm), int(bool(silu)),
+                                               _ptr(residual), y.data_ptr(), z.data_ptr(), _ptr(ws), nb.value,
+                                               _stream()))
+    return y, z
 
 
 # ---------------------------------------------------------------------------

@@ -205,10 +205,14 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         ps += __shfl_xor(ps, 32, 64);
         lrun = lrun * alpha + ps;
         mrun = mnew;
+        // once the maxima settle most blocks leave every query's maximum as it
+        // was (alpha == 1 in all lanes), and the rescale is skipped
+        if (__ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int t = 0; t < G::TH; ++t)
+            for (int t = 0; t < G::TH; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][i] *= alpha;
+                for (int i = 0; i < 4; ++i) acc[t][i] *= alpha;
+        }
         __builtin_amdgcn_sched_barrier(0);
         floatx4 vv[2][CH];
 #pragma unroll

@@ -247,9 +247,9 @@ int32_t vae_groupnorm_silu(const float *x, int32_t c, int64_t spatial, const vae
 namespace {
 // Workspace of vae_conv2d_groupnorm_silu: the conv's workspace, then the
 // GroupNorm records of its output, then the GroupNorm partial sums.
-size_t conv_gn_records_bytes(const vae_conv *c, int cin, int H, int W, int upsample) {
+size_t conv_gn_records_bytes(const vae_conv *c, int cin, int H, int W, int upsample, int T = 1, int kt = 1) {
     ConvLaunch a{};
-    a.cin = cin; a.cout = c->out_channels; a.H = H; a.W = W; a.T = 1; a.kt = 1;
+    a.cin = cin; a.cout = c->out_channels; a.H = H; a.W = W; a.T = T; a.kt = kt;
     a.upsample = upsample;
     int n = 0;   // the most records any form writes, so the size holds whatever the setting
     for (int layout : {0, upsample ? 2 : 1, upsample ? 4 : 3}) {
@@ -258,9 +258,9 @@ size_t conv_gn_records_bytes(const vae_conv *c, int cin, int H, int W, int upsam
     }
     return (size_t)32 * n * sizeof(floatx4);
 }
-size_t conv_gn_ws(const vae_conv *c, int H, int W, int upsample) {
-    return align256(conv_ws(c, 1, 1, H, W)) + align256(conv_gn_records_bytes(c, c->in_channels, H, W, upsample)) +
-           groupnorm_ws_bytes(c->out_channels, (long long)H * W);
+size_t conv_gn_ws(const vae_conv *c, int H, int W, int upsample, int T = 1, int kt = 1) {
+    return align256(conv_ws(c, kt, T, H, W)) + align256(conv_gn_records_bytes(c, c->in_channels, H, W, upsample, T, kt)) +
+           groupnorm_ws_bytes(c->out_channels, (long long)T * H * W);
 }
 }  // namespace
 
@@ -317,6 +317,60 @@ int32_t vae_conv2d_groupnorm_silu(const float *x, int32_t cin, int32_t h, int32_
     if ((rc = launch_conv3x3(a, s))) return rc;
     return launch_groupnorm(y, conv->out_channels, (long long)H * W, norm->gamma, norm->beta, apply_silu ? 1 : 0,
                             nullptr, z, gws, s, a.gn_rec, nrec);
+}
+
+int32_t vae_conv3d_causal_groupnorm_workspace_bytes(const vae_conv *conv, int32_t t, int32_t h, int32_t w,
+                                                    size_t *bytes) {
+    const char *who = "vae_conv3d_causal_groupnorm_workspace_bytes";
+    int32_t rc = check_conv(who, conv, 3);
+    if (rc) return rc;
+    if (!bytes) return bad("%s: bytes is NULL", who);
+    if (t <= 0) return bad("%s: t must be positive", who);
+    if (t > 65535) return unsupported("%s: t %d exceeds the grid limit", who, t);
+    if ((rc = check_plane(who, (long long)conv->out_channels * t, h, w))) return rc;
+    if (conv->out_channels % 32) return unsupported("%s: out_channels %d not divisible by 32", who, conv->out_channels);
+    *bytes = conv_gn_ws(conv, h, w, 0, t, 3);
+    return VAE_OK;
+}
+
+int32_t vae_conv3d_causal_groupnorm_silu(const float *x, int32_t cin, int32_t t, int32_t h, int32_t w,
+                                         const vae_conv *conv, const vae_norm *norm, int32_t apply_silu,
+                                         const float *residual, float *y, float *z, void *ws, size_t ws_bytes,
+                                         void *stream) {
+    const char *who = "vae_conv3d_causal_groupnorm_silu";
+    int32_t rc = check_conv(who, conv, 3);
+    if (rc) return rc;
+    if (!x || !y || !z) return bad("%s: x, y or z is NULL", who);
+    if (!norm || !norm->gamma || !norm->beta) return bad("%s: norm missing", who);
+    if (t <= 0) return bad("%s: t must be positive", who);
+    if (t > 65535) return unsupported("%s: t %d exceeds the grid limit", who, t);
+    if ((rc = check_plane(who, (long long)cin * t, h, w))) return rc;
+    if ((rc = check_plane(who, (long long)conv->out_channels * t, h, w))) return rc;
+    if (conv->in_channels != cin) return bad("%s: conv expects %d input channels, got %d", who, conv->in_channels, cin);
+    if (norm->channels != conv->out_channels)
+        return bad("%s: norm has %d channels, conv output %d", who, norm->channels, conv->out_channels);
+    if (conv->out_channels % 32) return unsupported("%s: out_channels %d not divisible by 32", who, conv->out_channels);
+    if (x == y) return bad("%s: y may not alias x", who);
+    if (residual == y) return bad("%s: the residual may not alias y", who);
+    const size_t need = conv_gn_ws(conv, h, w, 0, t, 3);
+    if (!ws || ws_bytes < need)
+        return set_error("%s: workspace %zu bytes < %zu", who, ws_bytes, need), VAE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *base = static_cast<char *>(ws);
+    ConvLaunch a{};
+    a.wino = conv3x3_layout(0, 0);
+    if ((rc = pack_conv3x3_layout(a.wino, conv->weight, conv->out_channels, cin, 3, reinterpret_cast<float *>(base), s)))
+        return rc;
+    a.x = x; a.wpk = reinterpret_cast<const float *>(base); a.bias = conv->bias; a.y = y;
+    a.part = conv_ws_part(conv, 3, ws);
+    a.cin = cin; a.cout = conv->out_channels; a.H = h; a.W = w; a.T = t; a.kt = 3;
+    char *recs = base + align256(conv_ws(conv, 3, t, h, w));
+    void *gws = recs + align256(conv_gn_records_bytes(conv, cin, h, w, 0, t, 3));
+    const int nrec = conv3x3_gn_records(a);
+    a.gn_rec = nrec > 0 ? reinterpret_cast<floatx4 *>(recs) : nullptr;
+    if ((rc = launch_conv3x3(a, s))) return rc;
+    return launch_groupnorm(y, conv->out_channels, (long long)t * h * w, norm->gamma, norm->beta, apply_silu ? 1 : 0,
+                            residual, z, gws, s, a.gn_rec, nrec);
 }
 
 int32_t vae_upsample_nearest2x(const float *x, int32_t c, int32_t h, int32_t w, float *y, void *stream) {

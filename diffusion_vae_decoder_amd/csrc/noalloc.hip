@@ -20,7 +20,8 @@
 namespace {
 
 // Largest workspace any GroupNorm needs: 32 groups x at most 64 parts x 2
-// doubles of partial sums, plus 32 doubles of shifts (33,024 bytes).
+// doubles of partial sums, 32 doubles of shifts and 32 (mean, rstd) pairs
+// (33,280 bytes).
 constexpr size_t kScratchBytes = 36 * 1024;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];

@@ -96,12 +96,14 @@ __global__ __launch_bounds__(kThreads) void gn_stats(const float *__restrict__ x
     }
 }
 
-// With `rec` set (a short list of producer records per group) each workgroup
-// merges its group's records itself, as gn_merge does, instead of reading
-// merged partials.
+// With `rec` set (a short list of producer records per group) or `part` (the
+// statistics pass's partial sums) each workgroup merges its group's
+// statistics itself; otherwise it reads the group's (mean, rstd) that gn_merge
+// wrote.
 template <bool VEC, bool SILU, bool RES>
 __global__ __launch_bounds__(kThreads) void gn_apply(const float *x, long long spatial, int cpg,
-                                                     int parts, const double *__restrict__ part,
+                                                     const floatx2 *__restrict__ gstat,
+                                                     const double *__restrict__ part, int parts,
                                                      const double *__restrict__ shifts,
                                                      const float *__restrict__ gamma,
                                                      const float *__restrict__ beta,
@@ -111,37 +113,47 @@ __global__ __launch_bounds__(kThreads) void gn_apply(const float *x, long long s
     __shared__ float stat[2];
     const int c = blockIdx.y;
     const int g = c / cpg;
-    double s1 = 0.0, s2 = 0.0;
-    if (rec) {
-        for (int i = threadIdx.x; i < nrec; i += kThreads) {
-            const floatx4 v = rec[(long long)g * nrec + i];
-            const double n = v[0], m = v[1];
-            s1 += n * m;
-            s2 += (double)v[2] + n * m * m;
+    float mean, scale;
+    if (rec || part) {
+        // the workgroup merges its group's statistics itself: producer records,
+        // or the statistics pass's shifted partial sums, in a fixed order
+        double s1 = 0.0, s2 = 0.0;
+        if (rec) {
+            for (int i = threadIdx.x; i < nrec; i += kThreads) {
+                const floatx4 v = rec[(long long)g * nrec + i];
+                const double n = v[0], m = v[1];
+                s1 += n * m;
+                s2 += (double)v[2] + n * m * m;
+            }
+        } else if (threadIdx.x < parts) {
+            s1 = part[2 * ((long long)g * parts + threadIdx.x)];
+            s2 = part[2 * ((long long)g * parts + threadIdx.x) + 1];
         }
-    } else if (threadIdx.x < parts) {
-        s1 = part[2 * ((long long)g * parts + threadIdx.x)];
-        s2 = part[2 * ((long long)g * parts + threadIdx.x) + 1];
-    }
-    block_sum2(s1, s2, scratch);
-    if (threadIdx.x == 0) {
-        const double n = (double)spatial * cpg;
-        double mean, var;
-        if (rec) {   // s1 = sum n m, s2 = sum (M2 + n m^2) over the records
-            mean = s1 / n;
-            var = (s2 - s1 * mean) / n;
-        } else {     // shifted sums d = x - shift
-            const double md = s1 / n;
-            var = s2 / n - md * md;
-            mean = shifts[g] + md;
+        block_sum2(s1, s2, scratch);
+        if (threadIdx.x == 0) {
+            const double n = (double)spatial * cpg;
+            double mu, var;
+            if (rec) {   // s1 = sum n m, s2 = sum (M2 + n m^2) over the records
+                mu = s1 / n;
+                var = (s2 - s1 * mu) / n;
+            } else {     // shifted sums d = x - shift
+                const double md = s1 / n;
+                var = s2 / n - md * md;
+                mu = shifts[g] + md;
+            }
+            if (var < 0.0) var = 0.0;
+            stat[0] = (float)mu;
+            stat[1] = (float)(1.0 / sqrt(var + 1e-6) * (double)gamma[c]);
         }
-        if (var < 0.0) var = 0.0;
-        const double rstd = 1.0 / sqrt(var + 1e-6);
-        stat[0] = (float)mean;
-        stat[1] = (float)(rstd * (double)gamma[c]);
+        __syncthreads();
+        mean = stat[0];
+        scale = stat[1];
+    } else {
+        const floatx2 st = gstat[g];
+        mean = st[0];
+        scale = st[1] * gamma[c];
     }
-    __syncthreads();
-    const float mean = stat[0], scale = stat[1], b = beta[c];
+    const float b = beta[c];
     const long long cbase = (long long)c * spatial;
     const long long lo = (long long)blockIdx.x * kApplyElems;
     long long hi = lo + kApplyElems;
@@ -180,48 +192,43 @@ __global__ __launch_bounds__(kThreads) void gn_apply(const float *x, long long s
     }
 }
 
+// (mean, rstd) of each group from the statistics pass's shifted partial sums,
+// added in part order (deterministic): one thread per group.
+__global__ __launch_bounds__(64) void gn_finalize(long long gsize, int parts, const double *__restrict__ part,
+                                                  const double *__restrict__ shifts, floatx2 *__restrict__ gstat) {
+    const int g = threadIdx.x;
+    if (g >= kGroups) return;
+    double s1 = 0.0, s2 = 0.0;
+    for (int i = 0; i < parts; ++i) {
+        s1 += part[2 * ((long long)g * parts + i)];
+        s2 += part[2 * ((long long)g * parts + i) + 1];
+    }
+    const double n = (double)gsize;
+    const double md = s1 / n;
+    double var = s2 / n - md * md;
+    if (var < 0.0) var = 0.0;
+    gstat[g] = floatx2{(float)(shifts[g] + md), (float)(1.0 / sqrt(var + 1e-6))};
+}
+
 // Per-channel coefficients of GroupNorm for a consumer that normalises on
-// load: coef[c] = (mean_g, rstd_g * gamma[c], beta[c], 0).  One workgroup per
-// group merges the group's partials in the same fixed order as gn_apply.
-__global__ __launch_bounds__(kThreads) void gn_coef(long long gsize, int cpg, int parts,
-                                                    const double *__restrict__ part,
-                                                    const double *__restrict__ shifts,
+// load: coef[c] = (mean_g, rstd_g * gamma[c], beta[c], 0).
+__global__ __launch_bounds__(kThreads) void gn_coef(int c, int cpg, const floatx2 *__restrict__ gstat,
                                                     const float *__restrict__ gamma,
                                                     const float *__restrict__ beta, float *__restrict__ coef) {
-    __shared__ double scratch[8];
-    __shared__ double stat[2];
-    const int g = blockIdx.x;
-    double s1 = 0.0, s2 = 0.0;
-    if (threadIdx.x < parts) {
-        s1 = part[2 * ((long long)g * parts + threadIdx.x)];
-        s2 = part[2 * ((long long)g * parts + threadIdx.x) + 1];
-    }
-    block_sum2(s1, s2, scratch);
-    if (threadIdx.x == 0) {
-        const double n = (double)gsize;
-        const double md = s1 / n;
-        double var = s2 / n - md * md;
-        if (var < 0.0) var = 0.0;
-        stat[0] = shifts[g] + md;
-        stat[1] = 1.0 / sqrt(var + 1e-6);
-    }
-    __syncthreads();
-    for (int j = threadIdx.x; j < cpg; j += kThreads) {
-        const int c = g * cpg + j;
-        floatx4 v = {(float)stat[0], (float)(stat[1] * (double)gamma[c]), beta[c], 0.f};
-        reinterpret_cast<floatx4 *>(coef)[c] = v;
-    }
+    const int ch = blockIdx.x * kThreads + threadIdx.x;
+    if (ch >= c) return;
+    const floatx2 st = gstat[ch / cpg];
+    reinterpret_cast<floatx4 *>(coef)[ch] = floatx4{st[0], st[1] * gamma[ch], beta[ch], 0.f};
 }
 
 // One workgroup per group merges the group's records (count n, mean m, M2)
 // into float64 sums S0 = sum n, S1 = sum n m and S2 = sum (M2 + n m^2), in a
-// fixed order (a strided pass per thread, then a fixed tree), and stores
-// them in the partial-sum form gn_apply and gn_coef read with one part:
-// shift = S1 / S0, sum d = 0, sum d^2 = S2 - S1^2 / S0.  The records' own
+// fixed order (a strided pass per thread, then a fixed tree), and stores the
+// group's mean S1 / S0 and rstd 1 / sqrt((S2 - S1^2 / S0) / S0 + eps).  The records' own
 // centring keeps M2 accurate in float32; the float64 sums then lose nothing
 // to cancellation unless the mean exceeds the spread by ~1e6.
 __global__ __launch_bounds__(kThreads) void gn_merge(const floatx4 *__restrict__ rec, int nrec,
-                                                     double *__restrict__ part, double *__restrict__ shift_out) {
+                                                     floatx2 *__restrict__ gstat) {
     __shared__ double sh[3 * 4];
     const int g = blockIdx.x;
     const floatx4 *r = rec + (long long)g * nrec;
@@ -254,22 +261,26 @@ __global__ __launch_bounds__(kThreads) void gn_merge(const floatx4 *__restrict__
         const double mean = t1 / n;
         double m2 = t2 - t1 * mean;
         if (m2 < 0.0) m2 = 0.0;
-        part[2 * g] = 0.0;
-        part[2 * g + 1] = m2;
-        shift_out[g] = mean;
+        gstat[g] = floatx2{(float)mean, (float)(1.0 / sqrt(m2 / n + 1e-6))};
     }
 }
 
+struct ApplyStats {
+    const floatx2 *gstat;                  // merged (mean, rstd) per group, or
+    const double *part; int parts;         // the statistics pass's partial sums, or
+    const double *shifts;
+    const floatx4 *rec; int nrec;          // producer records
+};
+
 template <bool VEC, bool SILU>
-void apply2(bool res, dim3 grid, hipStream_t s, const float *x, long long spatial, int cpg,
-            int parts, const double *part, const double *shifts, const float *gamma,
-            const float *beta, const float *r, float *y, const floatx4 *rec, int nrec) {
+void apply2(bool res, dim3 grid, hipStream_t s, const float *x, long long spatial, int cpg, const ApplyStats &st,
+            const float *gamma, const float *beta, const float *r, float *y) {
     if (res)
-        hipLaunchKernelGGL((gn_apply<VEC, SILU, true>), grid, dim3(kThreads), 0, s, x, spatial, cpg,
-                           parts, part, shifts, gamma, beta, r, y, rec, nrec);
+        hipLaunchKernelGGL((gn_apply<VEC, SILU, true>), grid, dim3(kThreads), 0, s, x, spatial, cpg, st.gstat, st.part,
+                           st.parts, st.shifts, gamma, beta, r, y, st.rec, st.nrec);
     else
-        hipLaunchKernelGGL((gn_apply<VEC, SILU, false>), grid, dim3(kThreads), 0, s, x, spatial, cpg,
-                           parts, part, shifts, gamma, beta, r, y, rec, nrec);
+        hipLaunchKernelGGL((gn_apply<VEC, SILU, false>), grid, dim3(kThreads), 0, s, x, spatial, cpg, st.gstat,
+                           st.part, st.parts, st.shifts, gamma, beta, r, y, st.rec, st.nrec);
 }
 
 // ------------------------------------------------------------- upsample x2
@@ -304,19 +315,13 @@ __global__ void upsample2x_scalar(const float *__restrict__ x, float *__restrict
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Statistics of x's 32 groups into ws: from the records a producer wrote
-// (one merged part per group) or from a pass over x.  Returns the parts.
-int32_t groupnorm_stats(const float *x, int c, long long spatial, void *ws, hipStream_t s, const floatx4 *rec,
-                        int nrec, int *parts_out) {
+// The statistics pass over x: shifted partial sums of each group's slices
+// into ws (parts per group), and each group's shift.
+int32_t groupnorm_pass(const float *x, int c, long long spatial, void *ws, hipStream_t s) {
     const long long gsize = (long long)(c / kGroups) * spatial;
-    const int parts = rec ? 1 : parts_for(gsize);
+    const int parts = parts_for(gsize);
     double *part = reinterpret_cast<double *>(ws);
     double *shifts = part + 2 * kGroups * parts;
-    *parts_out = parts;
-    if (rec) {
-        hipLaunchKernelGGL(gn_merge, dim3(kGroups), dim3(kThreads), 0, s, rec, nrec, part, shifts);
-        return check_launch("gn_merge");
-    }
     if (gsize % 4 == 0 && aligned16(x))
         hipLaunchKernelGGL(gn_stats<true>, dim3(parts, kGroups), dim3(kThreads), 0, s, x, gsize, parts, part, shifts);
     else
@@ -324,49 +329,83 @@ int32_t groupnorm_stats(const float *x, int c, long long spatial, void *ws, hipS
     return check_launch("gn_stats");
 }
 
+// Statistics of x's 32 groups: (mean, rstd) per group into `gstat`, from the
+// records a producer wrote or from a pass over x (partial sums in ws).
+int32_t groupnorm_stats(const float *x, int c, long long spatial, void *ws, floatx2 *gstat, hipStream_t s,
+                        const floatx4 *rec, int nrec) {
+    if (rec) {
+        hipLaunchKernelGGL(gn_merge, dim3(kGroups), dim3(kThreads), 0, s, rec, nrec, gstat);
+        return check_launch("gn_merge");
+    }
+    int32_t rc = groupnorm_pass(x, c, spatial, ws, s);
+    if (rc != VAE_OK) return rc;
+    const long long gsize = (long long)(c / kGroups) * spatial;
+    const int parts = parts_for(gsize);
+    const double *part = reinterpret_cast<const double *>(ws);
+    hipLaunchKernelGGL(gn_finalize, dim3(1), dim3(64), 0, s, gsize, parts, part, part + 2 * kGroups * parts, gstat);
+    return check_launch("gn_finalize");
+}
+
 }  // namespace
 
+// Workspace: the statistics pass's partial sums and shifts, then (mean, rstd)
+// per group.
 size_t groupnorm_ws_bytes(int c, long long spatial) {
     const long long gsize = (long long)(c / kGroups) * spatial;
-    return (size_t)kGroups * parts_for(gsize) * 2 * sizeof(double) + kGroups * sizeof(double);
+    return (size_t)kGroups * parts_for(gsize) * 2 * sizeof(double) + kGroups * sizeof(double) +
+           kGroups * sizeof(floatx2);
 }
+
+namespace {
+floatx2 *gstat_of(void *ws, int c, long long spatial) {
+    const long long gsize = (long long)(c / kGroups) * spatial;
+    return reinterpret_cast<floatx2 *>(static_cast<char *>(ws) +
+                                       (size_t)kGroups * parts_for(gsize) * 2 * sizeof(double) +
+                                       kGroups * sizeof(double));
+}
+}  // namespace
 
 int32_t launch_groupnorm(const float *x, int c, long long spatial, const float *gamma,
                          const float *beta, int silu, const float *res, float *y, void *ws,
                          hipStream_t s, const floatx4 *rec, int nrec) {
     const int cpg = c / kGroups;
-    int parts = 0;
-    // a few records per group: every apply workgroup merges its group's own
-    const bool inline_rec = rec && nrec <= kInlineRecords;
-    if (!inline_rec) {
-        int32_t rc = groupnorm_stats(x, c, spatial, ws, s, rec, nrec, &parts);
-        if (rc != VAE_OK) return rc;
+    ApplyStats st{};
+    int32_t rc = VAE_OK;
+    if (rec && nrec <= kInlineRecords) {
+        // a few records per group: every apply workgroup merges its group's own
+        st.rec = rec;
+        st.nrec = nrec;
+    } else if (rec) {
+        st.gstat = gstat_of(ws, c, spatial);
+        rc = groupnorm_stats(x, c, spatial, ws, const_cast<floatx2 *>(st.gstat), s, rec, nrec);
+    } else {
+        // every apply workgroup merges the statistics pass's partial sums
+        // (cheaper than a launch that merges them once)
+        rc = groupnorm_pass(x, c, spatial, ws, s);
+        st.parts = parts_for((long long)cpg * spatial);
+        st.part = reinterpret_cast<const double *>(ws);
+        st.shifts = st.part + 2 * kGroups * st.parts;
     }
-    const floatx4 *arec = inline_rec ? rec : nullptr;
-    const double *part = reinterpret_cast<const double *>(ws);
-    const double *shifts = part + 2 * kGroups * parts;
+    if (rc != VAE_OK) return rc;
     const bool vec = spatial % 4 == 0 && aligned16(x) && aligned16(y) && (!res || aligned16(res));
     const dim3 grid((unsigned)((spatial + kApplyElems - 1) / kApplyElems), (unsigned)c);
     if (vec) {
-        if (silu) apply2<true, true>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y, arec, nrec);
-        else apply2<true, false>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y, arec, nrec);
+        if (silu) apply2<true, true>(res, grid, s, x, spatial, cpg, st, gamma, beta, res, y);
+        else apply2<true, false>(res, grid, s, x, spatial, cpg, st, gamma, beta, res, y);
     } else {
-        if (silu) apply2<false, true>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y, arec, nrec);
-        else apply2<false, false>(res, grid, s, x, spatial, cpg, parts, part, shifts, gamma, beta, res, y, arec, nrec);
+        if (silu) apply2<false, true>(res, grid, s, x, spatial, cpg, st, gamma, beta, res, y);
+        else apply2<false, false>(res, grid, s, x, spatial, cpg, st, gamma, beta, res, y);
     }
     return check_launch("gn_apply");
 }
 
 int32_t launch_groupnorm_coef(const float *x, int c, long long spatial, const float *gamma, const float *beta,
                               void *ws, float *coef, hipStream_t s, const floatx4 *rec, int nrec) {
-    const int cpg = c / kGroups;
-    const long long gsize = (long long)cpg * spatial;
-    int parts = 0;
-    int32_t rc = groupnorm_stats(x, c, spatial, ws, s, rec, nrec, &parts);
+    floatx2 *gstat = gstat_of(ws, c, spatial);
+    int32_t rc = groupnorm_stats(x, c, spatial, ws, gstat, s, rec, nrec);
     if (rc != VAE_OK) return rc;
-    const double *part = reinterpret_cast<const double *>(ws);
-    const double *shifts = part + 2 * kGroups * parts;
-    hipLaunchKernelGGL(gn_coef, dim3(kGroups), dim3(kThreads), 0, s, gsize, cpg, parts, part, shifts, gamma, beta, coef);
+    hipLaunchKernelGGL(gn_coef, dim3((unsigned)((c + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, c,
+                       c / kGroups, gstat, gamma, beta, coef);
     return check_launch("gn_coef");
 }
 

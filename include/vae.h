@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 8
+#define VAE_ABI_VERSION 9
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -184,7 +184,7 @@ int32_t vae_groupnorm_silu(const float *x, int32_t c, int64_t spatial, const vae
  * harnesses that forbid allocation).  Same arguments, kernels and results as
  * vae_groupnorm_silu; its partial sums live in a static device buffer of the
  * library (36 KiB per GPU, held until the process ends; every GroupNorm
- * needs at most 33,024 bytes of it, and a larger need is refused with
+ * needs at most 33,280 bytes of it, and a larger need is refused with
  * VAE_ERR_UNSUPPORTED).  The buffer is looked up on the first call on each
  * device (the current device) and shared by every later call on that GPU:
  * calls that overlap in time on one GPU race on it, so callers serialise
@@ -254,6 +254,22 @@ int32_t vae_conv3d_causal_workspace_bytes(const vae_conv *conv, int32_t t, int32
 int32_t vae_conv3d_causal(const float *x, int32_t cin, int32_t t, int32_t h, int32_t w,
                           const vae_conv *conv, float *y, void *ws, size_t ws_bytes,
                           void *stream);
+
+/* The causal 3-D conv followed by GroupNorm(32) (+ SiLU) of its output and an
+ * optional residual added after it: one layer of the LTX-style causal stack
+ * (VAE decode -> GPU handoff, "The CPU VAE code").
+ *   y = conv3d_causal(x)                                as vae_conv3d_causal
+ *   z = SiLU?(GroupNorm(y)) [+ residual]                statistics over
+ *       (C/32) x t x h x w, taken from the conv's epilogue records, so the
+ *       normalisation needs no separate statistics pass over y
+ * norm->channels == conv->out_channels, a multiple of 32.  y may not alias x
+ * or the residual; z may alias y (it is written last) or the residual. */
+int32_t vae_conv3d_causal_groupnorm_workspace_bytes(const vae_conv *conv, int32_t t, int32_t h, int32_t w,
+                                                    size_t *bytes);
+int32_t vae_conv3d_causal_groupnorm_silu(const float *x, int32_t cin, int32_t t, int32_t h, int32_t w,
+                                         const vae_conv *conv, const vae_norm *norm, int32_t apply_silu,
+                                         const float *residual, float *y, float *z, void *ws, size_t ws_bytes,
+                                         void *stream);
 
 /* --------------------------------------------------------------- decoder */
 

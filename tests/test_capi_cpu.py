@@ -150,12 +150,12 @@ def test_conv_groupnorm_validation(lib):
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(c), 37, 45, 0, byref(nb)) == VAE_OK
     # packed weights, 32 groups x 16-byte records for the form writing the most
     # (the implicit GEMM's 2 x 10 blocks of 4 x 32 outputs; F(2x2): 2 x 5, F(4x4):
-    # 1 x 3), GroupNorm partials
-    assert nb.value == packed_bytes(128, 16) + 20 * 32 * 16 + 32 * 16 + 32 * 8
+    # 1 x 3), GroupNorm partials (sums, shift) and per-group (mean, rstd)
+    assert nb.value == packed_bytes(128, 16) + 20 * 32 * 16 + 32 * 16 + 32 * 8 + 32 * 8
     c64 = conv(64, 16, 3)                        # 2 channels per group: no records, a statistics pass
     n64 = c_size_t()
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(c64), 37, 45, 0, byref(n64)) == VAE_OK
-    assert n64.value == 256 * ((packed_bytes(64, 16) + 255) // 256) + 32 * 16 + 32 * 8
+    assert n64.value == 256 * ((packed_bytes(64, 16) + 255) // 256) + 32 * 16 + 32 * 8 + 32 * 8
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(conv(100, 16, 3)), 8, 8, 0, byref(nb)) == VAE_ERR_UNSUPPORTED
     assert lib.vae_conv2d_groupnorm_workspace_bytes(byref(conv(128, 16, 1)), 8, 8, 0, byref(nb)) == VAE_ERR_UNSUPPORTED
     n = VaeNorm(FAKE, FAKE, 128)
@@ -328,3 +328,31 @@ def test_attention_streaming_validation(lib):
         == VAE_ERR_INVALID_ARG
     # the decoder's form switch rejects a NULL decoder and unknown forms
     assert lib.vae_decoder_set_attention(NULL, 1) == VAE_ERR_INVALID_ARG
+
+
+def test_conv3d_groupnorm_validation(lib):
+    c3 = conv(128, 128, 3)
+    nb = c_size_t()
+    assert lib.vae_conv3d_causal_groupnorm_workspace_bytes(byref(c3), 17, 256, 256, byref(nb)) == VAE_OK
+    plain = c_size_t()
+    assert lib.vae_conv3d_causal_workspace_bytes(byref(c3), 17, 256, 256, byref(plain)) == VAE_OK
+    # the conv's workspace, then the records (32 groups x 16 bytes per tile) and GroupNorm partials
+    assert plain.value < nb.value < plain.value + (1 << 24)
+    assert lib.vae_conv3d_causal_groupnorm_workspace_bytes(byref(conv(100, 128, 3)), 2, 8, 8, byref(nb)) \
+        == VAE_ERR_UNSUPPORTED
+    n = VaeNorm(FAKE, FAKE, 128)
+    ws = c_size_t()
+    lib.vae_conv3d_causal_groupnorm_workspace_bytes(byref(c3), 3, 8, 8, byref(ws))
+
+    def call(**k):
+        a = dict(x=FAKE, cin=128, t=3, h=8, w=8, conv=byref(c3), norm=byref(n), silu=1, res=NULL, y=FAKE + 4096,
+                 z=FAKE + 4096, ws=FAKE + 1 << 20, nb=ws.value)
+        a.update(k)
+        return lib.vae_conv3d_causal_groupnorm_silu(a["x"], a["cin"], a["t"], a["h"], a["w"], a["conv"], a["norm"],
+                                                    a["silu"], a["res"], a["y"], a["z"], a["ws"], a["nb"], NULL)
+    assert call(z=NULL) == VAE_ERR_INVALID_ARG
+    assert call(t=0) == VAE_ERR_INVALID_ARG
+    assert call(norm=byref(VaeNorm(FAKE, FAKE, 64))) == VAE_ERR_INVALID_ARG and "norm" in err(lib)
+    assert call(y=FAKE) == VAE_ERR_INVALID_ARG and "alias" in err(lib)
+    assert call(res=FAKE + 4096) == VAE_ERR_INVALID_ARG and "residual" in err(lib)
+    assert call(nb=ws.value - 1) == VAE_ERR_WORKSPACE

@@ -325,6 +325,29 @@ def test_conv3d_causal(api, algo, cin, cout, t, h, w):
     assert rel_err(host(y), oracle.conv3d_causal(x, wt, b)) <= LAYER_TOL
 
 
+@pytest.mark.parametrize("cin,cout,t,h,w,res,silu", [(16, 128, 3, 9, 13, False, True),
+                                                     (128, 128, 4, 16, 16, True, True),
+                                                     (64, 256, 2, 7, 33, True, False)])
+def test_conv3d_causal_groupnorm_silu(api, cin, cout, t, h, w, res, silu):
+    # GroupNorm statistics from the causal conv's epilogue (or its K-split
+    # reduction on these small shapes), residual added after the SiLU
+    x = vaegen.activation(23, "x3g", (cin, t, h, w))
+    wt, b = conv_params(23, "c3g", cin, cout, 3, dims=3)
+    n = vaegen.norm_params(23, "n3g", cout)
+    r = vaegen.activation(23, "r3g", (cout, t, h, w)) if res else None
+    y, z = api.conv3d_causal_groupnorm_silu(dev(x), dev(wt), dev(b), dev(n["n3g.weight"]), dev(n["n3g.bias"]),
+                                            silu=silu, residual=dev(r) if res else None,
+                                            out=nan_like((cout, t, h, w)), out_norm=nan_like((cout, t, h, w)))
+    yref = oracle.conv3d_causal(x, wt, b)
+    zref = oracle.group_norm(yref, n["n3g.weight"], n["n3g.bias"])
+    if silu:
+        zref = oracle.silu(zref)
+    if res:
+        zref = zref + r
+    assert rel_err(host(y), yref) <= LAYER_TOL
+    assert rel_err(host(z), zref) <= LAYER_TOL
+
+
 def test_causal_stack_small(api):
     c = 64
     p = vaegen.causal_stack_params(12, c=c)
@@ -340,6 +363,17 @@ def test_causal_stack_small(api):
         h = cur
     ref = oracle.causal_stack(x, p)
     assert rel_err(host(h), ref) <= LAYER_TOL
+    # the same stack through the conv -> GroupNorm entry point, in place
+    h2 = dev(x)
+    for i in (0, 2):
+        cur = h2
+        for j in (i, i + 1):
+            out = nan_like(cur.shape)
+            _, cur = api.conv3d_causal_groupnorm_silu(cur, P[f"stack.{j}.conv.weight"], P[f"stack.{j}.conv.bias"],
+                                                      P[f"stack.{j}.norm.weight"], P[f"stack.{j}.norm.bias"],
+                                                      residual=h2 if j == i + 1 else None, out=out, out_norm=out)
+        h2 = cur
+    assert rel_err(host(h2), ref) <= LAYER_TOL
 
 
 # ---------------------------------------------------------------------------
