@@ -1,7 +1,10 @@
 """ctypes declarations of libvae.so (see include/vae.h).
 
 The library is loaded from this package directory.  There is no fallback: if
-``libvae.so`` is missing, :func:`load` raises, naming the build command.
+``libvae.so`` is missing, :func:`load` raises, naming the build command.  The
+environment variable VAE_LIBRARY may name the sanitizer build
+``libvae_san.so`` of the same directory instead (it needs the ASan runtime
+preloaded into the process).
 """
 from __future__ import annotations
 
@@ -9,7 +12,11 @@ import ctypes
 import os
 from ctypes import POINTER, c_char, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvae.so")
+_LIB_NAMES = ("libvae.so", "libvae_san.so")
+_LIB_NAME = os.environ.get("VAE_LIBRARY", "libvae.so")
+if _LIB_NAME not in _LIB_NAMES:
+    raise ImportError(f"VAE_LIBRARY={_LIB_NAME!r}; expected one of {_LIB_NAMES}")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
 
 VAE_OK = 0
 VAE_ERR_INVALID_ARG = -1

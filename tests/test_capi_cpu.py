@@ -39,6 +39,14 @@ def test_abi_version(lib):
     assert lib.vae_abi_version() == _lib.ABI_VERSION
 
 
+def test_the_named_library_is_loaded(lib):
+    # VAE_LIBRARY selects the sanitizer build; then ASan must be live in the process
+    name = os.environ.get("VAE_LIBRARY", "libvae.so")
+    assert os.path.basename(_lib.LIB_PATH) == name
+    if name == "libvae_san.so":
+        assert hasattr(ctypes.CDLL(None), "__asan_report_load4")
+
+
 def conv(cout, cin, k, w=FAKE, b=FAKE):
     return VaeConv(w, b, cout, cin, k)
 
