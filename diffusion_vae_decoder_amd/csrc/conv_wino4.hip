@@ -238,30 +238,46 @@ __device__ __attribute__((always_inline)) inline void w4_stage(const WParams &p,
 }
 
 // One step from LDS for point half H of a plain input: the lane's patch of
-// its channel, the half's transform and its 2 x 18 MFMAs.  The patch rows
-// pass through B^T for the half's three columns as they are read, then each
-// column is finished and multiplied at once.  Product k = 6 c + r of the half
-// is point (r, 3H + c); its A operand for row block b is component k % 4 of
-// float4 b * 10 + 5 H + k / 4.
+// its channel, the half's transform and its 2 x 18 MFMAs.  Every LDS read of
+// the step (the 6 x 6 patch and the half's U) is issued first, so their
+// latency is paid once per step and the transform consumes the values in the
+// order they arrive (left to the compiler, the U reads went out just before
+// their MFMAs into reused registers, each with a wait of its own).  The patch
+// rows pass through B^T for the half's three columns, then each column is
+// finished and multiplied at once.  Product k = 6 c + r of the half is point
+// (r, 3H + c); its A operand for row block b is component k % 4 of float4
+// b * 10 + 5 H + k / 4.
 template <int TCW, int H>
 __device__ __attribute__((always_inline)) inline void w4_step(const float *lx, const floatx4 *lu, const int (&pb)[3],
                                                              int lane, floatx4 (&acc)[kW4RB][W4Shape<false>::NX]) {
     using G = W4Geom<TCW, false>;
     using S = W4Shape<false>;
-    float t[6][3];   // d B, the half's columns
+    static_assert(S::NX == 4 * (S::Q1 - 1) + 2, "products 16 and 17 fill half of the last float4");
+    float d[6][6];
 #pragma unroll
-    for (int r = 0; r < 6; ++r) {
-        float d[6];
+    for (int r = 0; r < 6; ++r)
 #pragma unroll
         for (int h = 0; h < 3; ++h) {
             const floatx2 a = *reinterpret_cast<const floatx2 *>(lx + pb[h] + r * G::HCP);
-            d[2 * h] = a[0];
-            d[2 * h + 1] = a[1];
+            d[r][2 * h] = a[0];
+            d[r][2 * h + 1] = a[1];
         }
-        w4_bt_half<H>(d, t[r][0], t[r][1], t[r][2]);
-    }
+    // the last float4 of a row block is read as its used half, so the
+    // compiler does not reuse the other half's registers (which would make it
+    // wait for every read in flight first)
     const floatx4 *ul = lu + H * S::Q1 * 64 + lane;
-    floatx4 u[kW4RB][S::Q1];
+    floatx4 u[kW4RB][S::Q1 - 1];
+    floatx2 ulast[kW4RB];
+#pragma unroll
+    for (int b = 0; b < kW4RB; ++b) {
+#pragma unroll
+        for (int q = 0; q < S::Q1 - 1; ++q) u[b][q] = ul[(b * S::UQ + q) * 64];
+        ulast[b] = *reinterpret_cast<const floatx2 *>(ul + (b * S::UQ + S::Q1 - 1) * 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float t[6][3];   // d B, the half's columns
+#pragma unroll
+    for (int r = 0; r < 6; ++r) w4_bt_half<H>(d[r], t[r][0], t[r][1], t[r][2]);
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
         float v[6];
@@ -271,8 +287,8 @@ __device__ __attribute__((always_inline)) inline void w4_step(const float *lx, c
             const int k = 6 * c + r;
 #pragma unroll
             for (int b = 0; b < kW4RB; ++b) {
-                if (k % 4 == 0) u[b][k / 4] = ul[(b * S::UQ + k / 4) * 64];
-                acc[b][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(u[b][k / 4][k % 4], v[r], acc[b][k], 0, 0, 0);
+                const float ua = k / 4 == S::Q1 - 1 ? ulast[b][k & 1] : u[b][k / 4 < S::Q1 - 1 ? k / 4 : 0][k % 4];
+                acc[b][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ua, v[r], acc[b][k], 0, 0, 0);
             }
         }
     }
