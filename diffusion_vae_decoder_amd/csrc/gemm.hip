@@ -11,7 +11,7 @@
 // as [k][m] / [k][n] rows (double-buffered); each wave computes 64 x 64 as
 // 2 x 2 v_mfma_f32_32x32x2_f32 tiles.  Lane half h of a wave carries the K
 // indices [8h, 8h + 8) of a chunk.  When every tile is full (M, N multiples
-// of 128, K of 16, float4-aligned operands) the operand loads walk
+// of 128, K of 16, float4-aligned operands and bias) the operand loads walk
 // precomputed pointers with no bounds checks.
 //
 // Problems whose tiles cannot fill the GPU (the small attentions) split K
@@ -158,8 +158,11 @@ __device__ __attribute__((always_inline)) inline void tile_store(float *lds, con
     }
 }
 
+// Four waves per SIMD (four workgroups per CU): the accumulators then live in
+// the architectural VGPRs (left free, the compiler put them in AGPRs and the
+// kernel ran three waves per SIMD, 6-9% slower on the decoder's shapes).
 template <bool A_MK, bool B_NK, bool VEC, bool RES, bool FULL, int EPI, bool BSM, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void gemm_mfma(Params p) {
     __shared__ __attribute__((aligned(16))) float As[2][BK * LD];
     __shared__ __attribute__((aligned(16))) float Bs[2][BK * LD];
     const int tid = threadIdx.x;
@@ -262,6 +265,17 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
 
     // Epilogue: D[i][j] of a 32x32 MFMA tile sits in lane j + 32*((i/4)%2),
     // register (i%4) + 4*(i/8).
+    // full tiles: the lane's 32 bias values as float4s (rows m .. m + 3 of a
+    // register quad), one load each instead of one per output row
+    floatx4 bq[2][4];
+    if (FULL && !SPLIT) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                bq[i][g] = p.bias ? *reinterpret_cast<const floatx4 *>(p.bias + m0 + wm * 64 + i * 32 + 8 * g + 4 * half)
+                                  : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -275,7 +289,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma(Params p) {
                     p.part[((long long)split * p.M + m) * p.N + n] = acc[i][j][r];
                 } else if (m < p.M) {
                     float v = p.alpha * acc[i][j][r];
-                    if (p.bias) v += p.bias[m];
+                    if (FULL) v += bq[i][r >> 2][r & 3];
+                    else if (p.bias) v += p.bias[m];
                     if (RES) v += p.R[(long long)m * p.ldr + n];
                     if (EPI != EPI_COLSTAT) p.C[(long long)m * p.ldc + n] = v;   // COLSTAT stores below
                     acc[i][j][r] = v;
@@ -425,7 +440,7 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
     const int b_contig = b_nk ? g.K : g.N;
     const bool vec = a_contig % 4 == 0 && b_contig % 4 == 0 && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
                      aligned16(g.A) && aligned16(g.B);
-    const bool full = vec && g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0;
+    const bool full = vec && g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0 && (!g.bias || aligned16(g.bias));
     const dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)p.ksplit);
     const bool res = g.R != nullptr;
     if (g.colstat || g.bsoft) {
