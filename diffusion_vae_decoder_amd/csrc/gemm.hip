@@ -12,7 +12,9 @@
 // 2 x 2 v_mfma_f32_32x32x2_f32 tiles.  Lane half h of a wave carries the K
 // indices [8h, 8h + 8) of a chunk.  When every tile is full (M, N multiples
 // of 128, K of 16, float4-aligned operands and bias) the operand loads walk
-// precomputed pointers with no bounds checks.
+// precomputed pointers with no bounds checks, each 2-deep K step's LDS
+// operands are read while the previous step's MFMAs run, and the epilogue
+// stores through buffer resources (row offsets in scalar registers).
 //
 // Problems whose tiles cannot fill the GPU (the small attentions) split K
 // into ranges of at least 8 chunks; each split stores raw partial sums and
@@ -50,6 +52,7 @@ struct Params {
     const floatx2 *bsblk;   // B_SOFTMAX: the block statistics EPI_COLSTAT wrote for B
     float *part;       // split K: partial sums [ksplit][M][N]
     int M, N, K, ksplit;
+    int buf_epi;       // full tiles: C (and R) within 32-bit byte offsets of a tile's first row
     long long lda, ldb, ldc, ldr;
     float alpha;
 };
@@ -239,15 +242,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         }
         const float *a = As[buf];
         const float *b = Bs[buf];
+        // the operands of step s + 1 are read while step s's MFMAs run (left
+        // to itself the compiler read each step's operands into the same four
+        // registers and waited for them right before its MFMAs)
+        float a0 = a[a_off], a1 = a[a_off + 32], b0 = b[b_off], b1 = b[b_off + 32];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const float a0 = a[a_off + s * LD], a1 = a[a_off + s * LD + 32];
-            const float b0 = b[b_off + s * LD], b1 = b[b_off + s * LD + 32];
+            float a0n = 0.f, a1n = 0.f, b0n = 0.f, b1n = 0.f;
+            if (s < 7) {
+                a0n = a[a_off + (s + 1) * LD];
+                a1n = a[a_off + (s + 1) * LD + 32];
+                b0n = b[b_off + (s + 1) * LD];
+                b1n = b[b_off + (s + 1) * LD + 32];
+            }
             acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
             acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
             acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
             acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+            a0 = a0n; a1 = a1n; b0 = b0n; b1 = b1n;
         }
+        // order: the reads of steps 0 and 1, then per step its four MFMAs
+        // followed by the reads of the step after next
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int s = 0; s < 7; ++s) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            if (s < 6) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         if (it + 1 < n_iter) {
             if (BSM) {
                 const int k1 = kb + (it + 1) * BK;
@@ -275,6 +297,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             for (int g = 0; g < 4; ++g)
                 bq[i][g] = p.bias ? *reinterpret_cast<const floatx4 *>(p.bias + m0 + wm * 64 + i * 32 + 8 * g + 4 * half)
                                   : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (FULL && !SPLIT && EPI == EPI_STORE) {
+        if (p.buf_epi) {
+            // stores through buffer resources: the row offset of each
+            // register (uniform) in a scalar offset, the lane's column and
+            // row half in the vector offset, no per-element address arithmetic
+            const long long r0 = m0 + wm * 64, c0 = n0 + wn * 64;
+            const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+                p.C + r0 * p.ldc + c0, (short)0, (int)((64 * p.ldc + 64) * 4), 0x00020000);
+            __amdgpu_buffer_rsrc_t rr = cr;
+            if (RES)
+                rr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.R) + r0 * p.ldr + c0, (short)0,
+                                                       (int)((64 * p.ldr + 64) * 4), 0x00020000);
+            const int vc = (int)((4 * half * p.ldc + l32) * 4), vr = RES ? (int)((4 * half * p.ldr + l32) * 4) : 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = i * 32 + 8 * (r >> 2) + (r & 3);
+                        float v = p.alpha * acc[i][j][r] + bq[i][r >> 2][r & 3];
+                        if (RES)
+                            v += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                rr, vr, (int)((row * p.ldr + j * 32) * 4), 0));
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), cr, vc,
+                                                                  (int)((row * p.ldc + j * 32) * 4), 0);
+                    }
+            return;
+        }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -441,6 +493,7 @@ int32_t launch_gemm(const GemmLaunch &g, hipStream_t s) {
     const bool vec = a_contig % 4 == 0 && b_contig % 4 == 0 && g.lda % 4 == 0 && g.ldb % 4 == 0 &&
                      aligned16(g.A) && aligned16(g.B);
     const bool full = vec && g.M % BM == 0 && g.N % BN == 0 && g.K % BK == 0 && (!g.bias || aligned16(g.bias));
+    p.buf_epi = g.ldc * 256 + 256 < (1LL << 31) && (!g.R || g.ldr * 256 + 256 < (1LL << 31));
     const dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), (unsigned)p.ksplit);
     const bool res = g.R != nullptr;
     if (g.colstat || g.bsoft) {
