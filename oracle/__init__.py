@@ -6,6 +6,8 @@ import this package.  The product path never does.
 from .vae_oracle import (  # noqa: F401
     EPS,
     GROUPS,
+    TILE,
+    TILE_OVERLAP_MIN,
     attention,
     causal_stack,
     conv2d,
@@ -14,6 +16,7 @@ from .vae_oracle import (  # noqa: F401
     conv3d_causal_at,
     decode,
     decode_causal3d,
+    decode_tiled,
     denormalize,
     group_norm,
     group_norm_silu,
@@ -22,5 +25,6 @@ from .vae_oracle import (  # noqa: F401
     resnet_causal3d,
     silu,
     softmax_rows,
+    split_tiles,
     upsample_nearest2x,
 )

@@ -32,7 +32,10 @@ document with its reason):
   * the causal 3-D decoder is the decoder chain with every 3x3 conv a causal
     3x3x3 conv, attention over all positions of the clip and upsampling in
     height and width only (the pages name the 3-D causal conv and its time
-    padding, nothing more).
+    padding, nothing more);
+  * the tiled decode is the tiling of [vae3d] (VideoVae's tile schedule,
+    cross-fade and crop) applied unchanged to this decoder, with the 8 pixels
+    of a latent cell as the schedule's step.
 """
 from __future__ import annotations
 
@@ -367,3 +370,84 @@ def conv3d_causal_at(x, w, b, o: int, t: int, i: int, j: int) -> float:
                 if 0 <= yy < h and 0 <= xx < wd:
                     acc += float(w[o, :, dt, dy, dx] @ _f64(x[:, tt, yy, xx]))
     return acc
+
+
+# --------------------------------------------------------------------------
+# Tiled decode ([vae3d]: the constants TILE and TILE_OVERLAP_MIN, split_tiles,
+# VideoVae::decode_clip and blend).
+
+TILE = 256           # pixel edge of a tile
+TILE_OVERLAP_MIN = 64
+
+
+def split_tiles(length: int, ratio: int, tile: int = TILE, overlap_min: int = TILE_OVERLAP_MIN):
+    """Tile schedule along one pixel axis ([vae3d] split_tiles): every tile is
+    exactly ``tile`` long, or one tile covers an axis no longer than that.
+    The tile count is the smallest for which tiles overlapping by
+    ``overlap_min`` cover the axis; the length left over is then handed to the
+    overlaps ``ratio`` pixels (one latent cell) at a time, cycling from the
+    first overlap, so the count stays and the overlaps grow.  Tile ``k + 1``
+    starts ``tile - overlaps[k]`` after tile ``k``.  Returns
+    ``(starts, lengths, overlaps)``."""
+    if tile >= length:
+        return [0], [length], []
+    if overlap_min >= tile:
+        raise ValueError("the overlap must be shorter than a tile")
+    n = -(-length // tile)
+    while n * tile < (n - 1) * overlap_min + length:
+        n += 1
+    overlaps = [overlap_min] * (n - 1)
+    for step in range((n * tile - (n - 1) * overlap_min - length) // ratio):
+        overlaps[step % (n - 1)] += ratio
+    starts = [0]
+    for ov in overlaps:
+        starts.append(starts[-1] + tile - ov)
+    return starts, [tile] * n, overlaps
+
+
+def decode_tiled(z, p: dict, scaling_factor: float, shift_factor: float, tile: int = TILE,
+                 overlap_min: int = TILE_OVERLAP_MIN, scale: int = 8, decode_fn=None) -> np.ndarray:
+    """The decoder run tile by tile ([vae3d] VideoVae::decode_clip, blend):
+    the output plane ``[8h, 8w]`` is cut by :func:`split_tiles` along each
+    axis (step ``scale``, the pixels per latent cell), each tile's latent
+    block is decoded on its own, and the tiles are assembled in row-major
+    order.  A tile's first ``e`` rows (``e`` = its overlap with the tile above)
+    become ``(1 - k/e) * above + (k/e) * tile`` for row ``k``, ``above`` being
+    the last ``e`` rows of the tile above as decoded (before its own blends);
+    then its first ``e'`` columns likewise with the last ``e'`` columns of the
+    decoded tile to its left.  Each tile then drops its trailing overlap rows
+    and columns (not the last tile of a column or row) and the rest is placed
+    at the tile's start, so each output pixel comes from one tile.
+    ``decode_fn(latent_block)`` decodes one block (default: :func:`decode`
+    with the given parameters)."""
+    if decode_fn is None:
+        def decode_fn(block):
+            return decode(block, p, scaling_factor, shift_factor)
+    z = _f64(z)
+    h, w = z.shape[-2:]
+    H, W = h * scale, w * scale
+    ys, yl, yo = split_tiles(H, scale, tile, overlap_min)
+    xs, xl, xo = split_tiles(W, scale, tile, overlap_min)
+    raw = {}
+    for i, (y0, th) in enumerate(zip(ys, yl)):
+        for j, (x0, tw) in enumerate(zip(xs, xl)):
+            raw[i, j] = _f64(decode_fn(z[..., y0 // scale:(y0 + th) // scale, x0 // scale:(x0 + tw) // scale]))
+    out = np.zeros(raw[0, 0].shape[:-2] + (H, W))
+    for i in range(len(ys)):
+        for j in range(len(xs)):
+            t = raw[i, j].copy()
+            th, tw = yl[i], xl[j]
+            if i > 0:
+                e = yo[i - 1]
+                k = np.arange(e) / e
+                above = raw[i - 1, j][..., yl[i - 1] - e:, :]
+                t[..., :e, :] = above * (1 - k)[:, None] + t[..., :e, :] * k[:, None]
+            if j > 0:
+                e = xo[j - 1]
+                k = np.arange(e) / e
+                left = raw[i, j - 1][..., :, xl[j - 1] - e:]
+                t[..., :, :e] = left * (1 - k) + t[..., :, :e] * k
+            kh = th - yo[i] if i + 1 < len(ys) else th
+            kw = tw - xo[j] if j + 1 < len(xs) else tw
+            out[..., ys[i]:ys[i] + kh, xs[j]:xs[j] + kw] = t[..., :kh, :kw]
+    return out
