@@ -25,6 +25,9 @@ the device and the latent already resident in HBM.  Default workload: latent
                with the CPU model and thread count; `secondary_sample` times
                conv_in + the first mid resnet of the 1024x1024 decode
   secondary    the 256x256 decode (latent [16,32,32])
+  tiled        the main latent decoded in 256-pixel tiles with overlaps of at
+               least 64 (vae_decode_tiled), with its workspace beside the
+               whole-image decode's
   sweep        the single-layer sweep at full size (3x3 and 1x1 convs,
                GroupNorm+SiLU) and a standalone nearest-x2 upsample
   stack3d      the causal 3-D conv stack on [128,17,256,256]
@@ -60,7 +63,7 @@ def parse():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the second decode size (keeps profiler summaries to one workload)")
+                    help="skip the second decode size and the tiled decode (keeps profiler summaries to one workload)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the single-layer sweep")
     ap.add_argument("--no-3d", action="store_true", help="skip the causal 3-D stack and decode")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timings")
@@ -480,6 +483,30 @@ def secondary(dec, args, h2: int) -> dict:
             "conv3x3_frac_fp32_mfma_peak": cr["frac_fp32_mfma_peak"]}
 
 
+def tiled(dec, args, h: int, tile: int = 256, overlap: int = 64) -> dict:
+    """The same latent decoded in tiles (vae_decode_tiled: the pages' 256-pixel
+    tiles with overlaps of at least 64): W warm-ups, then K timed tiled decodes
+    (events around the whole call on the current stream), and the workspace
+    the tiled and the whole-image decode need."""
+    import torch
+    z = torch.from_numpy(vaegen.latent(args.seed, h, h)).cuda()
+    rgb = torch.empty(dec.output_shape(h, h), dtype=torch.float32, device="cuda")
+    for _ in range(max(args.warmup, 1)):
+        dec.decode_tiled(z, tile, overlap, out=rgb)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dec.decode_tiled(z, tile, overlap, out=rgb)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"workload": f"decode latent [16,{h},{h}] -> RGB [3,{8 * h},{8 * h}] in {tile}-pixel tiles, "
+                        f"overlap >= {overlap}",
+            "ms_per_step": e0.elapsed_time(e1) / args.steps,
+            "workspace_bytes": dec.tiled_workspace_bytes(h, h, tile, overlap),
+            "whole_image_workspace_bytes": dec.workspace_bytes(h, h)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -591,6 +618,7 @@ def main():
     # secondary: the other decode size the metric names (after the timed region)
     if not args.no_secondary:
         out["secondary"] = secondary(dec, args, 32 if h != 32 else 128)
+        out["tiled"] = tiled(dec, args, h)
     if not args.no_sweep:
         out["sweep"] = sweep(args)
     if not args.no_3d:

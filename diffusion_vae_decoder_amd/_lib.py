@@ -23,7 +23,7 @@ VAE_ERR_INVALID_ARG = -1
 VAE_ERR_UNSUPPORTED = -2
 VAE_ERR_WORKSPACE = -3
 VAE_ERR_HIP = -4
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class VaeConv(ctypes.Structure):
@@ -104,6 +104,9 @@ SIGNATURES = {
     "vae_decoder3d_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32, POINTER(c_size_t)]),
     "vae_decode3d": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_size_t,
                                c_void_p]),
+    "vae_decoder_tiled_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(c_size_t)]),
+    "vae_decode_tiled": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                   c_size_t, c_void_p]),
     "vae_decoder_output_shape": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32),
                                            POINTER(c_int32)]),
     "vae_decoder_destroy": (None, [c_void_p]),

@@ -396,6 +396,27 @@ class Decoder:
                                        self._ws.numel(), _stream()))
         return rgb
 
+    def tiled_workspace_bytes(self, h: int, w: int, tile: int = 256, overlap: int = 64) -> int:
+        nb = c_size_t()
+        check(self._lib.vae_decoder_tiled_workspace_bytes(self._h, h, w, tile, overlap, byref(nb)))
+        return nb.value
+
+    def decode_tiled(self, latent: torch.Tensor, tile: int = 256, overlap: int = 64,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """latent [c, h, w] -> rgb [3, 8h, 8w], decoded in tiles of `tile`
+        output pixels overlapping by at least `overlap` (vae_decode_tiled)."""
+        self._check_latent(latent)
+        if self.causal3d:
+            raise ValueError("decode_tiled: a 2-D decoder only")
+        c, h, w = latent.shape
+        nb = self.tiled_workspace_bytes(h, w, tile, overlap)
+        ws = torch.empty(nb, dtype=torch.uint8, device=latent.device)
+        co, ho, wo = self.output_shape(h, w)
+        rgb = _out(out, (co, ho, wo), latent.device)
+        check(self._lib.vae_decode_tiled(self._h, latent.data_ptr(), h, w, tile, overlap, rgb.data_ptr(),
+                                         ws.data_ptr(), ws.numel(), _stream()))
+        return rgb
+
     def _check_latent(self, latent) -> None:
         if not isinstance(latent, torch.Tensor):
             raise TypeError("latent must be a torch.Tensor")

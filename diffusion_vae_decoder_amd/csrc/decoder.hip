@@ -731,6 +731,132 @@ int32_t decode_t(vae_decoder *d, const float *latent, int T, int h, int w, float
 
 }  // namespace
 
+// ---------------------------------------------------------------- tiled decode
+// The tiling of the video VAE in cortiq-engine 0.8.78 `vae3d.rs` (the
+// constants TILE and TILE_OVERLAP_MIN, split_tiles, VideoVae::decode_clip and
+// blend), applied to this decoder: the output plane is cut into tiles of a
+// fixed pixel edge along each axis, each tile's latent block is decoded on
+// its own, and the decoded tiles are assembled with a linear cross-fade
+// across their overlaps.
+namespace {
+
+constexpr int kMaxTiles = 64;   // tiles along one axis
+
+// One axis of the schedule (split_tiles): every tile `len` pixels long (one
+// tile of the whole axis when it is no longer than a tile); the fewest tiles
+// that cover the axis with neighbours overlapping by `ov_min`, the length
+// left over then added to the overlaps one latent cell (`step` pixels) at a
+// time, from the first overlap on, cycling.  Tile k + 1 starts len - ov[k]
+// after tile k.
+struct TileAxis {
+    int n, len;
+    int start[kMaxTiles];
+    int ov[kMaxTiles];   // overlap of tile k with tile k + 1
+};
+
+int32_t tile_axis(int length, int step, int tile, int ov_min, TileAxis &a, const char *who) {
+    a = TileAxis{};
+    if (tile >= length) {
+        a.n = 1;
+        a.len = length;
+        return VAE_OK;
+    }
+    long long n = (length + tile - 1) / tile;
+    while (n * tile < (n - 1) * ov_min + length) ++n;
+    if (n > kMaxTiles) return fail(VAE_ERR_UNSUPPORTED, "%s: %lld tiles along an axis (at most %d)", who, n, kMaxTiles);
+    a.n = (int)n;
+    a.len = tile;
+    for (int k = 0; k + 1 < a.n; ++k) a.ov[k] = ov_min;
+    const long long slack = n * tile - (n - 1) * ov_min - length;   // < tile - ov_min: n is the fewest
+    for (long long q = 0; q < slack / step; ++q) a.ov[q % (n - 1)] += step;
+    for (int k = 0; k + 1 < a.n; ++k) a.start[k + 1] = a.start[k] + tile - a.ov[k];
+    return VAE_OK;
+}
+
+// The latent block [c, bh, bw] at (r0, c0) of z [c, h, w].
+__global__ __launch_bounds__(256) void tile_extract(const float *__restrict__ z, int c, int h, int w, int r0, int c0,
+                                                    int bh, int bw, float *__restrict__ out) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long long)c * bh * bw) return;
+    const int x = (int)(i % bw);
+    const long long r = i / bw;
+    const int y = (int)(r % bh), ch = (int)(r / bh);
+    out[i] = z[((long long)ch * h + r0 + y) * w + c0 + x];
+}
+
+struct TileGrid {
+    TileAxis ys, xs;
+};
+
+// Output [C, H, W] from the decoded tiles raw[i][j][C][th][tw].  The tiles'
+// kept parts partition the plane: tile row i keeps rows [ys.start[i],
+// ys.start[i + 1]) (the last one to H), and so on for columns.  A pixel at
+// (hh, ww) of tile (i, j): the decoded value; within the overlap e with the
+// tile above, (1 - hh/e) * (that tile's row th - e + hh) + (hh/e) * value;
+// then within the overlap e' with the tile to the left, (1 - ww/e') * (that
+// tile's column tw - e' + ww, as decoded) + (ww/e') * value.  One thread per
+// output element; workgroup b covers 256 columns of row b / xchunks (c * H + y).
+__global__ __launch_bounds__(256) void tile_assemble(const float *__restrict__ raw, int C, int H, int W, int xchunks,
+                                                     TileGrid g, float *__restrict__ out) {
+    const int row = blockIdx.x / xchunks;
+    const int x = (blockIdx.x - row * xchunks) * 256 + threadIdx.x;
+    if (x >= W) return;
+    const int c = row / H, y = row - c * H;
+    int i = 0, j = 0;
+    while (i + 1 < g.ys.n && g.ys.start[i + 1] <= y) ++i;
+    while (j + 1 < g.xs.n && g.xs.start[j + 1] <= x) ++j;
+    const int th = g.ys.len, tw = g.xs.len;
+    const int hh = y - g.ys.start[i], ww = x - g.xs.start[j];
+    const long long plane = (long long)th * tw;
+    auto tile = [&](int ti, int tj) { return raw + ((long long)(ti * g.xs.n + tj) * C + c) * plane; };
+    float v = tile(i, j)[(long long)hh * tw + ww];
+    if (i > 0 && hh < g.ys.ov[i - 1]) {
+        const int e = g.ys.ov[i - 1];
+        const float wb = (float)hh / (float)e, wa = 1.f - wb;
+        v = tile(i - 1, j)[(long long)(th - e + hh) * tw + ww] * wa + v * wb;
+    }
+    if (j > 0 && ww < g.xs.ov[j - 1]) {
+        const int e = g.xs.ov[j - 1];
+        const float wb = (float)ww / (float)e, wa = 1.f - wb;
+        v = tile(i, j - 1)[(long long)hh * tw + tw - e + ww] * wa + v * wb;
+    }
+    out[(long long)row * W + x] = v;
+}
+
+struct TilePlan {
+    TileGrid g;
+    int scale, lat_c, out_c, bh, bw;   // a tile's latent block is bh x bw
+    size_t lat, stage, raw, dec;       // workspace segments (bytes)
+};
+
+int32_t tile_plan(const vae_decoder *d, int h, int w, int tile, int overlap, TilePlan &tp, const char *who) {
+    if (!d) return fail(VAE_ERR_INVALID_ARG, "%s: NULL decoder", who);
+    if (d->kt != 1) return fail(VAE_ERR_INVALID_ARG, "%s: a 3-D decoder", who);
+    if (h <= 0 || w <= 0) return fail(VAE_ERR_INVALID_ARG, "%s: sizes must be positive", who);
+    int32_t c, H, W;
+    vae_decoder_output_shape(d, h, w, &c, &H, &W);
+    const int scale = H / h;
+    if (tile <= 0 || overlap < 0 || overlap >= tile || tile % scale || overlap % scale)
+        return fail(VAE_ERR_INVALID_ARG,
+                    "%s: tile %d and overlap %d must be multiples of %d pixels with 0 <= overlap < tile", who, tile,
+                    overlap, scale);
+    int32_t rc;
+    if ((rc = tile_axis(H, scale, tile, overlap, tp.g.ys, who)) || (rc = tile_axis(W, scale, tile, overlap, tp.g.xs, who)))
+        return rc;
+    tp.scale = scale;
+    tp.lat_c = d->latent_c;
+    tp.out_c = c;
+    tp.bh = tp.g.ys.len / scale;
+    tp.bw = tp.g.xs.len / scale;
+    const size_t tpx = (size_t)tp.g.ys.len * tp.g.xs.len;
+    tp.lat = align256((size_t)tp.lat_c * tp.bh * tp.bw * 4);
+    tp.stage = align256((size_t)c * tpx * 4);
+    tp.raw = align256((size_t)tp.g.ys.n * tp.g.xs.n * c * tpx * 4);
+    return workspace_bytes_t(d, 1, tp.bh, tp.bw, &tp.dec, who);
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t vae_decoder_pack_bytes(const vae_weights *w, size_t *bytes) {
@@ -783,6 +909,54 @@ int32_t vae_decode3d(vae_decoder *d, const float *latent, int32_t t, int32_t h, 
                      size_t ws_bytes, void *stream) {
     if (d && d->kt != 3) return fail(VAE_ERR_INVALID_ARG, "vae_decode3d: not a 3-D decoder");
     return decode_t(d, latent, t, h, w, rgb, ws, ws_bytes, stream, "vae_decode3d");
+}
+
+int32_t vae_decoder_tiled_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, int32_t tile, int32_t overlap,
+                                          size_t *bytes) {
+    if (!bytes) return fail(VAE_ERR_INVALID_ARG, "vae_decoder_tiled_workspace_bytes: NULL pointer");
+    TilePlan tp;
+    const int32_t rc = tile_plan(d, h, w, tile, overlap, tp, "vae_decoder_tiled_workspace_bytes");
+    if (rc) return rc;
+    *bytes = tp.lat + tp.stage + tp.raw + tp.dec;
+    return VAE_OK;
+}
+
+int32_t vae_decode_tiled(vae_decoder *d, const float *latent, int32_t h, int32_t w, int32_t tile, int32_t overlap,
+                         float *rgb, void *ws, size_t ws_bytes, void *stream) {
+    const char *who = "vae_decode_tiled";
+    if (!latent || !rgb) return fail(VAE_ERR_INVALID_ARG, "%s: NULL pointer", who);
+    TilePlan tp;
+    int32_t rc = tile_plan(d, h, w, tile, overlap, tp, who);
+    if (rc) return rc;
+    const size_t need = tp.lat + tp.stage + tp.raw + tp.dec;
+    if (!ws || ws_bytes < need) return fail(VAE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", who, ws_bytes, need);
+    char *base = static_cast<char *>(ws);
+    float *lat = reinterpret_cast<float *>(base);
+    float *stage = reinterpret_cast<float *>(base + tp.lat);
+    float *raw = reinterpret_cast<float *>(base + tp.lat + tp.stage);
+    void *dws = base + tp.lat + tp.stage + tp.raw;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const TileGrid &g = tp.g;
+    const size_t tile_bytes = (size_t)tp.out_c * g.ys.len * g.xs.len * 4;
+    const long long lat_elems = (long long)tp.lat_c * tp.bh * tp.bw;
+    // every tile decodes from the same block buffer into the same staging
+    // buffer (one HIP graph serves them all when graphs are on), then moves
+    // to its own slot
+    for (int i = 0; i < g.ys.n; ++i)
+        for (int j = 0; j < g.xs.n; ++j) {
+            hipLaunchKernelGGL(tile_extract, dim3((unsigned)((lat_elems + 255) / 256)), dim3(256), 0, s, latent,
+                               tp.lat_c, h, w, g.ys.start[i] / tp.scale, g.xs.start[j] / tp.scale, tp.bh, tp.bw, lat);
+            if ((rc = check_launch("tile_extract"))) return rc;
+            if ((rc = decode_t(d, lat, 1, tp.bh, tp.bw, stage, dws, tp.dec, stream, who))) return rc;
+            if ((rc = hip_status(hipMemcpyAsync(reinterpret_cast<char *>(raw) + (size_t)(i * g.xs.n + j) * tile_bytes,
+                                                stage, tile_bytes, hipMemcpyDeviceToDevice, s),
+                                 "hipMemcpyAsync")))
+                return rc;
+        }
+    const int H = h * tp.scale, W = w * tp.scale, xchunks = (W + 255) / 256;
+    hipLaunchKernelGGL(tile_assemble, dim3((unsigned)((long long)tp.out_c * H * xchunks)), dim3(256), 0, s, raw, tp.out_c,
+                       H, W, xchunks, g, rgb);
+    return check_launch("tile_assemble");
 }
 
 int32_t vae_decoder_set_graph(vae_decoder *d, int32_t on) {

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 9
+#define VAE_ABI_VERSION 10
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -315,6 +315,35 @@ int32_t vae_decoder3d_workspace_bytes(const vae_decoder *d, int32_t t, int32_t h
 /* latent [latent_channels, t, h, w] -> rgb [out_channels, t, 8h, 8w]. */
 int32_t vae_decode3d(vae_decoder *d, const float *latent, int32_t t, int32_t h, int32_t w, float *rgb,
                      void *ws, size_t ws_bytes, void *stream);
+
+/* Tiled decode: the tiling of the video VAE in cortiq-engine 0.8.78
+ * `vae3d.rs` (constants TILE = 256 and TILE_OVERLAP_MIN = 64, split_tiles,
+ * VideoVae::decode_clip, blend) applied to this 2-D decoder, for outputs whose
+ * whole-image workspace is too large.  Along each axis of the [8h, 8w] output
+ * the tiles are `tile` pixels long (one tile if the axis is no longer); their
+ * count is the fewest that cover the axis with neighbours overlapping by
+ * `overlap` pixels, and the length left over widens the overlaps one latent
+ * cell (8 pixels) at a time, from the first overlap on, cycling.  Each tile's
+ * latent block is decoded on its own (vae_decode, graph mode and attention
+ * form as set on `d`); tile (i, j) then cross-fades its first rows into the
+ * last rows of the decoded tile above, weight k/e for row k of an overlap of
+ * e rows, and its first columns likewise into the decoded tile to its left,
+ * and keeps the part before the next tiles start (the last tile of a row or
+ * column keeps the rest), so each output pixel is written once.
+ *   latent [latent_channels, h, w], rgb [out_channels, 8h, 8w] (device);
+ *   tile, overlap  pixels, multiples of 8, 0 <= overlap < tile (the pages:
+ *                  256 and 64); at most 64 tiles per axis;
+ *   ws   >= vae_decoder_tiled_workspace_bytes(...) device bytes: one tile's
+ *        latent block, its decode workspace and every decoded tile
+ *        (ny x nx x out_channels x tile x tile floats), owned by the caller.
+ * A 2-D decoder only.  VAE_ERR_INVALID_ARG for bad sizes, VAE_ERR_UNSUPPORTED
+ * beyond 64 tiles per axis, VAE_ERR_WORKSPACE for a short workspace, all
+ * before any launch.  A single tile (tile >= 8h and 8w) gives vae_decode's
+ * result exactly. */
+int32_t vae_decoder_tiled_workspace_bytes(const vae_decoder *d, int32_t h, int32_t w, int32_t tile, int32_t overlap,
+                                          size_t *bytes);
+int32_t vae_decode_tiled(vae_decoder *d, const float *latent, int32_t h, int32_t w, int32_t tile, int32_t overlap,
+                         float *rgb, void *ws, size_t ws_bytes, void *stream);
 
 /* Output spatial scale of the chain (8 for four up blocks) and its channels. */
 int32_t vae_decoder_output_shape(const vae_decoder *d, int32_t h, int32_t w, int32_t *c,

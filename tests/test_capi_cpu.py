@@ -270,6 +270,10 @@ def test_decoder_pack_and_validation(lib):
     w6.n_up = 0
     assert lib.vae_decoder_pack_bytes(byref(w6), byref(nb)) == VAE_ERR_INVALID_ARG
     assert lib.vae_decode(NULL, FAKE, 8, 8, FAKE, FAKE, 1, NULL) == VAE_ERR_INVALID_ARG
+    nb0 = c_size_t()
+    assert lib.vae_decoder_tiled_workspace_bytes(NULL, 8, 8, 256, 64, byref(nb0)) == VAE_ERR_INVALID_ARG
+    assert lib.vae_decode_tiled(NULL, FAKE, 8, 8, 256, 64, FAKE, FAKE, 1, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_decode_tiled(NULL, NULL, 8, 8, 256, 64, FAKE, FAKE, 1, NULL) == VAE_ERR_INVALID_ARG
     assert lib.vae_decoder_set_profiling(NULL, 1) == VAE_ERR_INVALID_ARG
 
 
