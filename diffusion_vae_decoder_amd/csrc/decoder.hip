@@ -253,6 +253,15 @@ struct vae_decoder {
     bool profiling = false;
     std::vector<ProfEntry> prof;
     size_t prof_used = 0;
+    // streams of the tiled decode's concurrent tiles (created on first use,
+    // default priority), and the events that fork them from and join them to
+    // the caller's stream
+    static constexpr int kTileStreams = 3;
+    struct TileStreams {
+        bool made = false;
+        hipStream_t s[kTileStreams] = {};
+        hipEvent_t fork = nullptr, join[kTileStreams] = {};
+    } tiles;
 };
 
 namespace {
@@ -823,10 +832,13 @@ __global__ __launch_bounds__(256) void tile_assemble(const float *__restrict__ r
     out[(long long)row * W + x] = v;
 }
 
+// Workspace: the decoded tiles, a staging tile, and per concurrent stream a
+// latent block and a decode workspace.
 struct TilePlan {
     TileGrid g;
     int scale, lat_c, out_c, bh, bw;   // a tile's latent block is bh x bw
-    size_t lat, stage, raw, dec;       // workspace segments (bytes)
+    size_t lat, stage, raw, dec;       // workspace segments (bytes; lat and dec per stream)
+    size_t total() const { return raw + stage + vae_decoder::kTileStreams * (lat + dec); }
 };
 
 int32_t tile_plan(const vae_decoder *d, int h, int w, int tile, int overlap, TilePlan &tp, const char *who) {
@@ -917,7 +929,7 @@ int32_t vae_decoder_tiled_workspace_bytes(const vae_decoder *d, int32_t h, int32
     TilePlan tp;
     const int32_t rc = tile_plan(d, h, w, tile, overlap, tp, "vae_decoder_tiled_workspace_bytes");
     if (rc) return rc;
-    *bytes = tp.lat + tp.stage + tp.raw + tp.dec;
+    *bytes = tp.total();
     return VAE_OK;
 }
 
@@ -928,31 +940,69 @@ int32_t vae_decode_tiled(vae_decoder *d, const float *latent, int32_t h, int32_t
     TilePlan tp;
     int32_t rc = tile_plan(d, h, w, tile, overlap, tp, who);
     if (rc) return rc;
-    const size_t need = tp.lat + tp.stage + tp.raw + tp.dec;
+    const size_t need = tp.total();
     if (!ws || ws_bytes < need) return fail(VAE_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", who, ws_bytes, need);
     char *base = static_cast<char *>(ws);
-    float *lat = reinterpret_cast<float *>(base);
-    float *stage = reinterpret_cast<float *>(base + tp.lat);
-    float *raw = reinterpret_cast<float *>(base + tp.lat + tp.stage);
-    void *dws = base + tp.lat + tp.stage + tp.raw;
+    float *raw = reinterpret_cast<float *>(base);
+    float *stage = reinterpret_cast<float *>(base + tp.raw);
+    auto lat = [&](int k) { return reinterpret_cast<float *>(base + tp.raw + tp.stage + k * (tp.lat + tp.dec)); };
+    auto dws = [&](int k) { return static_cast<void *>(base + tp.raw + tp.stage + k * (tp.lat + tp.dec) + tp.lat); };
     hipStream_t s = static_cast<hipStream_t>(stream);
     const TileGrid &g = tp.g;
+    const int ntiles = g.ys.n * g.xs.n;
     const size_t tile_bytes = (size_t)tp.out_c * g.ys.len * g.xs.len * 4;
     const long long lat_elems = (long long)tp.lat_c * tp.bh * tp.bw;
-    // every tile decodes from the same block buffer into the same staging
-    // buffer (one HIP graph serves them all when graphs are on), then moves
-    // to its own slot
-    for (int i = 0; i < g.ys.n; ++i)
-        for (int j = 0; j < g.xs.n; ++j) {
-            hipLaunchKernelGGL(tile_extract, dim3((unsigned)((lat_elems + 255) / 256)), dim3(256), 0, s, latent,
-                               tp.lat_c, h, w, g.ys.start[i] / tp.scale, g.xs.start[j] / tp.scale, tp.bh, tp.bw, lat);
-            if ((rc = check_launch("tile_extract"))) return rc;
-            if ((rc = decode_t(d, lat, 1, tp.bh, tp.bw, stage, dws, tp.dec, stream, who))) return rc;
-            if ((rc = hip_status(hipMemcpyAsync(reinterpret_cast<char *>(raw) + (size_t)(i * g.xs.n + j) * tile_bytes,
-                                                stage, tile_bytes, hipMemcpyDeviceToDevice, s),
+    auto slot = [&](int t) { return reinterpret_cast<float *>(reinterpret_cast<char *>(raw) + (size_t)t * tile_bytes); };
+    auto extract = [&](int t, float *dst, hipStream_t st) {
+        const int i = t / g.xs.n, j = t - i * g.xs.n;
+        hipLaunchKernelGGL(tile_extract, dim3((unsigned)((lat_elems + 255) / 256)), dim3(256), 0, st, latent,
+                           tp.lat_c, h, w, g.ys.start[i] / tp.scale, g.xs.start[j] / tp.scale, tp.bh, tp.bw, dst);
+        return check_launch("tile_extract");
+    };
+    // Tiles decode concurrently on the decoder's own streams unless the
+    // decode is profiled (the records are the handle's), graph replay is on
+    // (one graph serves the tiles) or the caller's stream is being captured.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (s && (rc = hip_status(hipStreamIsCapturing(s, &cs), "hipStreamIsCapturing"))) return rc;
+    const int nk = (d->profiling || d->graph.on || cs != hipStreamCaptureStatusNone || ntiles < 2)
+                       ? 1 : (ntiles < vae_decoder::kTileStreams ? ntiles : vae_decoder::kTileStreams);
+    if (nk == 1) {
+        // every tile decodes from one block buffer into one staging buffer
+        // (one HIP graph serves them all when graphs are on), then moves to its slot
+        for (int t = 0; t < ntiles; ++t) {
+            if ((rc = extract(t, lat(0), s))) return rc;
+            if ((rc = decode_t(d, lat(0), 1, tp.bh, tp.bw, stage, dws(0), tp.dec, stream, who))) return rc;
+            if ((rc = hip_status(hipMemcpyAsync(slot(t), stage, tile_bytes, hipMemcpyDeviceToDevice, s),
                                  "hipMemcpyAsync")))
                 return rc;
         }
+    } else {
+        vae_decoder::TileStreams &ts = d->tiles;
+        if (!ts.made) {
+            for (int k = 0; k < vae_decoder::kTileStreams; ++k) {
+                if ((rc = hip_status(hipStreamCreateWithFlags(&ts.s[k], hipStreamNonBlocking), "hipStreamCreateWithFlags")))
+                    return rc;
+                if ((rc = hip_status(hipEventCreateWithFlags(&ts.join[k], hipEventDisableTiming), "hipEventCreateWithFlags")))
+                    return rc;
+            }
+            if ((rc = hip_status(hipEventCreateWithFlags(&ts.fork, hipEventDisableTiming), "hipEventCreateWithFlags")))
+                return rc;
+            ts.made = true;
+        }
+        if ((rc = hip_status(hipEventRecord(ts.fork, s), "hipEventRecord"))) return rc;
+        for (int k = 0; k < nk; ++k)
+            if ((rc = hip_status(hipStreamWaitEvent(ts.s[k], ts.fork, 0), "hipStreamWaitEvent"))) return rc;
+        // tile t on stream t % nk, decoded straight into its slot
+        for (int t = 0; t < ntiles; ++t) {
+            const int k = t % nk;
+            if ((rc = extract(t, lat(k), ts.s[k]))) return rc;
+            if ((rc = run_chain(d, lat(k), 1, tp.bh, tp.bw, slot(t), dws(k), ts.s[k]))) return rc;
+        }
+        for (int k = 0; k < nk; ++k) {
+            if ((rc = hip_status(hipEventRecord(ts.join[k], ts.s[k]), "hipEventRecord"))) return rc;
+            if ((rc = hip_status(hipStreamWaitEvent(s, ts.join[k], 0), "hipStreamWaitEvent"))) return rc;
+        }
+    }
     const int H = h * tp.scale, W = w * tp.scale, xchunks = (W + 255) / 256;
     hipLaunchKernelGGL(tile_assemble, dim3((unsigned)((long long)tp.out_c * H * xchunks)), dim3(256), 0, s, raw, tp.out_c,
                        H, W, xchunks, g, rgb);
@@ -973,6 +1023,14 @@ int32_t vae_decoder_set_graph(vae_decoder *d, int32_t on) {
 void vae_decoder_destroy(vae_decoder *d) {
     if (!d) return;
     if (d->graph.exec) (void)hipGraphExecDestroy(d->graph.exec);
+    if (d->tiles.made) {
+        for (int k = 0; k < vae_decoder::kTileStreams; ++k) {
+            (void)hipStreamSynchronize(d->tiles.s[k]);
+            (void)hipStreamDestroy(d->tiles.s[k]);
+            (void)hipEventDestroy(d->tiles.join[k]);
+        }
+        (void)hipEventDestroy(d->tiles.fork);
+    }
     for (ProfEntry &e : d->prof) {
         if (e.start) (void)hipEventDestroy(e.start);
         if (e.stop) (void)hipEventDestroy(e.stop);

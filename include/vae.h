@@ -333,9 +333,16 @@ int32_t vae_decode3d(vae_decoder *d, const float *latent, int32_t t, int32_t h, 
  *   latent [latent_channels, h, w], rgb [out_channels, 8h, 8w] (device);
  *   tile, overlap  pixels, multiples of 8, 0 <= overlap < tile (the pages:
  *                  256 and 64); at most 64 tiles per axis;
- *   ws   >= vae_decoder_tiled_workspace_bytes(...) device bytes: one tile's
- *        latent block, its decode workspace and every decoded tile
- *        (ny x nx x out_channels x tile x tile floats), owned by the caller.
+ *   ws   >= vae_decoder_tiled_workspace_bytes(...) device bytes: every
+ *        decoded tile (ny x nx x out_channels x tile x tile floats), a staging
+ *        tile, and for each of three concurrent tile decodes a latent block and
+ *        a decode workspace; owned by the caller.
+ * With graph mode and profiling off and `stream` not being captured, the tiles
+ * decode three at a time on streams the handle creates on first use (default
+ * priority, destroyed with the handle), forked from and joined back to
+ * `stream` by events, so the call is ordered on `stream` like any other; else
+ * one after another on `stream`.  Calls on one handle from several host
+ * threads at once race.
  * A 2-D decoder only.  VAE_ERR_INVALID_ARG for bad sizes, VAE_ERR_UNSUPPORTED
  * beyond 64 tiles per axis, VAE_ERR_WORKSPACE for a short workspace, all
  * before any launch.  A single tile (tile >= 8h and 8w) gives vae_decode's

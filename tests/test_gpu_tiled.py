@@ -73,6 +73,28 @@ def test_tiled_decode_in_graph_mode_matches_eager(decoder):
         decoder.set_graph(False)
 
 
+def test_concurrent_tiles_equal_sequential_tiles(decoder):
+    # 3 x 2 tiles: by default they decode on the handle's three streams; with
+    # profiling on, one after another on the caller's stream.  Both run the
+    # same kernels on the same blocks, so the results agree bit for bit, also
+    # when the caller's stream is a side stream and when the call repeats.
+    z = dev(vaegen.latent(15, 9, 5))
+    conc = host(decoder.decode_tiled(z, 32, 8))
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            out = decoder.decode_tiled(z, 32, 8)
+    side.synchronize()
+    np.testing.assert_array_equal(host(out), conc)
+    decoder.set_profiling(True)
+    try:
+        seq = host(decoder.decode_tiled(z, 32, 8))
+        assert len(decoder.profile()) > 0
+    finally:
+        decoder.set_profiling(False)
+    np.testing.assert_array_equal(seq, conc)
+
+
 def test_tiled_decode_512_against_stored_oracle(decoder):
     # stored oracle values (tests/golden/make_golden.py): 3 x 3 tiles of 256
     # pixels overlapping by 128; rows and columns at and around every tile
