@@ -28,6 +28,8 @@ constexpr int kGroups = 32;
 constexpr int kMaxParts = 64;
 constexpr long long kPartElems = 16384;   // group elements per stats workgroup, at least
 constexpr int kApplyElems = 4096;         // elements per apply workgroup (16 per thread)
+constexpr int kApplyBatch = kApplyElems / (4 * kThreads);   // float4 loads in flight per apply thread
+constexpr int kStatsBatch = 8;            // float4 loads in flight per statistics thread
 constexpr int kInlineRecords = 512;       // producer records per group an apply workgroup merges itself
 
 int parts_for(long long gsize) {
@@ -75,12 +77,24 @@ __global__ __launch_bounds__(kThreads) void gn_stats(const float *__restrict__ x
     double s1 = 0.0, s2 = 0.0;
     if (VEC) {
         const floatx4 *b4 = reinterpret_cast<const floatx4 *>(base);
-        for (long long i = lo / 4 + threadIdx.x; i < hi / 4; i += kThreads) {
-            const floatx4 v = b4[i];
+        auto add = [&](const floatx4 &v) {
             const float d0 = v[0] - shift, d1 = v[1] - shift, d2 = v[2] - shift, d3 = v[3] - shift;
             s1 += (double)((d0 + d1) + (d2 + d3));
             s2 += (double)((d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3));
+        };
+        // kStatsBatch loads in flight per thread (one at a time, each waited
+        // for, leaves the pass latency-bound); the float4s are added in the
+        // same order as by the plain loop
+        long long i = lo / 4 + threadIdx.x;
+        const long long e = hi / 4;
+        for (; i + (kStatsBatch - 1) * kThreads < e; i += kStatsBatch * kThreads) {
+            floatx4 v[kStatsBatch];
+#pragma unroll
+            for (int k = 0; k < kStatsBatch; ++k) v[k] = b4[i + k * kThreads];
+#pragma unroll
+            for (int k = 0; k < kStatsBatch; ++k) add(v[k]);
         }
+        for (; i < e; i += kThreads) add(b4[i]);
     } else {
         for (long long i = lo + threadIdx.x; i < hi; i += kThreads) {
             const float d = base[i] - shift;
@@ -167,22 +181,36 @@ __global__ __launch_bounds__(kThreads) void gn_apply(const float *x, long long s
         const floatx4 *x4 = reinterpret_cast<const floatx4 *>(x + cbase);
         const floatx4 *r4 = reinterpret_cast<const floatx4 *>(res + cbase);
         floatx4 *y4 = reinterpret_cast<floatx4 *>(y + cbase);
-        for (long long i = lo / 4 + threadIdx.x; i < hi / 4; i += kThreads) {
-            const floatx4 v = x4[i];
+        auto out = [&](const floatx4 &v, const floatx4 &r) {
             floatx4 o;
             o[0] = f(v[0]);
             o[1] = f(v[1]);
             o[2] = f(v[2]);
             o[3] = f(v[3]);
             if (RES) {
-                const floatx4 r = r4[i];
                 o[0] += r[0];
                 o[1] += r[1];
                 o[2] += r[2];
                 o[3] += r[3];
             }
-            y4[i] = o;
+            return o;
+        };
+        // all of a thread's loads of a full chunk are issued before its first
+        // store (a wait for a load also waits for the stores before it); each
+        // element is still read before the same thread writes it, so y may be x
+        long long i = lo / 4 + threadIdx.x;
+        const long long e = hi / 4;
+        for (; i + (kApplyBatch - 1) * kThreads < e; i += kApplyBatch * kThreads) {
+            floatx4 v[kApplyBatch], r[kApplyBatch];
+#pragma unroll
+            for (int k = 0; k < kApplyBatch; ++k) {
+                v[k] = x4[i + k * kThreads];
+                if (RES) r[k] = r4[i + k * kThreads];
+            }
+#pragma unroll
+            for (int k = 0; k < kApplyBatch; ++k) y4[i + k * kThreads] = out(v[k], r[k]);
         }
+        for (; i < e; i += kThreads) y4[i] = out(x4[i], RES ? r4[i] : floatx4{});
     } else {
         for (long long i = lo + threadIdx.x; i < hi; i += kThreads) {
             float t = f(x[cbase + i]);
