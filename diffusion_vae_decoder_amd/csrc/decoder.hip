@@ -979,29 +979,43 @@ int32_t vae_decode_tiled(vae_decoder *d, const float *latent, int32_t h, int32_t
     } else {
         vae_decoder::TileStreams &ts = d->tiles;
         if (!ts.made) {
-            for (int k = 0; k < vae_decoder::kTileStreams; ++k) {
-                if ((rc = hip_status(hipStreamCreateWithFlags(&ts.s[k], hipStreamNonBlocking), "hipStreamCreateWithFlags")))
-                    return rc;
-                if ((rc = hip_status(hipEventCreateWithFlags(&ts.join[k], hipEventDisableTiming), "hipEventCreateWithFlags")))
-                    return rc;
+            for (int k = 0; k < vae_decoder::kTileStreams && rc == VAE_OK; ++k) {
+                rc = hip_status(hipStreamCreateWithFlags(&ts.s[k], hipStreamNonBlocking), "hipStreamCreateWithFlags");
+                if (rc == VAE_OK)
+                    rc = hip_status(hipEventCreateWithFlags(&ts.join[k], hipEventDisableTiming), "hipEventCreateWithFlags");
             }
-            if ((rc = hip_status(hipEventCreateWithFlags(&ts.fork, hipEventDisableTiming), "hipEventCreateWithFlags")))
+            if (rc == VAE_OK)
+                rc = hip_status(hipEventCreateWithFlags(&ts.fork, hipEventDisableTiming), "hipEventCreateWithFlags");
+            if (rc) {   // release what was made; the next call tries again
+                for (int k = 0; k < vae_decoder::kTileStreams; ++k) {
+                    if (ts.s[k]) (void)hipStreamDestroy(ts.s[k]);
+                    if (ts.join[k]) (void)hipEventDestroy(ts.join[k]);
+                    ts.s[k] = nullptr;
+                    ts.join[k] = nullptr;
+                }
+                if (ts.fork) (void)hipEventDestroy(ts.fork);
+                ts.fork = nullptr;
                 return rc;
+            }
             ts.made = true;
         }
         if ((rc = hip_status(hipEventRecord(ts.fork, s), "hipEventRecord"))) return rc;
         for (int k = 0; k < nk; ++k)
             if ((rc = hip_status(hipStreamWaitEvent(ts.s[k], ts.fork, 0), "hipStreamWaitEvent"))) return rc;
-        // tile t on stream t % nk, decoded straight into its slot
-        for (int t = 0; t < ntiles; ++t) {
+        // tile t on stream t % nk, decoded straight into its slot; the
+        // caller's stream joins the streams even after a failed launch, so
+        // nothing that was enqueued outlives the caller's view of the call
+        for (int t = 0; t < ntiles && rc == VAE_OK; ++t) {
             const int k = t % nk;
-            if ((rc = extract(t, lat(k), ts.s[k]))) return rc;
-            if ((rc = run_chain(d, lat(k), 1, tp.bh, tp.bw, slot(t), dws(k), ts.s[k]))) return rc;
+            rc = extract(t, lat(k), ts.s[k]);
+            if (rc == VAE_OK) rc = run_chain(d, lat(k), 1, tp.bh, tp.bw, slot(t), dws(k), ts.s[k]);
         }
         for (int k = 0; k < nk; ++k) {
-            if ((rc = hip_status(hipEventRecord(ts.join[k], ts.s[k]), "hipEventRecord"))) return rc;
-            if ((rc = hip_status(hipStreamWaitEvent(s, ts.join[k], 0), "hipStreamWaitEvent"))) return rc;
+            int32_t jr = hip_status(hipEventRecord(ts.join[k], ts.s[k]), "hipEventRecord");
+            if (jr == VAE_OK) jr = hip_status(hipStreamWaitEvent(s, ts.join[k], 0), "hipStreamWaitEvent");
+            if (jr != VAE_OK && rc == VAE_OK) rc = jr;
         }
+        if (rc) return rc;
     }
     const int H = h * tp.scale, W = w * tp.scale, xchunks = (W + 255) / 256;
     hipLaunchKernelGGL(tile_assemble, dim3((unsigned)((long long)tp.out_c * H * xchunks)), dim3(256), 0, s, raw, tp.out_c,
