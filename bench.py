@@ -32,6 +32,10 @@ the device and the latent already resident in HBM.  Default workload: latent
                GroupNorm+SiLU) and a standalone nearest-x2 upsample
   stack3d      the causal 3-D conv stack on [128,17,256,256]
   decode3d     the causal 3-D decoder on a latent [16,17,32,32]
+  measured_peaks  the GPU's own FP32 MFMA and HBM ceilings from the library's
+               probes, and the roofline kernel's and the 3x3 convs' executed
+               MFMA rates as fractions of the measured MFMA ceiling (the
+               `roofline` object keeps the published peak)
 """
 from __future__ import annotations
 
@@ -68,6 +72,7 @@ def parse():
     ap.add_argument("--no-3d", action="store_true", help="skip the causal 3-D stack and decode")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timings")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA and HBM ceilings")
     ap.add_argument("--conv3x3", default=None,
                     help="form of the 3x3 convs (winograd_2x2, implicit_gemm, winograd_4x4); default: the library's")
     ap.add_argument("--attention", default=None, choices=["split_softmax", "streaming"],
@@ -507,6 +512,46 @@ def tiled(dec, args, h: int, tile: int = 256, overlap: int = 64) -> dict:
             "whole_image_workspace_bytes": dec.workspace_bytes(h, h)}
 
 
+def measured_peaks(reps: int = 5) -> dict:
+    """The GPU's own ceilings from the library's probes (vae_probe_mfma_f32,
+    vae_probe_hbm), timed with HIP events on the stream they run on: the best
+    of `reps` launches of each."""
+    import torch
+    from diffusion_vae_decoder_amd import api
+
+    def best(fn):
+        ts = []
+        for _ in range(reps + 1):   # the first launch warms up
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) / 1e3)
+        return min(ts[1:])
+
+    # one workgroup per CU: the probe's 8 accumulator chains need all of a
+    # SIMD's registers, so each SIMD holds one wave
+    blocks, iters = torch.cuda.get_device_properties(0).multi_processor_count, 65536
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = api.probe_mfma_f32(blocks, iters, out)[1]
+    t_mfma = best(lambda: api.probe_mfma_f32(blocks, iters, out))
+    n = 1 << 28   # 1 GiB of float32, four times the Infinity Cache
+    grids = (1024, 4096, 16384)
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    part = torch.empty(max(grids) * 256, dtype=torch.float32, device="cuda")
+    t_read = min(best(lambda: api.probe_hbm(x, blocks=g, out=part[:g * 256])) for g in grids)
+    t_copy = min(best(lambda: api.probe_hbm(x, y, blocks=g)) for g in grids)
+    del x, y
+    torch.cuda.synchronize()
+    return {"mfma_f32_tflops": flops / t_mfma / 1e12, "mfma_probe": f"{blocks} workgroups x 4 waves x {iters} rounds "
+            "of 8 independent v_mfma_f32_32x32x2_f32 on register operands",
+            "hbm_read_gbs": n * 4 / t_read / 1e9, "hbm_copy_gbs": 2 * n * 4 / t_copy / 1e9,
+            "hbm_probe": "1 GiB read once (per-thread sums) and copied (read + write counted), the best of "
+                         f"{list(grids)} workgroups of 256 threads streaming 16 KB chunks"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -624,6 +669,12 @@ def main():
     if not args.no_3d:
         out["stack3d"] = stack3d(args)
         out["decode3d"] = decode3d(args)
+    if not args.no_peaks:
+        pk = measured_peaks()
+        pk["roofline_frac_of_measured_mfma"] = roof["achieved"] / pk["mfma_f32_tflops"] if roof["unit"] == "TFLOP/s" \
+            else roof["achieved"] / pk["hbm_copy_gbs"]
+        pk["conv3x3_frac_of_measured_mfma"] = cr["mfma_executed_tflops"] / pk["mfma_f32_tflops"]
+        out["measured_peaks"] = pk
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")

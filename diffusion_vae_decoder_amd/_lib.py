@@ -23,7 +23,7 @@ VAE_ERR_INVALID_ARG = -1
 VAE_ERR_UNSUPPORTED = -2
 VAE_ERR_WORKSPACE = -3
 VAE_ERR_HIP = -4
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 
 class VaeConv(ctypes.Structure):
@@ -107,6 +107,8 @@ SIGNATURES = {
     "vae_decoder_tiled_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, POINTER(c_size_t)]),
     "vae_decode_tiled": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                    c_size_t, c_void_p]),
+    "vae_probe_mfma_f32": (c_int32, [c_int32, c_int32, c_void_p, c_size_t, POINTER(c_double), c_void_p]),
+    "vae_probe_hbm": (c_int32, [c_void_p, c_size_t, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]),
     "vae_decoder_output_shape": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_int32), POINTER(c_int32),
                                            POINTER(c_int32)]),
     "vae_decoder_destroy": (None, [c_void_p]),

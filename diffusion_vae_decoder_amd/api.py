@@ -20,7 +20,7 @@ from ._lib import VaeAttn, VaeConv, VaeError, VaeNorm, VaeProfRecord, VaeResnet,
 __all__ = [
     "VaeError", "conv2d", "conv_in", "groupnorm_silu", "groupnorm_silu_noalloc", "upsample_nearest2x", "attention",
     "attention_streaming", "ATTENTION_FORMS",
-    "conv3d_causal", "conv3d_causal_groupnorm_silu", "Decoder", "CONV3X3_ALGORITHMS", "set_conv3x3_algorithm", "get_conv3x3_algorithm",
+    "conv3d_causal", "conv3d_causal_groupnorm_silu", "probe_mfma_f32", "probe_hbm", "Decoder", "CONV3X3_ALGORITHMS", "set_conv3x3_algorithm", "get_conv3x3_algorithm",
 ]
 
 # Forms of the 3x3 convolutions (vae_set_conv3x3_algorithm): Winograd
@@ -284,6 +284,33 @@ def conv3d_causal_groupnorm_silu(x: torch.Tensor, weight: torch.Tensor, bias: to
                                                _ptr(residual), y.data_ptr(), z.data_ptr(), _ptr(ws), nb.value,
                                                _stream()))
     return y, z
+
+
+def probe_mfma_f32(blocks: int, iters: int, out: Optional[torch.Tensor] = None):
+    """Enqueues the FP32 MFMA probe (vae_probe_mfma_f32) on the current
+    stream; returns (out [blocks * 256], FLOPs of the launch)."""
+    lib = _lib_()
+    o = _out(out, (blocks * 256,), torch.device("cuda", torch.cuda.current_device()))
+    flops = ctypes.c_double()
+    check(lib.vae_probe_mfma_f32(blocks, iters, o.data_ptr(), o.numel(), byref(flops), _stream()))
+    return o, flops.value
+
+
+def probe_hbm(x: torch.Tensor, y: Optional[torch.Tensor] = None, blocks: int = 2048,
+              out: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """Enqueues the HBM probe (vae_probe_hbm): a read of x (returns the
+    per-thread sums [blocks * 256]) or, with y, a copy of x into y."""
+    lib = _lib_()
+    _dev(x, "x")
+    if y is not None:
+        _dev(y, "y")
+        if y.numel() != x.numel():
+            raise ValueError("probe_hbm: y must have as many elements as x")
+        check(lib.vae_probe_hbm(x.data_ptr(), x.numel(), y.data_ptr(), blocks, None, 0, _stream()))
+        return None
+    o = _out(out, (blocks * 256,), x.device)
+    check(lib.vae_probe_hbm(x.data_ptr(), x.numel(), None, blocks, o.data_ptr(), o.numel(), _stream()))
+    return o
 
 
 # ---------------------------------------------------------------------------

@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define VAE_ABI_VERSION 10
+#define VAE_ABI_VERSION 11
 
 #define VAE_OK 0
 #define VAE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive size, mismatched channels */
@@ -416,6 +416,36 @@ int32_t vae_decoder_set_profiling(vae_decoder *d, int32_t on);
  * (oldest first) into `out`; *n receives the number recorded since the last
  * vae_decoder_set_profiling call. */
 int32_t vae_decoder_profile(vae_decoder *d, vae_prof_record *out, int32_t max, int32_t *n);
+
+/* ------------------------------------------------------------ measurement */
+
+/* Measurement only, no step of the decode: probes of known work that
+ * measure the GPU's own ceilings, so the kernels above (the convs bound by
+ * the FP32 matrix units, the normalisation and upsample by HBM) can be read
+ * against measured peaks beside the published ones.  They only enqueue on
+ * `stream`; the caller times them with events there.
+ *
+ * vae_probe_mfma_f32: `blocks` workgroups of 256 threads, each wave running
+ * `iters` rounds of 8 independent v_mfma_f32_32x32x2_f32 on register
+ * operands; *flops receives the launch's FLOPs (blocks x 4 waves x iters x 8
+ * x 4096).  Lane l of every wave feeds a(l) = 1 + l/64 as the A operand
+ * (A[l % 32][l / 32]) and b(l) = 1 - l/128 as the B operand (B[l / 32][l % 32]),
+ * and each thread writes the sum of its accumulators to out[block * 256 +
+ * thread], so a wave's 64 outputs sum to 8 x iters x sum_k A_k B_k with A_k =
+ * sum_m a(m + 32k), B_k = sum_n b(n + 32k), up to float32 rounding.
+ *   out  >= blocks x 256 floats (device); 1 <= blocks <= 65535,
+ *        1 <= iters <= 2^20.
+ * vae_probe_hbm: y == NULL: reads x [n] once and writes each thread's sum of
+ * what it read to out (>= blocks x 256 floats; the outputs sum to sum(x) up
+ * to rounding); y != NULL: copies x to y (out unused).  n a positive multiple
+ * of 4, x and y 16-byte aligned, 1 <= blocks <= 65535; workgroups of 256
+ * threads stream contiguous 16 KB chunks, grid-stride over the chunks, four
+ * 16-byte loads in flight per thread.
+ * Both return VAE_ERR_INVALID_ARG for bad arguments, before any launch. */
+int32_t vae_probe_mfma_f32(int32_t blocks, int32_t iters, float *out, size_t out_floats, double *flops,
+                           void *stream);
+int32_t vae_probe_hbm(const float *x, size_t n, float *y, int32_t blocks, float *out, size_t out_floats,
+                      void *stream);
 
 #ifdef __cplusplus
 }

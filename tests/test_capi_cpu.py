@@ -368,3 +368,23 @@ def test_conv3d_groupnorm_validation(lib):
     assert call(y=FAKE) == VAE_ERR_INVALID_ARG and "alias" in err(lib)
     assert call(res=FAKE + 4096) == VAE_ERR_INVALID_ARG and "residual" in err(lib)
     assert call(nb=ws.value - 1) == VAE_ERR_WORKSPACE
+
+
+def test_probe_validation(lib):
+    # the measurement probes refuse bad arguments before any launch
+    fl = ctypes.c_double()
+    assert lib.vae_probe_mfma_f32(0, 16, FAKE, 1 << 20, byref(fl), NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_mfma_f32(256, 0, FAKE, 1 << 20, byref(fl), NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_mfma_f32(256, (1 << 20) + 1, FAKE, 1 << 20, byref(fl), NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_mfma_f32(256, 16, NULL, 1 << 20, byref(fl), NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_mfma_f32(256, 16, FAKE, 1 << 20, NULL, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_mfma_f32(256, 16, FAKE, 256 * 256 - 1, byref(fl), NULL) == VAE_ERR_INVALID_ARG
+    assert "out holds" in err(lib)
+    assert lib.vae_probe_hbm(NULL, 1024, NULL, 16, FAKE, 1 << 20, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_hbm(FAKE, 1024, NULL, 16, NULL, 1 << 20, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_hbm(FAKE, 1022, NULL, 16, FAKE, 1 << 20, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_hbm(FAKE, 0, NULL, 16, FAKE, 1 << 20, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_hbm(FAKE + 4, 1024, NULL, 16, FAKE, 1 << 20, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_hbm(FAKE, 1024, FAKE + 8, 16, NULL, 0, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_hbm(FAKE, 1024, NULL, 0, FAKE, 1 << 20, NULL) == VAE_ERR_INVALID_ARG
+    assert lib.vae_probe_hbm(FAKE, 1024, NULL, 16, FAKE, 16 * 256 - 1, NULL) == VAE_ERR_INVALID_ARG
