@@ -278,6 +278,13 @@ __device__ __attribute__((always_inline)) inline void w4_step(const float *lx, c
     float t[6][3];   // d B, the half's columns
 #pragma unroll
     for (int r = 0; r < 6; ++r) w4_bt_half<H>(d[r], t[r][0], t[r][1], t[r][2]);
+    // The two waves of a SIMD (from two workgroups) share its datapath; with
+    // the MFMA phase at the higher priority, one wave's MFMAs go first while
+    // the other's transform, loads and barrier wait fill the gaps, instead of
+    // both alternating instruction by instruction (measured 2-8% per plain
+    // layer of the 1024x1024 decode; the whole step at the higher priority,
+    // or the upsampled step's MFMA phase, measured slower).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
         float v[6];
@@ -292,6 +299,7 @@ __device__ __attribute__((always_inline)) inline void w4_step(const float *lx, c
             }
         }
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // The 25 products of an upsampled input, over rows a and columns c indexing
