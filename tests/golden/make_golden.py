@@ -3,7 +3,7 @@
 Calls only the float64 oracle (oracle/) on inputs from the seeded generator
 (vaegen/, seed 0); nothing here touches the GPU path.  Run from the repo root:
 
-    python tests/golden/make_golden.py [decode1024] [stack3d] [tiled512]
+    python tests/golden/make_golden.py [decode1024] [stack3d] [tiled512] [tiled1024]
 
 Outputs (numpy .npz, float64):
   decode_1024.npz  latent [16,128,128] -> RGB [3,1024,1024]: a lattice of
@@ -18,6 +18,8 @@ Outputs (numpy .npz, float64):
                    every row and column within 2 pixels of a tile start or
                    end, a lattice of every 16th row and column, and 16384
                    pseudo-random pixels
+  decode_tiled_1024.npz  latent [16,128,128] -> RGB [3,1024,1024] in the same
+                   tiles (5 x 5 tiles, overlaps 64), sampled the same way
 Each file also holds max|ref| and the L2 norm of the whole reference output.
 The 256 x 256 decode is compared on every pixel by running the oracle inside
 the test, so it has no stored file.
@@ -90,13 +92,15 @@ def stack3d():
                         max_abs=np.abs(y).max(), l2=np.sqrt((y * y).sum()), seed=SEED)
 
 
-def tiled512():
-    h = 64
+def tiled(h: int, name: str):
+    """The oracle's tiled decode (256-pixel tiles, overlaps of at least 64) of
+    the seed's latent [16, h, h]: rows and columns at and around every tile
+    start and end, every 16th, and 16384 random pixels."""
     p = vaegen.decoder_params(SEED)
     z = vaegen.latent(SEED, h, h)
     t = time.time()
     y = oracle.decode_tiled(z, p, vaegen.SCALING_FACTOR, vaegen.SHIFT_FACTOR, tile=256, overlap_min=64)
-    print(f"decode_tiled_512: oracle took {time.time() - t:.1f} s", flush=True)
+    print(f"{name}: oracle took {time.time() - t:.1f} s", flush=True)
     c, H, W = y.shape
     starts, lens, _ = oracle.split_tiles(H, 8, 256, 64)
     edges = sorted({e + d for s0, n in zip(starts, lens) for e in (s0, s0 + n) for d in (-2, -1, 0, 1)
@@ -104,17 +108,19 @@ def tiled512():
     idx = np.array(edges, dtype=np.int64)
     rng = np.random.default_rng(20251)
     pix = np.stack([rng.integers(0, c, 16384), rng.integers(0, H, 16384), rng.integers(0, W, 16384)], axis=1)
-    np.savez_compressed(os.path.join(HERE, "decode_tiled_512"), rows=idx, cols=idx, lattice=y[:, idx][:, :, idx],
+    np.savez_compressed(os.path.join(HERE, name), rows=idx, cols=idx, lattice=y[:, idx][:, :, idx],
                         pixels=pix, pixel_values=y[pix[:, 0], pix[:, 1], pix[:, 2]], shape=np.array(y.shape),
                         tile=256, overlap=64, max_abs=np.abs(y).max(), l2=np.sqrt((y * y).sum()), seed=SEED)
 
 
 if __name__ == "__main__":
     keep_heap()
-    which = sys.argv[1:] or ["decode1024", "stack3d", "tiled512"]
+    which = sys.argv[1:] or ["decode1024", "stack3d", "tiled512", "tiled1024"]
     if "decode1024" in which:
         decode1024()
     if "stack3d" in which:
         stack3d()
     if "tiled512" in which:
-        tiled512()
+        tiled(64, "decode_tiled_512")
+    if "tiled1024" in which:
+        tiled(128, "decode_tiled_1024")

@@ -95,13 +95,20 @@ def test_concurrent_tiles_equal_sequential_tiles(decoder):
     np.testing.assert_array_equal(seq, conc)
 
 
-def test_tiled_decode_512_against_stored_oracle(decoder):
-    # stored oracle values (tests/golden/make_golden.py): 3 x 3 tiles of 256
-    # pixels overlapping by 128; rows and columns at and around every tile
-    # start and end, every 16th row and column, 16384 random pixels
-    g = np.load(os.path.join(GOLDEN, "decode_tiled_512.npz"))
+@pytest.mark.parametrize("name,h", [
+    # 3 x 3 tiles of 256 pixels overlapping by 128
+    ("decode_tiled_512", 64),
+    # the benchmarked configuration: 5 x 5 tiles overlapping by 64
+    ("decode_tiled_1024", 128),
+])
+def test_tiled_decode_against_stored_oracle(decoder, name, h):
+    # stored oracle values (tests/golden/make_golden.py): rows and columns at
+    # and around every tile start and end, every 16th row and column, 16384
+    # random pixels
+    g = np.load(os.path.join(GOLDEN, name + ".npz"))
     assert int(g["seed"]) == 0
-    z = vaegen.latent(0, 64, 64)
+    z = vaegen.latent(0, h, h)
+    print(f"{name}: tiled decode of latent [16,{h},{h}]", flush=True)
     rgb = decoder.decode_tiled(dev(z), int(g["tile"]), int(g["overlap"]), out=nan_like(tuple(g["shape"])))
     check_guards(rgb)
     rgb = host(rgb)
