@@ -121,6 +121,34 @@ def test_tiled_decode_against_stored_oracle(decoder, name, h):
     assert abs(math.sqrt((rgb.astype(np.float64) ** 2).sum()) / float(g["l2"]) - 1.0) < 1e-4
 
 
+def test_tiled_decode_4096_corner_tiles_against_oracle(decoder, params):
+    """A 4096 x 4096 output (latent [16,512,512], 21 x 21 tiles), far beyond
+    what the whole-image decode's workspace and score matrix allow: the first
+    and the last tile keep, unblended, the part before (after) their
+    neighbours' overlap, which must equal the oracle's decode of their latent
+    blocks; everything is written and finite."""
+    h = 512
+    z = vaegen.latent(21, h, h)
+    starts, lens, _ = oracle.split_tiles(8 * h, 8, 256, 64)
+    assert len(starts) == 21 and lens == [256] * 21
+    print("tiled decode of latent [16,512,512] in 21 x 21 tiles", flush=True)
+    rgb = decoder.decode_tiled(dev(z), 256, 64, out=nan_like((3, 8 * h, 8 * h)))
+    check_guards(rgb)
+    rgb = host(rgb)
+    assert np.isfinite(rgb).all()
+    e0 = starts[1]                  # tile 0 alone before tile 1 begins
+    e1 = starts[-2] + lens[-2]      # the last tile alone after tile n-2 ends
+    b0, b1 = starts[-1] // 8, starts[-1] // 8 + 32
+    for rows, cols, block, crop in [
+        (slice(0, e0), slice(0, e0), z[:, :32, :32], (slice(0, e0), slice(0, e0))),
+        (slice(e1, 8 * h), slice(e1, 8 * h), z[:, b0:b1, b0:b1],
+         (slice(e1 - starts[-1], 256), slice(e1 - starts[-1], 256))),
+    ]:
+        ref = oracle.decode(block, params, SF, SH)[:, crop[0], crop[1]]
+        cos, mx = rgb_metrics(rgb[:, rows, cols], ref)
+        assert cos >= 0.99999 and mx <= 1e-3 * np.abs(ref).max(), (cos, mx)
+
+
 def test_tiled_decode_rejects_bad_arguments(api, decoder):
     lib = decoder._lib
     nb = ctypes.c_size_t()
