@@ -42,6 +42,7 @@ def decoder(api, params):
 @pytest.mark.parametrize("h,w,tile,ov", [
     (12, 10, 64, 16),   # 96 x 80 px: 2 x 2 tiles of 64, overlaps 32 and 48
     (9, 5, 32, 8),      # 72 x 40 px: 3 x 2 tiles of 32, overlaps (16, 8) and 24
+    (12, 10, 32, 0),    # 96 x 80 px, no minimum overlap: rows of tiles abut, columns overlap by 8
 ])
 def test_tiled_decode_matches_oracle(decoder, params, h, w, tile, ov):
     z = vaegen.latent(11, h, w)

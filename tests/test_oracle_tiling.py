@@ -14,7 +14,7 @@ def covers(starts, lens, L):
     return starts[0] == 0 and starts[-1] + lens[-1] >= L
 
 
-@pytest.mark.parametrize("tile,ovmin,ratio", [(256, 64, 8), (64, 16, 8), (48, 8, 4), (256, 64, 1)])
+@pytest.mark.parametrize("tile,ovmin,ratio", [(256, 64, 8), (64, 16, 8), (48, 8, 4), (256, 64, 1), (32, 0, 8)])
 def test_split_tiles_schedule_properties(tile, ovmin, ratio):
     for L in range(1, 1400):
         starts, lens, ovs = oracle.split_tiles(L, ratio, tile, ovmin)
@@ -51,6 +51,10 @@ def test_split_tiles_worked_values():
     # the first three overlaps
     assert oracle.split_tiles(1000, 8) == ([0, 184, 368, 552, 744], [256] * 5, [72, 72, 72, 64])
     assert oracle.split_tiles(256, 8) == ([0], [256], [])
+    # no minimum overlap: tiles that divide the axis abut; 80 px in 32-px
+    # tiles leave 16 px of slack, one step of 8 to each overlap
+    assert oracle.split_tiles(96, 8, 32, 0) == ([0, 32, 64], [32] * 3, [0, 0])
+    assert oracle.split_tiles(80, 8, 32, 0) == ([0, 24, 48], [32] * 3, [8, 8])
     with pytest.raises(ValueError):
         oracle.split_tiles(300, 8, 64, 64)
 
